@@ -1,0 +1,166 @@
+/*
+ * gpt2fwd.h - C ABI of the MI355X (gfx950) GPT-2 forward-pass library.
+ *
+ * One entry per step of the forward pass, following the per-kernel split of
+ * "ECE408 Final Project - GPT-2, Milestone 1" (Code Submission and Grading,
+ * kernel table: Encoder, LayerNorm, MatMul, Attention including Softmax,
+ * Residual, GELU), plus the vocabulary softmax of the classifier (llm.c
+ * discussion "State of the Union [April 22, 2024]", kernel summaries:
+ * fused_classifier_kernel3), the whole forward, and a KV-cache decode step
+ * (optdl2025 projects, "Understanding and Improving GPT-2 Implementations in
+ * NanoGPT": KV caching for autoregressive prediction).
+ *
+ * Ownership (as the ECE408 page fixes for its xxxx_forward() host functions,
+ * Milestone Requirements): the caller allocates, fills and frees every buffer.
+ * The library never allocates, frees or copies device memory, and never
+ * synchronises. Every pointer argument is a DEVICE pointer unless marked
+ * "host". Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns once it is enqueued; results are valid after
+ * the caller synchronises that stream.
+ *
+ * Errors: every entry returns an int status (GPT2_OK = 0 or a negative
+ * GPT2_ERR_*). Arguments are validated before any launch, so a failed call
+ * enqueues nothing. A launch failure returns GPT2_ERR_HIP and records the HIP
+ * error code for gpt2_last_hip_error() (per host thread). No entry prints,
+ * aborts or throws. A zero-sized problem returns GPT2_OK and launches nothing.
+ *
+ * Layout: row-major, contiguous. Every device pointer must be 16-byte aligned.
+ * dtype (GPT2_F32 or GPT2_BF16) applies to weights and activations alike;
+ * LayerNorm statistics are always fp32 and all accumulation is fp32.
+ * bf16 results are rounded to nearest even. Outputs may alias inputs only
+ * where stated.
+ */
+#ifndef GPT2FWD_H
+#define GPT2FWD_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { GPT2_F32 = 0, GPT2_BF16 = 1 };
+
+enum {
+    GPT2_OK = 0,
+    GPT2_ERR_INVALID_ARGUMENT = -1,   /* NULL pointer, negative size, C % NH != 0, ... */
+    GPT2_ERR_UNSUPPORTED = -2,        /* valid but not handled: head size, alignment, width */
+    GPT2_ERR_HIP = -3,                /* a launch failed; see gpt2_last_hip_error() */
+    GPT2_ERR_WORKSPACE_TOO_SMALL = -4
+};
+
+/* Token + position embedding (ECE408 Milestone 1 kernel table: Encoder).
+ *   out[b,t,:] = wte[tokens[b,t],:] + wpe[t,:]
+ * out [B,T,C]; tokens int32 [B,T] (values must lie in [0, rows of wte): not
+ * checked on the device); wte [*,C]; wpe [>=T,C]. C % 8 == 0.
+ * To embed a single position p for every sequence (decode), pass T = 1 and
+ * wpe + p*C. */
+int encoder_forward(void* out, const int32_t* tokens, const void* wte, const void* wpe,
+                    int B, int T, int C, int dtype, void* stream);
+
+/* LayerNorm over the last dimension (ECE408 kernel table: LayerNorm):
+ *   mu = mean(x), var = mean((x-mu)^2), rstd = 1/sqrt(var+eps),
+ *   out = (x-mu)*rstd*gamma + beta.
+ * inp, out [N,C]; gamma, beta [C]; mean, rstd fp32 [N], nullable.
+ * 8 <= C <= 4096, C % 8 == 0. out must not alias inp. */
+int layernorm_forward(void* out, float* mean, float* rstd, const void* inp,
+                      const void* gamma, const void* beta, int N, int C, float eps,
+                      int dtype, void* stream);
+
+/* Linear layer (ECE408 kernel table: MatMul):
+ *   out[n,o] = sum_c inp[n,c] * weight[o,c] + bias[o]
+ * inp [N,C]; weight [OC,C] (out_features x in_features); bias [OC], nullable;
+ * out [N,OC], must not alias inp/weight. C % 8 == 0, OC % 8 == 0. */
+int matmul_forward(void* out, const void* inp, const void* weight, const void* bias,
+                   int N, int C, int OC, int dtype, void* stream);
+
+/* Causal multi-head self-attention with its softmax fused (ECE408 kernel
+ * table: Attention including Softmax; the tiled online-softmax algorithm of
+ * the optdl2025 project "Understand FlashAttention (I)", computing only the
+ * lower triangle as the llm.c "big stones" list proposes).
+ * qkv [B,T,3C] = [q | k | v], head h at columns h*hs..(h+1)*hs-1 of each third,
+ * hs = C/NH in {16, 32, 64, 128}; out [B,T,C] with the same head order.
+ *   out_t = sum_{j<=t} softmax_j(q_t.k_j / sqrt(hs)) v_j */
+int attention_forward(void* out, const void* qkv, int B, int T, int C, int NH,
+                      int dtype, void* stream);
+
+/* GELU, tanh form (ECE408 kernel table: GELU):
+ *   out = x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
+ * n elements; out may alias inp. */
+int gelu_forward(void* out, const void* inp, int64_t n, int dtype, void* stream);
+
+/* Residual add (ECE408 kernel table: Residual): out = a + b, n elements.
+ * out may alias a or b. */
+int residual_forward(void* out, const void* a, const void* b, int64_t n, int dtype,
+                     void* stream);
+
+/* Softmax over the vocabulary (forward half of llm.c's
+ * fused_classifier_kernel3): logits, probs [N,Vp]; the first V columns are
+ * real tokens, columns V..Vp-1 are padding and receive probability 0.
+ * V <= Vp <= 131072, Vp % 8 == 0. probs must not alias logits. */
+int softmax_forward(void* probs, const void* logits, int N, int V, int Vp, int dtype,
+                    void* stream);
+
+/* ---------------------------------------------------------------- model */
+typedef struct {
+    int L;        /* layers */
+    int C;        /* channels */
+    int NH;       /* heads; C/NH in {16,32,64,128} */
+    int V;        /* vocabulary */
+    int Vp;       /* padded vocabulary (rows of wte), Vp >= V, Vp % 8 == 0 */
+    int maxT;     /* rows of wpe */
+    int dtype;    /* GPT2_F32 or GPT2_BF16 */
+    float ln_eps; /* LayerNorm epsilon, 1e-5 for GPT-2 */
+} gpt2_config;
+
+/* Elements in the flat parameter buffer (host call):
+ * Vp*C + maxT*C + L*(12*C*C + 13*C) + 2*C, stored as
+ * wte[Vp,C] wpe[maxT,C] ln1_g[L,C] ln1_b[L,C] qkv_w[L,3C,C] qkv_b[L,3C]
+ * attproj_w[L,C,C] attproj_b[L,C] ln2_g[L,C] ln2_b[L,C] fc_w[L,4C,C] fc_b[L,4C]
+ * fcproj_w[L,C,4C] fcproj_b[L,C] lnf_g[C] lnf_b[C]. Rows V..Vp-1 of wte should
+ * be zero. Returns -1 for an invalid config. */
+int64_t gpt2_param_count(const gpt2_config* cfg /* host */);
+
+/* Bytes of workspace gpt2_forward needs for B sequences of T tokens (host
+ * call); -1 for an invalid config. */
+int64_t gpt2_workspace_bytes(const gpt2_config* cfg /* host */, int B, int T);
+
+/* The whole forward: pre-LayerNorm GPT-2 blocks, final LayerNorm, logits
+ * against the tied token embedding (no bias), vocabulary softmax.
+ * tokens int32 [B,T] (T <= maxT); params: the flat buffer above; logits
+ * [B,T,Vp]; probs [B,T,Vp] or NULL to skip the softmax. */
+int gpt2_forward(void* logits, void* probs, const int32_t* tokens, const void* params,
+                 const gpt2_config* cfg /* host */, int B, int T, void* workspace,
+                 int64_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- decode */
+/* Bytes of workspace attention_decode_forward needs (host call). */
+int64_t attention_decode_workspace_bytes(int B, int C, int NH, int maxT);
+
+/* One query per sequence against a KV cache (optdl2025 NanoGPT project: KV
+ * caching). qkv_new [B,3C] holds this step's q,k,v; kcache, vcache
+ * [B,NH,maxT,hs] for one layer. Writes k,v of qkv_new at position pos, then
+ * out[b, head h] = sum_{j<=pos} softmax_j(q.k_j/sqrt(hs)) v_j. 0 <= pos < maxT.
+ * Cache slot pos is never read before it is written. */
+int attention_decode_forward(void* out, const void* qkv_new, void* kcache, void* vcache,
+                             int B, int pos, int maxT, int C, int NH, int dtype,
+                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gpt2_decode_step needs (host call); -1 if invalid. */
+int64_t gpt2_decode_workspace_bytes(const gpt2_config* cfg /* host */, int B);
+
+/* One autoregressive step for B sequences, each with one new token at
+ * position pos: tokens int32 [B]; kcache, vcache [L,B,NH,maxT,hs] (updated at
+ * pos); logits [B,Vp]; probs [B,Vp] or NULL. */
+int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens, int pos,
+                     void* kcache, void* vcache, const void* params,
+                     const gpt2_config* cfg /* host */, int B, void* workspace,
+                     int64_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- status */
+const char* gpt2_status_string(int status);  /* static string, never NULL */
+int gpt2_last_hip_error(void);               /* hipError_t of this thread's last failure */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,272 @@
+"""Per-kernel parity: each C-ABI entry against the CPU oracle on the same
+seeded inputs (every kernel fed oracle-independent inputs, so one kernel's
+error never leaks into another's test). Shapes span several tiles and a
+ragged tail, plus the full GPT-2 small/medium shapes.
+
+Tolerances (floating point; derivations in the design notes):
+  encoder, residual           bit-exact (one fp32 add, then RNE for bf16)
+  matmul, integer inputs      bit-exact (every partial sum exact in fp32)
+  matmul                      fp32 ||d||/||ref|| <= 1e-5; bf16 <= 1e-2
+  layernorm                   fp32 max|d| <= 1e-5;       bf16 <= 1e-2 rel
+  gelu                        fp32 |d| <= 2e-6 max(1,|x|); bf16 <= 2^-8|ref| + 1e-6
+  attention                   fp32 max|d| <= 1e-5;       bf16 <= 1e-2 rel
+  softmax                     fp32 |d| <= 1e-6 |ref| + 1e-9; bf16 <= 2^-8|ref| + 1e-9
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import transformer_forward_pass_gpt_amd as G
+from transformer_forward_pass_gpt_amd import inputs as I
+
+from gpu_util import bf16_round, dev, dev_int, empty, host, host_bits, max_abs, rel_err
+
+pytestmark = pytest.mark.gpu
+DT = {"f32": I.F32, "bf16": I.BF16}
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------- encoder
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,C,V", [(2, 32, 64, 256), (3, 37, 104, 500), (2, 1024, 768, 50304)])
+def test_encoder(dt, B, T, C, V):
+    announce("encoder", dt, B, T, C, V)
+    d = DT[dt]
+    wte = I.random_tensor(1, (V, C), 0.02, d)
+    wpe = I.random_tensor(2, (T, C), 0.02, d)
+    tok = np.random.default_rng(3).integers(0, V, (B, T)).astype(np.int32)
+    out = empty((B, T, C), d)
+    G.encoder_forward(out, dev_int(tok), dev(wte, d), dev(wpe, d))
+    ref = oracle.encoder(tok, wte, wpe)
+    if d == I.BF16:
+        assert np.array_equal(host_bits(out), I.to_bf16_bits(ref))
+    else:
+        assert np.array_equal(host_bits(out), ref.view(np.uint32))
+
+
+# ----------------------------------------------------------------- residual
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [8, 1000003, 4096 * 768])
+def test_residual(dt, n):
+    announce("residual", dt, n)
+    d = DT[dt]
+    a = I.random_tensor(4, n, 1.0, d)
+    b = I.random_tensor(5, n, 1.0, d)
+    ta, tb = dev(a, d), dev(b, d)
+    out = empty(n, d)
+    G.residual_forward(out, ta, tb)
+    ref = oracle.residual(a, b)
+    exp = I.to_bf16_bits(ref) if d == I.BF16 else ref.view(np.uint32)
+    assert np.array_equal(host_bits(out), exp)
+    G.residual_forward(ta, ta, tb)  # in place, out aliasing a
+    assert np.array_equal(host_bits(ta), exp)
+
+
+# ----------------------------------------------------------------- gelu
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [13, 64 * 256, 4096 * 3072 + 5])
+def test_gelu(dt, n):
+    announce("gelu", dt, n)
+    d = DT[dt]
+    x = I.random_tensor(6, n, 2.0, d)
+    x[:4] = np.array([0.0, -30.0, 30.0, -7.5], np.float32)[: min(4, n)]
+    tx = dev(x, d)
+    out = empty(n, d)
+    G.gelu_forward(out, tx)
+    ref = oracle.gelu(x)
+    got = host(out)
+    if d == I.BF16:
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+    else:
+        assert np.all(np.abs(got - ref) <= 2e-6 * np.maximum(1.0, np.abs(x)))
+    G.gelu_forward(tx, tx)  # in place
+    assert np.array_equal(host_bits(tx), host_bits(out))
+
+
+# ----------------------------------------------------------------- layernorm
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C", [(64, 64), (37, 104), (4096, 768), (300, 1024), (5, 4096)])
+def test_layernorm(dt, N, C):
+    announce("layernorm", dt, N, C)
+    d = DT[dt]
+    x = (I.random_tensor(7, (N, C), 1.0, I.F32) * 0.3 + 0.1).astype(np.float32)
+    if d == I.BF16:
+        x = bf16_round(x)
+    g = I.random_tensor(8, C, 0.1, d) + np.float32(1.0)
+    g = bf16_round(g) if d == I.BF16 else g
+    b = I.random_tensor(9, C, 0.1, d)
+    out = empty((N, C), d)
+    mean = empty(N, I.F32)
+    rstd = empty(N, I.F32)
+    G.layernorm_forward(out, dev(x, d), dev(g, d), dev(b, d), 1e-5, mean, rstd)
+    ref, rm, rr = oracle.layernorm(x, g, b, 1e-5, return_stats=True)
+    got = host(out)
+    if d == I.BF16:
+        assert rel_err(got, ref) <= 1e-2
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-3)
+    else:
+        assert max_abs(got, ref) <= 1e-5
+    assert max_abs(host(mean), rm) <= 1e-6
+    assert np.all(np.abs(host(rstd) - rr) <= 1e-5 * rr)
+
+
+# ----------------------------------------------------------------- matmul
+MM_SHAPES = [
+    (64, 64, 192), (64, 256, 64), (65, 72, 200), (4097, 64, 40), (300, 768, 2304),
+    (32, 768, 2304), (32, 3072, 768), (7, 768, 256), (1000, 1024, 4096),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,OC", MM_SHAPES)
+def test_matmul_integer_exact(dt, N, C, OC):
+    """Small integers: every product and partial sum is an integer below 2^24,
+    so any correct summation order gives the exact result, bit for bit."""
+    announce("matmul-int", dt, N, C, OC)
+    d = DT[dt]
+    a = I.random_int_tensor(10, (N, C), -3, 3)
+    w = I.random_int_tensor(11, (OC, C), -3, 3)
+    b = I.random_int_tensor(12, OC, -8, 8)
+    out = empty((N, OC), d)
+    G.matmul_forward(out, dev(a, d), dev(w, d), dev(b, d))
+    ref = oracle.matmul(a, w, b)
+    got = host(out)
+    if d == I.BF16:  # the output itself is rounded to bf16
+        assert np.array_equal(got, bf16_round(ref))
+    else:
+        assert np.array_equal(got, ref)
+    out2 = empty((N, OC), d)
+    G.matmul_forward(out2, dev(a, d), dev(w, d), None)
+    exp2 = ref - b
+    assert np.array_equal(host(out2), bf16_round(exp2) if d == I.BF16 else exp2)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,OC", MM_SHAPES)
+def test_matmul_random(dt, N, C, OC):
+    announce("matmul-rand", dt, N, C, OC)
+    d = DT[dt]
+    a = I.random_tensor(13, (N, C), 1.0, d)
+    w = I.random_tensor(14, (OC, C), 0.02, d)
+    b = I.random_tensor(15, OC, 0.02, d)
+    out = empty((N, OC), d)
+    G.matmul_forward(out, dev(a, d), dev(w, d), dev(b, d))
+    ref = oracle.matmul(a, w, b)
+    assert rel_err(host(out), ref) <= (1e-2 if d == I.BF16 else 1e-5)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_matmul_full_logits_shape_sampled(dt):
+    """GPT-2 small logits GEMM (4096 x 768 -> 50304) in the launch the forward
+    uses; the oracle recomputes a sample of rows."""
+    announce("matmul-logits", dt)
+    d = DT[dt]
+    N, C, OC = 4096, 768, 50304
+    a = I.random_tensor(16, (N, C), 1.0, d)
+    w = I.random_tensor(17, (OC, C), 0.02, d)
+    out = empty((N, OC), d)
+    G.matmul_forward(out, dev(a, d), dev(w, d), None)
+    rows = np.array([0, 1, 127, 128, 2047, 4095])
+    got = host(out)[rows]
+    ref = oracle.matmul(a[rows], w, None)
+    assert rel_err(got, ref) <= (1e-2 if d == I.BF16 else 1e-5)
+
+
+# ----------------------------------------------------------------- attention
+ATT_SHAPES = [(2, 32, 64, 4), (1, 1, 64, 4), (2, 100, 128, 2), (1, 77, 256, 8), (2, 200, 256, 2),
+              (1, 1024, 768, 12), (1, 300, 512, 4)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,C,NH", ATT_SHAPES)
+def test_attention(dt, B, T, C, NH):
+    announce("attention", dt, B, T, C, NH)
+    d = DT[dt]
+    qkv = I.random_tensor(18, (B, T, 3 * C), 1.0, d)
+    out = empty((B, T, C), d, fill=float("nan"))
+    G.attention_forward(out, dev(qkv, d), NH)
+    ref = oracle.attention(qkv, NH)
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    if d == I.BF16:
+        assert rel_err(got, ref) <= 1e-2
+    else:
+        assert max_abs(got, ref) <= 1e-5
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_attention_equal_keys_prefix_mean(dt):
+    """Identical keys: every causal row is the running mean of v."""
+    announce("attention-prefix-mean", dt)
+    d = DT[dt]
+    B, T, C, NH = 1, 256, 128, 2
+    qkv = I.random_tensor(19, (B, T, 3 * C), 1.0, d)
+    qkv[:, :, C:2 * C] = qkv[:, :1, C:2 * C]
+    out = empty((B, T, C), d)
+    G.attention_forward(out, dev(qkv, d), NH)
+    v = qkv[:, :, 2 * C:].astype(np.float64)
+    exp = np.cumsum(v, axis=1) / np.arange(1, T + 1)[None, :, None]
+    tol = 1e-2 if d == I.BF16 else 1e-5
+    assert rel_err(host(out), exp) <= tol
+
+
+# ----------------------------------------------------------------- softmax
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,V,Vp", [(64, 256, 256), (5, 1000, 1024), (3, 50257, 50304), (2, 7, 8),
+                                    (4, 100000, 100000)])
+def test_softmax(dt, N, V, Vp):
+    announce("softmax", dt, N, V, Vp)
+    d = DT[dt]
+    logits = I.random_tensor(20, (N, Vp), 2.0, d)
+    out = empty((N, Vp), d, fill=float("nan"))
+    G.softmax_forward(out, dev(logits, d), V)
+    ref = oracle.softmax(logits, V)
+    got = host(out)
+    assert np.all(got[:, V:] == 0)
+    if d == I.BF16:
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * ref + 1e-9)
+    else:
+        assert np.all(np.abs(got - ref) <= 1e-6 * ref + 1e-9)
+        assert np.all(np.abs(got.astype(np.float64).sum(1) - 1) <= 1e-5)
+
+
+# ----------------------------------------------------------------- decode attention
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,C,NH,maxT,pos", [(2, 256, 4, 1024, 1023), (3, 256, 4, 1024, 0),
+                                              (2, 128, 8, 300, 257), (1, 768, 12, 1024, 700)])
+def test_attention_decode(dt, B, C, NH, maxT, pos):
+    announce("attention-decode", dt, B, C, NH, maxT, pos)
+    d = DT[dt]
+    hs = C // NH
+    kc = I.random_tensor(21, (B, NH, maxT, hs), 1.0, d)
+    vc = I.random_tensor(22, (B, NH, maxT, hs), 1.0, d)
+    kc[:, :, pos:] = np.nan  # never read before written
+    vc[:, :, pos:] = np.nan
+    qkv = I.random_tensor(23, (B, 3 * C), 1.0, d)
+    tk, tv = dev(kc, d), dev(vc, d)
+    out = empty((B, C), d)
+    ws = empty(G.attention_decode_workspace_bytes(B, C, NH, maxT) // 4, I.F32)
+    G.attention_decode_forward(out, dev(qkv, d), tk, tv, pos, NH, ws)
+    # reference: row `pos` of causal attention over a sequence whose earlier
+    # keys/values are the cache and whose last row is the new token
+    seq = np.zeros((B, pos + 1, 3 * C), np.float32)
+    seq[:, :pos, C:2 * C] = kc[:, :, :pos].transpose(0, 2, 1, 3).reshape(B, pos, C)
+    seq[:, :pos, 2 * C:] = vc[:, :, :pos].transpose(0, 2, 1, 3).reshape(B, pos, C)
+    seq[:, pos] = qkv
+    ref = oracle.attention(seq, NH)[:, pos]
+    got = host(out)
+    if d == I.BF16:
+        assert rel_err(got, ref) <= 1e-2
+    else:
+        assert max_abs(got, ref) <= 1e-5
+    # the step wrote k, v at pos, and nothing else changed
+    kgot, vgot = host(tk), host(tv)
+    assert np.array_equal(kgot[:, :, pos], qkv[:, C:2 * C].reshape(B, NH, hs))
+    assert np.array_equal(vgot[:, :, pos], qkv[:, 2 * C:].reshape(B, NH, hs))
+    assert np.array_equal(kgot[:, :, :pos], kc[:, :, :pos])

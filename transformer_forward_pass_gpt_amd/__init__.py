@@ -1,0 +1,253 @@
+"""GPT-2 forward pass on AMD MI355X (gfx950): Python binding of libgpt2fwd.so.
+
+Thin ctypes marshalling over the C ABI declared in include/gpt2fwd.h: every
+function takes torch tensors that already live on the GPU, passes their
+device pointers and the current HIP stream, and raises on a nonzero status.
+All compute happens in the HIP kernels; there is no CPU or PyTorch fallback:
+if the library is missing, every call raises.
+
+The library is loaded on first use, so ``transformer_forward_pass_gpt_amd.inputs``
+can be imported on a machine without a GPU or a built library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgpt2fwd.so")
+
+F32 = 0
+BF16 = 1
+
+OK = 0
+ERR_INVALID_ARGUMENT = -1
+ERR_UNSUPPORTED = -2
+ERR_HIP = -3
+ERR_WORKSPACE_TOO_SMALL = -4
+
+EXPORTS = (
+    "encoder_forward", "layernorm_forward", "matmul_forward", "attention_forward",
+    "gelu_forward", "residual_forward", "softmax_forward", "gpt2_param_count",
+    "gpt2_workspace_bytes", "gpt2_forward", "attention_decode_workspace_bytes",
+    "attention_decode_forward", "gpt2_decode_workspace_bytes", "gpt2_decode_step",
+    "gpt2_status_string", "gpt2_last_hip_error",
+)
+
+
+class GPT2Error(RuntimeError):
+    def __init__(self, fn, status, lib):
+        msg = lib.gpt2_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += " (hipError %d)" % lib.gpt2_last_hip_error()
+        super().__init__("%s failed: %s [%d]" % (fn, msg, status))
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int), ("C", ctypes.c_int), ("NH", ctypes.c_int),
+                ("V", ctypes.c_int), ("Vp", ctypes.c_int), ("maxT", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("ln_eps", ctypes.c_float)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgpt2fwd.so and declare the signatures. Raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("libgpt2fwd.so not built (%s); run "
+                               "`python -m transformer_forward_pass_gpt_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        CP = ctypes.POINTER(Config)
+        sig = {
+            "encoder_forward": (I, [P, P, P, P, I, I, I, I, P]),
+            "layernorm_forward": (I, [P, P, P, P, P, P, I, I, F, I, P]),
+            "matmul_forward": (I, [P, P, P, P, I, I, I, I, P]),
+            "attention_forward": (I, [P, P, I, I, I, I, I, P]),
+            "gelu_forward": (I, [P, P, I64, I, P]),
+            "residual_forward": (I, [P, P, P, I64, I, P]),
+            "softmax_forward": (I, [P, P, I, I, I, I, P]),
+            "gpt2_param_count": (I64, [CP]),
+            "gpt2_workspace_bytes": (I64, [CP, I, I]),
+            "gpt2_forward": (I, [P, P, P, P, CP, I, I, P, I64, P]),
+            "attention_decode_workspace_bytes": (I64, [I, I, I, I]),
+            "attention_decode_forward": (I, [P, P, P, P, I, I, I, I, I, I, P, I64, P]),
+            "gpt2_decode_workspace_bytes": (I64, [CP, I]),
+            "gpt2_decode_step": (I, [P, P, P, I, P, P, P, CP, I, P, I64, P]),
+            "gpt2_status_string": (ctypes.c_char_p, [I]),
+            "gpt2_last_hip_error": (I, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+# ------------------------------------------------------------------ helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("tensor dtype must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn, status):
+    if status != OK:
+        raise GPT2Error(fn, status, load_library())
+
+
+def make_config(L, C, NH, V, Vp, maxT, dtype, ln_eps=1e-5) -> Config:
+    return Config(L, C, NH, V, Vp, maxT, dtype, ln_eps)
+
+
+# ------------------------------------------------------------------ per-step entries
+def encoder_forward(out, tokens, wte, wpe, stream=None):
+    """out [B,T,C] = wte[tokens] + wpe[:T]; tokens int32 [B,T]."""
+    lib = load_library()
+    B, T = tokens.shape
+    C = wte.shape[-1]
+    _check("encoder_forward", lib.encoder_forward(
+        _dev(out, "out"), _dev(tokens, "tokens"), _dev(wte, "wte"), _dev(wpe, "wpe"),
+        B, T, C, _dtype_code(out), _stream(stream)))
+    return out
+
+
+def layernorm_forward(out, inp, gamma, beta, eps=1e-5, mean=None, rstd=None, stream=None):
+    lib = load_library()
+    C = inp.shape[-1]
+    N = inp.numel() // C if C else 0
+    _check("layernorm_forward", lib.layernorm_forward(
+        _dev(out, "out"), _dev(mean, "mean"), _dev(rstd, "rstd"), _dev(inp, "inp"),
+        _dev(gamma, "gamma"), _dev(beta, "beta"), N, C, float(eps), _dtype_code(inp),
+        _stream(stream)))
+    return out
+
+
+def matmul_forward(out, inp, weight, bias=None, stream=None):
+    """out [N,OC] = inp [N,C] @ weight[OC,C]^T + bias."""
+    lib = load_library()
+    C = inp.shape[-1]
+    N = inp.numel() // C if C else 0
+    OC = weight.shape[0]
+    _check("matmul_forward", lib.matmul_forward(
+        _dev(out, "out"), _dev(inp, "inp"), _dev(weight, "weight"), _dev(bias, "bias"),
+        N, C, OC, _dtype_code(inp), _stream(stream)))
+    return out
+
+
+def attention_forward(out, qkv, NH, stream=None):
+    """out [B,T,C] from qkv [B,T,3C], causal, NH heads."""
+    lib = load_library()
+    B, T, C3 = qkv.shape
+    _check("attention_forward", lib.attention_forward(
+        _dev(out, "out"), _dev(qkv, "qkv"), B, T, C3 // 3, NH, _dtype_code(qkv), _stream(stream)))
+    return out
+
+
+def gelu_forward(out, inp, stream=None):
+    lib = load_library()
+    _check("gelu_forward", lib.gelu_forward(_dev(out, "out"), _dev(inp, "inp"), inp.numel(),
+                                            _dtype_code(inp), _stream(stream)))
+    return out
+
+
+def residual_forward(out, a, b, stream=None):
+    lib = load_library()
+    _check("residual_forward", lib.residual_forward(_dev(out, "out"), _dev(a, "a"), _dev(b, "b"),
+                                                    a.numel(), _dtype_code(a), _stream(stream)))
+    return out
+
+
+def softmax_forward(probs, logits, V, stream=None):
+    """probs [N,Vp] = softmax over the first V columns of logits; padding -> 0."""
+    lib = load_library()
+    Vp = logits.shape[-1]
+    N = logits.numel() // Vp
+    _check("softmax_forward", lib.softmax_forward(_dev(probs, "probs"), _dev(logits, "logits"), N,
+                                                  V, Vp, _dtype_code(logits), _stream(stream)))
+    return probs
+
+
+# ------------------------------------------------------------------ model entries
+def param_count(cfg: Config) -> int:
+    return int(load_library().gpt2_param_count(ctypes.byref(cfg)))
+
+
+def workspace_bytes(cfg: Config, B: int, T: int) -> int:
+    return int(load_library().gpt2_workspace_bytes(ctypes.byref(cfg), B, T))
+
+
+def gpt2_forward(logits, probs, tokens, params, cfg: Config, workspace, stream=None):
+    """logits/probs [B,T,Vp] (probs may be None); tokens int32 [B,T]; params flat."""
+    lib = load_library()
+    B, T = tokens.shape
+    _check("gpt2_forward", lib.gpt2_forward(
+        _dev(logits, "logits"), _dev(probs, "probs"), _dev(tokens, "tokens"), _dev(params, "params"),
+        ctypes.byref(cfg), B, T, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return logits
+
+
+def attention_decode_workspace_bytes(B, C, NH, maxT) -> int:
+    return int(load_library().attention_decode_workspace_bytes(B, C, NH, maxT))
+
+
+def attention_decode_forward(out, qkv_new, kcache, vcache, pos, NH, workspace, stream=None):
+    """out [B,C]; qkv_new [B,3C]; kcache/vcache [B,NH,maxT,hs] for one layer."""
+    lib = load_library()
+    B, C3 = qkv_new.shape
+    maxT = kcache.shape[2]
+    _check("attention_decode_forward", lib.attention_decode_forward(
+        _dev(out, "out"), _dev(qkv_new, "qkv_new"), _dev(kcache, "kcache"), _dev(vcache, "vcache"),
+        B, int(pos), maxT, C3 // 3, NH, _dtype_code(qkv_new), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def decode_workspace_bytes(cfg: Config, B: int) -> int:
+    return int(load_library().gpt2_decode_workspace_bytes(ctypes.byref(cfg), B))
+
+
+def gpt2_decode_step(logits, probs, tokens, pos, kcache, vcache, params, cfg: Config, workspace,
+                     stream=None):
+    """One decode step: tokens int32 [B] at position pos; caches [L,B,NH,maxT,hs]."""
+    lib = load_library()
+    B = tokens.shape[0]
+    _check("gpt2_decode_step", lib.gpt2_decode_step(
+        _dev(logits, "logits"), _dev(probs, "probs"), _dev(tokens, "tokens"), int(pos),
+        _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(params, "params"), ctypes.byref(cfg), B,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return logits

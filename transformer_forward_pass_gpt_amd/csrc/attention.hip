@@ -1,0 +1,456 @@
+// Causal multi-head self-attention, softmax fused, on the gfx950 matrix cores.
+//
+// Method: the tiled, exact online-softmax forward ("Algorithm 1" of
+// FlashAttention, the optdl2025 project "Understand FlashAttention (I)"):
+// scores and probabilities are never written to HBM; each query keeps a
+// running max m and normaliser l and its output is rescaled as key blocks
+// arrive. Key blocks above the diagonal are never loaded or multiplied (the
+// "only doing lower triangular matmuls" item of llm.c's "State of the Union
+// [April 22, 2024]", big stones list). Heads are read straight out of the
+// packed qkv tensor and written straight into [B,T,C] (no permute/unpermute
+// pass; optdl2025 NanoGPT project: one projection for q, k, v and head
+// splitting).
+//
+// Mapping to 64-wide wavefronts: each wavefront owns 32 queries and computes
+// the TRANSPOSED score tile S^T = K Q^T with 32x32 MFMA tiles. In the 32x32
+// accumulator layout a lane owns one column (= one query) and 16 rows
+// (= keys), the other half-wave owning the other 16 keys of that query. So
+//  - the row max / row sum of the softmax is a per-lane loop plus ONE
+//    cross-half shuffle, and
+//  - the probabilities are already where the next product O^T = V^T P^T wants
+//    its B operand: no data movement between the two products.
+// The output O^T is likewise per-lane per-query, so the online rescale is a
+// per-lane scalar multiply.
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace gpt2 {
+
+template <typename T> struct MfmaS;  // one 16-byte fragment of the contraction
+template <> struct MfmaS<float> {
+    static __device__ __forceinline__ void run(f32x16& acc, const u32x4& a, const u32x4& b) {
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(b[e]),
+                                                      acc, 0, 0, 0);
+    }
+};
+template <> struct MfmaS<bf16> {
+    static __device__ __forceinline__ void run(f32x16& acc, const u32x4& a, const u32x4& b) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                     __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+};
+
+static constexpr int kBQ = 128;  // queries per workgroup (4 wavefronts x 32)
+static constexpr int kBKV = 64;  // keys per LDS block
+
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
+                                                        int Tn, int C, int NH, float sl2) {
+    constexpr bool F32 = std::is_same<T, float>::value;
+    constexpr int VE = Vec<T>::N;
+    constexpr int DT = (HS + 31) / 32;  // 32-row tiles of O^T (head dim padded to 32)
+    constexpr int HSP = DT * 32;
+    constexpr int KCH = HS / (2 * VE);  // 16-byte fragments along the head dim
+    static_assert(HS % (2 * VE) == 0, "head size must hold whole fragments");
+    constexpr int LDK = HS + VE;                // K block [kBKV][HS], 16-byte row pad
+    constexpr int LDV = F32 ? HSP + 8 : kBKV + 4;  // V: fp32 [key][d], bf16 transposed [d][key]
+    constexpr int VROWS = F32 ? kBKV : HSP;
+    __shared__ __attribute__((aligned(16))) T Ks[kBKV * LDK];
+    __shared__ __attribute__((aligned(16))) T Vs[VROWS * LDV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int qb = gridDim.x - 1 - blockIdx.x;  // longest query blocks start first
+    const int bh = blockIdx.y, b = bh / NH, hd = bh % NH;
+    const int q0 = qb * kBQ, qw = q0 + wid * 32;
+    const int64_t rs = 3 * (int64_t)C;
+    const T* base = qkv + (int64_t)b * Tn * rs;
+    const int qoff = hd * HS, koff = C + hd * HS, voff = 2 * C + hd * HS;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // Padded head columns of V (HS < 32) are never loaded: zero them once.
+    if (HS < HSP) {
+        for (int i = tid; i < VROWS * LDV; i += 256) {
+            int r = i / LDV, c = i % LDV;
+            bool pad = F32 ? (c >= HS) : (r >= HS);
+            if (pad) {
+                if constexpr (F32) Vs[i] = 0.f;
+                else Vs[i].bits = 0;
+            }
+        }
+    }
+
+    // Q fragments: the B operand of S^T = K Q^T. Lane (h, r32) holds query
+    // qw + r32, head dims kc*2*VE + h*VE .. +VE-1.
+    u32x4 qf[KCH];
+    {
+        const int q = qw + r32;
+#pragma unroll
+        for (int kc = 0; kc < KCH; kc++)
+            qf[kc] = q < Tn ? *reinterpret_cast<const u32x4*>(base + q * rs + qoff + kc * 2 * VE + h * VE)
+                            : zero;
+    }
+
+    f32x16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) o[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;  // for query qw + r32, in log2 units
+
+    const int kend = min(Tn, q0 + kBQ);
+    const int nkb = (kend + kBKV - 1) / kBKV;
+    constexpr int RV = HS / VE;  // 16-byte vectors per key row
+    for (int kb = 0; kb < nkb; kb++) {
+        const int k0 = kb * kBKV;
+        for (int li = tid; li < kBKV * RV; li += 256) {
+            const int r = li / RV, cv = li % RV, key = k0 + r;
+            u32x4 kx = zero, vx = zero;
+            if (key < Tn) {
+                kx = *reinterpret_cast<const u32x4*>(base + key * rs + koff + cv * VE);
+                vx = *reinterpret_cast<const u32x4*>(base + key * rs + voff + cv * VE);
+            }
+            *reinterpret_cast<u32x4*>(&Ks[r * LDK + cv * VE]) = kx;
+            if constexpr (F32) {
+                *reinterpret_cast<u32x4*>(&Vs[r * LDV + cv * VE]) = vx;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    Vs[(cv * 8 + e) * LDV + r].bits = (uint16_t)(vx[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        __syncthreads();
+        if (k0 <= qw + 31) {  // some of this wave's queries see this block
+            // S^T tiles: keys k0 + kt*32 + (8*(v/4) + 4*h + v%4), query qw + r32
+            f32x16 s[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++) {
+                s[kt] = f32x16{};
+#pragma unroll
+                for (int kc = 0; kc < KCH; kc++) {
+                    const u32x4 ka = *reinterpret_cast<const u32x4*>(
+                        &Ks[(kt * 32 + r32) * LDK + kc * 2 * VE + h * VE]);
+                    MfmaS<T>::run(s[kt], ka, qf[kc]);
+                }
+            }
+            const int q = qw + r32;
+            const bool need_mask = (k0 + kBKV - 1 > qw);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    float x = s[kt][v] * sl2;
+                    if (need_mask) {
+                        const int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        if (key > q) x = -INFINITY;
+                    }
+                    s[kt][v] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run, mx);  // finite: key 0 is in the first block
+            const float alpha = exp2f(m_run - m_new);
+            float ls = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const float p = exp2f(s[kt][v] - m_new);
+                    s[kt][v] = p;
+                    ls += p;
+                }
+            ls += __shfl_xor(ls, 32, 64);
+            l_run = l_run * alpha + ls;
+            m_run = m_new;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) o[dt][v] *= alpha;
+
+            // O^T += V^T P^T. The k slots of both operands name the same keys.
+            if constexpr (F32) {
+#pragma unroll
+                for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        const int kl = kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+#pragma unroll
+                        for (int dt = 0; dt < DT; dt++)
+                            o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[kl * LDV + dt * 32 + r32],
+                                                                        s[kt][v], o[dt], 0, 0, 0);
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ks++) {
+                        // slot (h, e): key 16ks + 4h + e (e<4), 16ks + 8 + 4h + e-4 (e>=4)
+                        u32x4 pb;
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            pb[e] = pack_bf16x2(s[kt][8 * ks + 2 * e], s[kt][8 * ks + 2 * e + 1]);
+                        const int kl = kt * 32 + 16 * ks + 4 * h;
+#pragma unroll
+                        for (int dt = 0; dt < DT; dt++) {
+                            const T* vr = &Vs[(dt * 32 + r32) * LDV + kl];
+                            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
+                            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
+                            const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                            MfmaS<T>::run(o[dt], va, pb);
+                        }
+                    }
+            }
+        }
+        __syncthreads();
+    }
+
+    // O^T register v of lane (h, r32): head dim dt*32 + 8*(v/4) + 4*h + v%4,
+    // query qw + r32. Four consecutive head dims per store.
+    const int q = qw + r32;
+    if (q < Tn) {
+        const float inv = 1.0f / l_run;
+        T* orow = out + ((int64_t)b * Tn + q) * C + hd * HS;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int d0 = dt * 32 + 8 * g + 4 * h;
+                if (d0 < HS) {
+                    const float x0 = o[dt][4 * g] * inv, x1 = o[dt][4 * g + 1] * inv;
+                    const float x2 = o[dt][4 * g + 2] * inv, x3 = o[dt][4 * g + 3] * inv;
+                    if constexpr (F32) {
+                        *reinterpret_cast<float4*>(orow + d0) = make_float4(x0, x1, x2, x3);
+                    } else {
+                        u32x2 pk = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+                        *reinterpret_cast<u32x2*>(orow + d0) = pk;
+                    }
+                }
+            }
+    }
+}
+
+template <typename T, int HS>
+static void launch_attn_hs(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s) {
+    const float sl2 = 1.4426950408889634f / sqrtf((float)HS);  // log2(e)/sqrt(hs)
+    dim3 grid((Tn + kBQ - 1) / kBQ, B * NH);
+    attention_kernel<T, HS><<<grid, 256, 0, s>>>(out, qkv, Tn, C, NH, sl2);
+}
+
+template <typename T>
+static void launch_attn_t(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s) {
+    switch (C / NH) {
+        case 16: launch_attn_hs<T, 16>(out, qkv, B, Tn, C, NH, s); break;
+        case 32: launch_attn_hs<T, 32>(out, qkv, B, Tn, C, NH, s); break;
+        case 64: launch_attn_hs<T, 64>(out, qkv, B, Tn, C, NH, s); break;
+        default: launch_attn_hs<T, 128>(out, qkv, B, Tn, C, NH, s); break;
+    }
+}
+
+int launch_attention(void* out, const void* qkv, int B, int T, int C, int NH, int dtype,
+                     hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_attn_t<bf16>((bf16*)out, (const bf16*)qkv, B, T, C, NH, s);
+    else
+        launch_attn_t<float>((float*)out, (const float*)qkv, B, T, C, NH, s);
+    return launch_status();
+}
+
+bool attention_head_size_ok(int hs) { return hs == 16 || hs == 32 || hs == 64 || hs == 128; }
+
+// ------------------------------------------------------------------ decode
+// One new query per sequence against a KV cache (optdl2025 NanoGPT project:
+// KV caching for autoregressive prediction). The keys 0..pos of each
+// (sequence, head) are split into chunks of kDecChunk; each workgroup streams
+// one chunk of K and V once with 16-byte loads and leaves an unnormalised
+// partial (o, m, l); a second kernel merges the partials in a fixed order,
+// so the result does not depend on scheduling.
+static constexpr int kDecChunk = 256;
+
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void decode_partial_kernel(float* __restrict__ part,
+                                                             const T* __restrict__ qkv_new,
+                                                             T* __restrict__ kc, T* __restrict__ vc,
+                                                             int pos, int maxT, int C, int NH,
+                                                             float sl2) {
+    constexpr int VE = Vec<T>::N;
+    constexpr int TPK = HS / VE;   // threads per key row
+    constexpr int KPP = 256 / TPK;  // keys per pass
+    static_assert(HS % VE == 0 && 64 % TPK == 0, "head size");
+    __shared__ float sc[kDecChunk];
+    __shared__ float red[KPP * HS];
+    __shared__ float sh[4];
+
+    const int split = blockIdx.x, nsplit = gridDim.x, bh = blockIdx.y;
+    const int b = bh / NH, hd = bh % NH;
+    const int j0 = split * kDecChunk, j1 = min(j0 + kDecChunk, pos + 1);
+    float* pp = part + ((int64_t)bh * nsplit + split) * (HS + 2);
+    const int tid = threadIdx.x, sub = tid % TPK, kg = tid / TPK;
+    const int lane = tid & 63, w = tid >> 6;
+    const T* qrow = qkv_new + (int64_t)b * 3 * C;
+    const T* knew = qrow + C + hd * HS;
+    const T* vnew = qrow + 2 * C + hd * HS;
+    T* K = kc + (int64_t)bh * maxT * HS;
+    T* Vc = vc + (int64_t)bh * maxT * HS;
+
+    if (j0 >= j1) {  // empty chunk: neutral partial
+        if (tid < HS) pp[tid] = 0.f;
+        if (tid == 0) { pp[HS] = -INFINITY; pp[HS + 1] = 0.f; }
+        return;
+    }
+    if (pos >= j0 && pos < j1 && tid < TPK) {  // this step's k, v into the cache
+        *reinterpret_cast<u32x4*>(K + (int64_t)pos * HS + sub * VE) =
+            *reinterpret_cast<const u32x4*>(knew + sub * VE);
+        *reinterpret_cast<u32x4*>(Vc + (int64_t)pos * HS + sub * VE) =
+            *reinterpret_cast<const u32x4*>(vnew + sub * VE);
+    }
+    float q[VE];
+    load_vec(qrow + hd * HS + sub * VE, q);
+    for (int j = j0 + kg; j < j1; j += KPP) {
+        float k[VE];
+        load_vec(j == pos ? knew + sub * VE : K + (int64_t)j * HS + sub * VE, k);
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; e++) d += q[e] * k[e];
+#pragma unroll
+        for (int o = TPK / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+        if (sub == 0) sc[j - j0] = d * sl2;
+    }
+    __syncthreads();
+    const int n = j1 - j0;
+    float mx = -INFINITY;
+    for (int i = tid; i < n; i += 256) mx = fmaxf(mx, sc[i]);
+    mx = wave_max(mx);
+    if (lane == 0) sh[w] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+    __syncthreads();
+    float ls = 0.f;
+    for (int i = tid; i < n; i += 256) {
+        const float p = exp2f(sc[i] - mx);
+        sc[i] = p;
+        ls += p;
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) sh[w] = ls;
+    __syncthreads();
+    ls = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+    float acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; e++) acc[e] = 0.f;
+    for (int j = j0 + kg; j < j1; j += KPP) {
+        float v[VE];
+        load_vec(j == pos ? vnew + sub * VE : Vc + (int64_t)j * HS + sub * VE, v);
+        const float p = sc[j - j0];
+#pragma unroll
+        for (int e = 0; e < VE; e++) acc[e] += p * v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < VE; e++) red[kg * HS + sub * VE + e] = acc[e];
+    __syncthreads();
+    if (tid < HS) {
+        float s = 0.f;
+        for (int g = 0; g < KPP; g++) s += red[g * HS + tid];
+        pp[tid] = s;
+    }
+    if (tid == 0) {
+        pp[HS] = mx;
+        pp[HS + 1] = ls;
+    }
+}
+
+template <typename T, int HS>
+__global__ __launch_bounds__(HS) void decode_combine_kernel(T* __restrict__ out,
+                                                            const float* __restrict__ part,
+                                                            int nsplit, int C, int NH) {
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH, d = threadIdx.x;
+    const float* pp = part + (int64_t)bh * nsplit * (HS + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; s++) M = fmaxf(M, pp[s * (HS + 2) + HS]);
+    float L = 0.f, o = 0.f;
+    for (int s = 0; s < nsplit; s++) {
+        const float m = pp[s * (HS + 2) + HS];
+        const float wgt = m == -INFINITY ? 0.f : exp2f(m - M);
+        L += pp[s * (HS + 2) + HS + 1] * wgt;
+        o += pp[s * (HS + 2) + d] * wgt;
+    }
+    store_scalar(out + (int64_t)b * C + hd * HS + d, o / L);
+}
+
+int64_t decode_workspace_bytes(int B, int C, int NH, int maxT) {
+    const int hs = C / NH;
+    const int64_t nsplit = (maxT + kDecChunk - 1) / kDecChunk;
+    return (int64_t)B * NH * nsplit * (hs + 2) * 4;
+}
+
+template <typename T, int HS>
+static void launch_decode_hs(T* out, const T* qkv_new, T* kc, T* vc, int B, int pos, int maxT,
+                             int C, int NH, float* part, hipStream_t s) {
+    const float sl2 = 1.4426950408889634f / sqrtf((float)HS);
+    const int nsplit = (pos + 1 + kDecChunk - 1) / kDecChunk;
+    decode_partial_kernel<T, HS><<<dim3(nsplit, B * NH), 256, 0, s>>>(part, qkv_new, kc, vc, pos,
+                                                                       maxT, C, NH, sl2);
+    decode_combine_kernel<T, HS><<<B * NH, HS, 0, s>>>(out, part, nsplit, C, NH);
+}
+
+template <typename T>
+static void launch_decode_t(T* out, const T* qkv_new, T* kc, T* vc, int B, int pos, int maxT,
+                            int C, int NH, float* part, hipStream_t s) {
+    switch (C / NH) {
+        case 16: launch_decode_hs<T, 16>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s); break;
+        case 32: launch_decode_hs<T, 32>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s); break;
+        case 64: launch_decode_hs<T, 64>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s); break;
+        default: launch_decode_hs<T, 128>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s); break;
+    }
+}
+
+int launch_attention_decode(void* out, const void* qkv_new, void* kcache, void* vcache, int B,
+                            int pos, int maxT, int C, int NH, int dtype, float* part,
+                            hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_decode_t<bf16>((bf16*)out, (const bf16*)qkv_new, (bf16*)kcache, (bf16*)vcache, B,
+                              pos, maxT, C, NH, part, s);
+    else
+        launch_decode_t<float>((float*)out, (const float*)qkv_new, (float*)kcache, (float*)vcache,
+                               B, pos, maxT, C, NH, part, s);
+    return launch_status();
+}
+
+}  // namespace gpt2
+
+using namespace gpt2;
+
+extern "C" int attention_forward(void* out, const void* qkv, int B, int T, int C, int NH,
+                                 int dtype, void* stream) {
+    if (!valid_dtype(dtype) || B < 0 || T < 0 || C < 0 || NH <= 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if ((int64_t)B * T == 0) return GPT2_OK;
+    if (!out || !qkv || C == 0 || C % NH) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!attention_head_size_ok(C / NH) || !aligned16(out) || !aligned16(qkv))
+        return GPT2_ERR_UNSUPPORTED;
+    if (out == qkv) return GPT2_ERR_INVALID_ARGUMENT;
+    return launch_attention(out, qkv, B, T, C, NH, dtype, (hipStream_t)stream);
+}
+
+extern "C" int64_t attention_decode_workspace_bytes(int B, int C, int NH, int maxT) {
+    if (B < 0 || C <= 0 || NH <= 0 || C % NH || maxT <= 0) return -1;
+    return decode_workspace_bytes(B, C, NH, maxT);
+}
+
+extern "C" int attention_decode_forward(void* out, const void* qkv_new, void* kcache, void* vcache,
+                                        int B, int pos, int maxT, int C, int NH, int dtype,
+                                        void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!valid_dtype(dtype) || B < 0 || C < 0 || NH <= 0 || maxT <= 0 || pos < 0 || pos >= maxT)
+        return GPT2_ERR_INVALID_ARGUMENT;
+    if (B == 0) return GPT2_OK;
+    if (!out || !qkv_new || !kcache || !vcache || !workspace || C == 0 || C % NH)
+        return GPT2_ERR_INVALID_ARGUMENT;
+    if (!attention_head_size_ok(C / NH) || !aligned16(out) || !aligned16(qkv_new) ||
+        !aligned16(kcache) || !aligned16(vcache) || !aligned16(workspace))
+        return GPT2_ERR_UNSUPPORTED;
+    if (workspace_bytes < decode_workspace_bytes(B, C, NH, maxT)) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    return launch_attention_decode(out, qkv_new, kcache, vcache, B, pos, maxT, C, NH, dtype,
+                                   (float*)workspace, (hipStream_t)stream);
+}

@@ -1,0 +1,90 @@
+// Device helpers shared by the gfx950 kernels: storage types, 16-byte vector
+// loads/stores with fp32 unpacking, bf16 rounding, wavefront reductions, the
+// MFMA operand types, and the host-side status plumbing.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gpt2fwd.h"
+
+namespace gpt2 {
+
+// bf16 storage: the raw 16-bit pattern (upper half of an fp32).
+struct bf16 {
+    uint16_t bits;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Elements of T per 16-byte vector.
+template <typename T> struct Vec;
+template <> struct Vec<float> { static constexpr int N = 4; };
+template <> struct Vec<bf16> { static constexpr int N = 8; };
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// 16-byte load of Vec<T>::N elements, widened to fp32.
+__device__ __forceinline__ void load_vec(const float* p, float (&v)[4]) {
+    float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+__device__ __forceinline__ void load_vec(const bf16* p, float (&v)[8]) {
+    uint4 x = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_to_f32(x.x & 0xffffu); v[1] = bf16_to_f32(x.x >> 16);
+    v[2] = bf16_to_f32(x.y & 0xffffu); v[3] = bf16_to_f32(x.y >> 16);
+    v[4] = bf16_to_f32(x.z & 0xffffu); v[5] = bf16_to_f32(x.z >> 16);
+    v[6] = bf16_to_f32(x.w & 0xffffu); v[7] = bf16_to_f32(x.w >> 16);
+}
+__device__ __forceinline__ void store_vec(float* p, const float (&v)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_vec(bf16* p, const float (&v)[8]) {
+    uint4 x;
+    x.x = pack_bf16x2(v[0], v[1]); x.y = pack_bf16x2(v[2], v[3]);
+    x.z = pack_bf16x2(v[4], v[5]); x.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = x;
+}
+
+__device__ __forceinline__ float load_scalar(const float* p) { return *p; }
+__device__ __forceinline__ float load_scalar(const bf16* p) { return bf16_to_f32(p->bits); }
+__device__ __forceinline__ void store_scalar(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_scalar(bf16* p, float v) { p->bits = (uint16_t)f32_to_bf16(v); }
+
+// Reductions across the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+}  // namespace gpt2
+
+// ------------------------------------------------------------------ host side
+namespace gpt2 {
+void set_last_hip_error(int e);
+// Status after a launch: GPT2_OK, or GPT2_ERR_HIP with the code recorded.
+int launch_status();
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool valid_dtype(int d) { return d == GPT2_F32 || d == GPT2_BF16; }
+inline int elem_size(int d) { return d == GPT2_BF16 ? 2 : 4; }
+}  // namespace gpt2

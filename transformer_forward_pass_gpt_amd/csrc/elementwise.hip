@@ -1,0 +1,153 @@
+// HBM-streaming kernels: token+position embedding, residual add, tanh-GELU.
+// Each thread moves 16-byte vectors in a grid-stride loop, so every wavefront
+// issues fully coalesced 1 KiB requests; arithmetic is fp32 and bf16 results
+// are rounded to nearest even.
+#include "common.h"
+
+namespace gpt2 {
+
+static constexpr int kThreads = 256;
+
+static unsigned stream_grid(int64_t nvec) {
+    // 256 CUs x 8 resident workgroups keeps enough requests in flight; the
+    // grid-stride loop covers the rest.
+    int64_t g = (nvec + kThreads - 1) / kThreads;
+    if (g > 2048) g = 2048;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+// out[b,t,:] = wte[tokens[b,t],:] + wpe[t,:]
+// (ECE408 Final Project - GPT-2, Milestone 1, kernel table: Encoder.)
+template <typename T>
+__global__ __launch_bounds__(kThreads) void encoder_kernel(T* __restrict__ out,
+                                                           const int32_t* __restrict__ tokens,
+                                                           const T* __restrict__ wte,
+                                                           const T* __restrict__ wpe, int T_, int C,
+                                                           int64_t nvec) {
+    constexpr int V = Vec<T>::N;
+    const int cv = C / V;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < nvec;
+         i += (int64_t)gridDim.x * kThreads) {
+        int64_t n = i / cv;
+        int c = (int)(i - n * cv) * V;
+        int t = (int)(n % T_);
+        int tok = tokens[n];
+        float a[V], b[V];
+        load_vec(wte + (int64_t)tok * C + c, a);
+        load_vec(wpe + (int64_t)t * C + c, b);
+#pragma unroll
+        for (int j = 0; j < V; j++) a[j] += b[j];
+        store_vec(out + n * C + c, a);
+    }
+}
+
+// out = a + b  (ECE408 Milestone 1, kernel table: Residual.)
+template <typename T>
+__global__ __launch_bounds__(kThreads) void residual_kernel(T* out, const T* a, const T* b,
+                                                            int64_t n) {
+    constexpr int V = Vec<T>::N;
+    const int64_t nvec = n / V;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < nvec; i += stride) {
+        float x[V], y[V];
+        load_vec(a + i * V, x);
+        load_vec(b + i * V, y);
+#pragma unroll
+        for (int j = 0; j < V; j++) x[j] += y[j];
+        store_vec(out + i * V, x);
+    }
+    for (int64_t i = nvec * V + blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n; i += stride)
+        store_scalar(out + i, load_scalar(a + i) + load_scalar(b + i));
+}
+
+// GELU, tanh form: x/2 (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+// Evaluated through the identity 1 + tanh(u) = 2 / (1 + e^{-2u}), so
+// g(x) = x / (1 + e^{-2u}): no cancellation for u << 0, and e^{-2u} = inf
+// gives the correct limit -0.
+// (ECE408 Milestone 1, kernel table: GELU.)
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float k2 = -2.0f * 0.7978845608028654f;  // -2 sqrt(2/pi)
+    float u = x * (1.0f + 0.044715f * x * x);
+    return x / (1.0f + expf(k2 * u));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gelu_kernel(T* out, const T* inp, int64_t n) {
+    constexpr int V = Vec<T>::N;
+    const int64_t nvec = n / V;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < nvec; i += stride) {
+        float x[V];
+        load_vec(inp + i * V, x);
+#pragma unroll
+        for (int j = 0; j < V; j++) x[j] = gelu_tanh(x[j]);
+        store_vec(out + i * V, x);
+    }
+    for (int64_t i = nvec * V + blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n; i += stride)
+        store_scalar(out + i, gelu_tanh(load_scalar(inp + i)));
+}
+
+int launch_encoder(void* out, const int32_t* tokens, const void* wte, const void* wpe, int B,
+                   int T, int C, int dtype, hipStream_t s) {
+    int64_t nvec = (int64_t)B * T * C / (dtype == GPT2_BF16 ? 8 : 4);
+    if (dtype == GPT2_BF16)
+        encoder_kernel<bf16><<<stream_grid(nvec), kThreads, 0, s>>>(
+            (bf16*)out, tokens, (const bf16*)wte, (const bf16*)wpe, T, C, nvec);
+    else
+        encoder_kernel<float><<<stream_grid(nvec), kThreads, 0, s>>>(
+            (float*)out, tokens, (const float*)wte, (const float*)wpe, T, C, nvec);
+    return launch_status();
+}
+
+int launch_residual(void* out, const void* a, const void* b, int64_t n, int dtype,
+                    hipStream_t s) {
+    int64_t nvec = n / (dtype == GPT2_BF16 ? 8 : 4) + 1;
+    if (dtype == GPT2_BF16)
+        residual_kernel<bf16><<<stream_grid(nvec), kThreads, 0, s>>>((bf16*)out, (const bf16*)a,
+                                                                    (const bf16*)b, n);
+    else
+        residual_kernel<float><<<stream_grid(nvec), kThreads, 0, s>>>(
+            (float*)out, (const float*)a, (const float*)b, n);
+    return launch_status();
+}
+
+int launch_gelu(void* out, const void* inp, int64_t n, int dtype, hipStream_t s) {
+    int64_t nvec = n / (dtype == GPT2_BF16 ? 8 : 4) + 1;
+    if (dtype == GPT2_BF16)
+        gelu_kernel<bf16><<<stream_grid(nvec), kThreads, 0, s>>>((bf16*)out, (const bf16*)inp, n);
+    else
+        gelu_kernel<float><<<stream_grid(nvec), kThreads, 0, s>>>((float*)out, (const float*)inp, n);
+    return launch_status();
+}
+
+}  // namespace gpt2
+
+// ------------------------------------------------------------------ C ABI
+using namespace gpt2;
+
+extern "C" int encoder_forward(void* out, const int32_t* tokens, const void* wte, const void* wpe,
+                               int B, int T, int C, int dtype, void* stream) {
+    if (!valid_dtype(dtype) || B < 0 || T < 0 || C < 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if ((int64_t)B * T * C == 0) return GPT2_OK;
+    if (!out || !tokens || !wte || !wpe) return GPT2_ERR_INVALID_ARGUMENT;
+    if (C % 8 || !aligned16(out) || !aligned16(wte) || !aligned16(wpe)) return GPT2_ERR_UNSUPPORTED;
+    return launch_encoder(out, tokens, wte, wpe, B, T, C, dtype, (hipStream_t)stream);
+}
+
+extern "C" int residual_forward(void* out, const void* a, const void* b, int64_t n, int dtype,
+                                void* stream) {
+    if (!valid_dtype(dtype) || n < 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (n == 0) return GPT2_OK;
+    if (!out || !a || !b) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!aligned16(out) || !aligned16(a) || !aligned16(b)) return GPT2_ERR_UNSUPPORTED;
+    return launch_residual(out, a, b, n, dtype, (hipStream_t)stream);
+}
+
+extern "C" int gelu_forward(void* out, const void* inp, int64_t n, int dtype, void* stream) {
+    if (!valid_dtype(dtype) || n < 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (n == 0) return GPT2_OK;
+    if (!out || !inp) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!aligned16(out) || !aligned16(inp)) return GPT2_ERR_UNSUPPORTED;
+    return launch_gelu(out, inp, n, dtype, (hipStream_t)stream);
+}

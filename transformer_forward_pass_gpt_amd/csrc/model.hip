@@ -1,0 +1,239 @@
+// The whole forward pass and the KV-cache decode step, composed from the
+// per-step launchers on one stream, plus the status plumbing of the C ABI.
+//
+// Block order (GPT-2, pre-LayerNorm):
+//   x <- x + attproj(attention(ln1(x)))
+//   x <- x + fcproj(gelu(fc(ln2(x))))
+// then lnf, logits against the tied token embedding, vocabulary softmax.
+// The steps are those of ECE408 Final Project - GPT-2, Milestone 1 (kernel
+// table); llm.c "State of the Union [April 22, 2024]" (step breakdown) splits
+// the same pass into encoder, forward blocks and classifier.
+#include "common.h"
+
+namespace gpt2 {
+
+static thread_local int g_last_hip_error = 0;
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+int launch_status() {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return GPT2_ERR_HIP;
+    }
+    return GPT2_OK;
+}
+
+int launch_encoder(void*, const int32_t*, const void*, const void*, int, int, int, int, hipStream_t);
+int launch_residual(void*, const void*, const void*, int64_t, int, hipStream_t);
+int launch_gelu(void*, const void*, int64_t, int, hipStream_t);
+int launch_layernorm(void*, float*, float*, const void*, const void*, const void*, int, int, float,
+                     int, hipStream_t);
+int launch_softmax(void*, const void*, int, int, int, int, hipStream_t);
+int launch_matmul(void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
+int launch_attention(void*, const void*, int, int, int, int, int, hipStream_t);
+int launch_attention_decode(void*, const void*, void*, void*, int, int, int, int, int, int, float*,
+                            hipStream_t);
+int64_t decode_workspace_bytes(int B, int C, int NH, int maxT);
+bool attention_head_size_ok(int hs);
+
+// Element offsets into the flat parameter buffer.
+struct ParamOffsets {
+    int64_t wte, wpe, ln1_g, ln1_b, qkv_w, qkv_b, ap_w, ap_b, ln2_g, ln2_b, fc_w, fc_b, fp_w, fp_b,
+        lnf_g, lnf_b, total;
+};
+
+static ParamOffsets param_offsets(const gpt2_config& c) {
+    const int64_t C = c.C, L = c.L;
+    ParamOffsets o;
+    int64_t p = 0;
+    o.wte = p;   p += (int64_t)c.Vp * C;
+    o.wpe = p;   p += (int64_t)c.maxT * C;
+    o.ln1_g = p; p += L * C;
+    o.ln1_b = p; p += L * C;
+    o.qkv_w = p; p += L * 3 * C * C;
+    o.qkv_b = p; p += L * 3 * C;
+    o.ap_w = p;  p += L * C * C;
+    o.ap_b = p;  p += L * C;
+    o.ln2_g = p; p += L * C;
+    o.ln2_b = p; p += L * C;
+    o.fc_w = p;  p += L * 4 * C * C;
+    o.fc_b = p;  p += L * 4 * C;
+    o.fp_w = p;  p += L * 4 * C * C;
+    o.fp_b = p;  p += L * C;
+    o.lnf_g = p; p += C;
+    o.lnf_b = p; p += C;
+    o.total = p;
+    return o;
+}
+
+static bool config_ok(const gpt2_config* c) {
+    return c && c->L >= 1 && c->C > 0 && c->NH > 0 && c->C % c->NH == 0 && c->V > 0 &&
+           c->Vp >= c->V && c->maxT > 0 && valid_dtype(c->dtype) && c->ln_eps >= 0.f;
+}
+static bool config_supported(const gpt2_config* c) {
+    return c->C % 8 == 0 && c->C <= 4096 && c->Vp % 8 == 0 && c->Vp <= 131072 &&
+           attention_head_size_ok(c->C / c->NH);
+}
+
+static inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+// Workspace: residual stream x [N,C], LayerNorm output [N,C], qkv [N,3C],
+// attention output [N,C], projection output [N,C], MLP hidden [N,4C].
+struct Workspace {
+    char *x, *ln, *qkv, *att, *tmp, *fc;
+    float* part;
+    int64_t bytes;
+};
+static Workspace carve(char* base, int64_t N, int64_t C, int es, int64_t part_bytes) {
+    Workspace w;
+    int64_t o = 0;
+    auto take = [&](int64_t n) { char* p = base ? base + o : nullptr; o += align256(n); return p; };
+    w.x = take(N * C * es);
+    w.ln = take(N * C * es);
+    w.qkv = take(N * 3 * C * es);
+    w.att = take(N * C * es);
+    w.tmp = take(N * C * es);
+    w.fc = take(N * 4 * C * es);
+    w.part = (float*)take(part_bytes);
+    w.bytes = o;
+    return w;
+}
+
+}  // namespace gpt2
+
+using namespace gpt2;
+
+#define CHECK(call)                       \
+    do {                                  \
+        int rc_ = (call);                 \
+        if (rc_ != GPT2_OK) return rc_;   \
+    } while (0)
+
+extern "C" const char* gpt2_status_string(int status) {
+    switch (status) {
+        case GPT2_OK: return "ok";
+        case GPT2_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case GPT2_ERR_UNSUPPORTED: return "unsupported shape, head size, width or alignment";
+        case GPT2_ERR_HIP: return "HIP launch error (see gpt2_last_hip_error)";
+        case GPT2_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int gpt2_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" int64_t gpt2_param_count(const gpt2_config* cfg) {
+    if (!config_ok(cfg)) return -1;
+    return param_offsets(*cfg).total;
+}
+
+extern "C" int64_t gpt2_workspace_bytes(const gpt2_config* cfg, int B, int T) {
+    if (!config_ok(cfg) || B < 0 || T < 0) return -1;
+    return carve(nullptr, (int64_t)B * T, cfg->C, elem_size(cfg->dtype), 0).bytes;
+}
+
+extern "C" int gpt2_forward(void* logits, void* probs, const int32_t* tokens, const void* params,
+                            const gpt2_config* cfg, int B, int T, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+    if (!config_ok(cfg) || B < 0 || T < 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if ((int64_t)B * T == 0) return GPT2_OK;
+    if (!logits || !tokens || !params || !workspace || T > cfg->maxT) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!config_supported(cfg) || !aligned16(logits) || !aligned16(params) ||
+        !aligned16(workspace) || (probs && !aligned16(probs)))
+        return GPT2_ERR_UNSUPPORTED;
+    if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
+    const int64_t N = (int64_t)B * T;
+    const int C = cfg->C, L = cfg->L, dt = cfg->dtype, es = elem_size(dt);
+    if (N > INT32_MAX / 4) return GPT2_ERR_UNSUPPORTED;
+    Workspace w = carve((char*)workspace, N, C, es, 0);
+    if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    const ParamOffsets po = param_offsets(*cfg);
+    const char* P = (const char*)params;
+    auto at = [&](int64_t off) { return (const void*)(P + off * es); };
+    hipStream_t s = (hipStream_t)stream;
+    const int n = (int)N;
+    const int64_t C64 = C;
+
+    CHECK(launch_encoder(w.x, tokens, at(po.wte), at(po.wpe), B, T, C, dt, s));
+    for (int l = 0; l < L; l++) {
+        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln1_g + l * C64),
+                               at(po.ln1_b + l * C64), n, C, cfg->ln_eps, dt, s));
+        CHECK(launch_matmul(w.qkv, w.ln, at(po.qkv_w + l * 3 * C64 * C64), at(po.qkv_b + l * 3 * C64),
+                            n, C, 3 * C, dt, s));
+        CHECK(launch_attention(w.att, w.qkv, B, T, C, cfg->NH, dt, s));
+        CHECK(launch_matmul(w.tmp, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), n, C, C,
+                            dt, s));
+        CHECK(launch_residual(w.x, w.x, w.tmp, N * C64, dt, s));
+        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln2_g + l * C64),
+                               at(po.ln2_b + l * C64), n, C, cfg->ln_eps, dt, s));
+        CHECK(launch_matmul(w.fc, w.ln, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), n,
+                            C, 4 * C, dt, s));
+        CHECK(launch_gelu(w.fc, w.fc, N * 4 * C64, dt, s));
+        CHECK(launch_matmul(w.tmp, w.fc, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), n,
+                            4 * C, C, dt, s));
+        CHECK(launch_residual(w.x, w.x, w.tmp, N * C64, dt, s));
+    }
+    CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.lnf_g), at(po.lnf_b), n, C,
+                           cfg->ln_eps, dt, s));
+    CHECK(launch_matmul(logits, w.ln, at(po.wte), nullptr, n, C, cfg->Vp, dt, s));
+    if (probs) CHECK(launch_softmax(probs, logits, n, cfg->V, cfg->Vp, dt, s));
+    return GPT2_OK;
+}
+
+extern "C" int64_t gpt2_decode_workspace_bytes(const gpt2_config* cfg, int B) {
+    if (!config_ok(cfg) || B < 0) return -1;
+    return carve(nullptr, B, cfg->C, elem_size(cfg->dtype),
+                 decode_workspace_bytes(B, cfg->C, cfg->NH, cfg->maxT))
+        .bytes;
+}
+
+extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens, int pos,
+                                void* kcache, void* vcache, const void* params,
+                                const gpt2_config* cfg, int B, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+    if (!config_ok(cfg) || B < 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (B == 0) return GPT2_OK;
+    if (!logits || !tokens || !params || !kcache || !vcache || !workspace || pos < 0 ||
+        pos >= cfg->maxT)
+        return GPT2_ERR_INVALID_ARGUMENT;
+    if (!config_supported(cfg) || !aligned16(logits) || !aligned16(params) || !aligned16(kcache) ||
+        !aligned16(vcache) || !aligned16(workspace) || (probs && !aligned16(probs)))
+        return GPT2_ERR_UNSUPPORTED;
+    if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
+    const int C = cfg->C, L = cfg->L, NH = cfg->NH, dt = cfg->dtype, es = elem_size(dt);
+    Workspace w = carve((char*)workspace, B, C, es, decode_workspace_bytes(B, C, NH, cfg->maxT));
+    if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    const ParamOffsets po = param_offsets(*cfg);
+    const char* P = (const char*)params;
+    auto at = [&](int64_t off) { return (const void*)(P + off * es); };
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t C64 = C;
+    const int64_t layer_elems = (int64_t)B * NH * cfg->maxT * (C / NH);
+
+    CHECK(launch_encoder(w.x, tokens, at(po.wte), at(po.wpe + (int64_t)pos * C64), B, 1, C, dt, s));
+    for (int l = 0; l < L; l++) {
+        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln1_g + l * C64),
+                               at(po.ln1_b + l * C64), B, C, cfg->ln_eps, dt, s));
+        CHECK(launch_matmul(w.qkv, w.ln, at(po.qkv_w + l * 3 * C64 * C64), at(po.qkv_b + l * 3 * C64),
+                            B, C, 3 * C, dt, s));
+        CHECK(launch_attention_decode(w.att, w.qkv, (char*)kcache + l * layer_elems * es,
+                                      (char*)vcache + l * layer_elems * es, B, pos, cfg->maxT, C, NH,
+                                      dt, w.part, s));
+        CHECK(launch_matmul(w.tmp, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), B, C, C,
+                            dt, s));
+        CHECK(launch_residual(w.x, w.x, w.tmp, B * C64, dt, s));
+        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln2_g + l * C64),
+                               at(po.ln2_b + l * C64), B, C, cfg->ln_eps, dt, s));
+        CHECK(launch_matmul(w.fc, w.ln, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), B,
+                            C, 4 * C, dt, s));
+        CHECK(launch_gelu(w.fc, w.fc, B * 4 * C64, dt, s));
+        CHECK(launch_matmul(w.tmp, w.fc, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), B,
+                            4 * C, C, dt, s));
+        CHECK(launch_residual(w.x, w.x, w.tmp, B * C64, dt, s));
+    }
+    CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.lnf_g), at(po.lnf_b), B, C,
+                           cfg->ln_eps, dt, s));
+    CHECK(launch_matmul(logits, w.ln, at(po.wte), nullptr, B, C, cfg->Vp, dt, s));
+    if (probs) CHECK(launch_softmax(probs, logits, B, cfg->V, cfg->Vp, dt, s));
+    return GPT2_OK;
+}

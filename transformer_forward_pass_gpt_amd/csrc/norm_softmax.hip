@@ -1,0 +1,250 @@
+// Row kernels: LayerNorm (one wavefront per row, the row held in registers)
+// and the vocabulary softmax (one workgroup per row, the row held in
+// registers). Each reads its input once and writes its output once; the
+// statistics are reduced with cross-lane shuffles in fp32.
+#include <math.h>
+
+#include "common.h"
+
+namespace gpt2 {
+
+// ------------------------------------------------------------------ LayerNorm
+// mu = mean(x), var = mean((x-mu)^2), rstd = 1/sqrt(var+eps),
+// y = (x-mu)*rstd*gamma + beta.  Two passes over the registers, so the
+// variance is the centred sum of squares, not E[x^2]-mu^2.
+// (ECE408 Final Project - GPT-2, Milestone 1, kernel table: LayerNorm;
+// llm.c "State of the Union [April 22, 2024]", kernel summaries:
+// layernorm_forward_kernel3.)
+template <typename T, int VPL>
+__global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, float* __restrict__ mean,
+                                                        float* __restrict__ rstd,
+                                                        const T* __restrict__ inp,
+                                                        const T* __restrict__ gamma,
+                                                        const T* __restrict__ beta, int N, int C,
+                                                        float eps) {
+    constexpr int V = Vec<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N) return;  // wave-uniform
+    const T* x = inp + (int64_t)row * C;
+    const int cv = C / V;
+    float v[VPL][V];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        int idx = lane + i * 64;
+        if (idx < cv) {
+            load_vec(x + idx * V, v[i]);
+#pragma unroll
+            for (int j = 0; j < V; j++) s += v[i][j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; j++) v[i][j] = 0.f;
+        }
+    }
+    s = wave_sum(s);
+    const float mu = s / (float)C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        if (lane + i * 64 < cv) {
+#pragma unroll
+            for (int j = 0; j < V; j++) {
+                float d = v[i][j] - mu;
+                ss += d * d;
+            }
+        }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)C + eps);
+    T* y = out + (int64_t)row * C;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        int idx = lane + i * 64;
+        if (idx < cv) {
+            float g[V], b[V];
+            load_vec(gamma + idx * V, g);
+            load_vec(beta + idx * V, b);
+#pragma unroll
+            for (int j = 0; j < V; j++) v[i][j] = (v[i][j] - mu) * r * g[j] + b[j];
+            store_vec(y + idx * V, v[i]);
+        }
+    }
+    if (lane == 0) {
+        if (mean) mean[row] = mu;
+        if (rstd) rstd[row] = r;
+    }
+}
+
+template <typename T>
+static void launch_ln_t(T* out, float* mean, float* rstd, const T* inp, const T* g, const T* b,
+                        int N, int C, float eps, hipStream_t s) {
+    const int vpl = (C / Vec<T>::N + 63) / 64;
+    dim3 grid((N + 3) / 4), block(256);
+    if (vpl <= 1)
+        layernorm_kernel<T, 1><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
+    else if (vpl <= 2)
+        layernorm_kernel<T, 2><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
+    else if (vpl <= 3)
+        layernorm_kernel<T, 3><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
+    else if (vpl <= 4)
+        layernorm_kernel<T, 4><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
+    else if (vpl <= 8)
+        layernorm_kernel<T, 8><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
+    else
+        layernorm_kernel<T, 16><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
+}
+
+int launch_layernorm(void* out, float* mean, float* rstd, const void* inp, const void* gamma,
+                     const void* beta, int N, int C, float eps, int dtype, hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_ln_t<bf16>((bf16*)out, mean, rstd, (const bf16*)inp, (const bf16*)gamma,
+                          (const bf16*)beta, N, C, eps, s);
+    else
+        launch_ln_t<float>((float*)out, mean, rstd, (const float*)inp, (const float*)gamma,
+                           (const float*)beta, N, C, eps, s);
+    return launch_status();
+}
+
+// ------------------------------------------------------------ vocab softmax
+// probs[v] = exp(l_v - m) / sum_{u<V} exp(l_u - m) for v < V, 0 for v >= V,
+// m = max_{u<V} l_u. One workgroup of up to 1024 threads per row; each
+// thread keeps PT 16-byte vectors of the row in registers between the max,
+// the sum and the write, so HBM sees one read and one write per element.
+// (llm.c "State of the Union", kernel summaries: the softmax half of
+// fused_classifier_kernel3.)
+template <int NW>
+__device__ __forceinline__ float block_max(float x, float* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    x = wave_max(x);
+    if (lane == 0) sh[w] = x;
+    __syncthreads();
+    x = lane < NW ? sh[lane] : -INFINITY;
+    x = wave_max(x);
+    __syncthreads();
+    return x;
+}
+template <int NW>
+__device__ __forceinline__ float block_sum(float x, float* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    x = wave_sum(x);
+    if (lane == 0) sh[w] = x;
+    __syncthreads();
+    x = lane < NW ? sh[lane] : 0.f;
+    x = wave_sum(x);
+    __syncthreads();
+    return x;
+}
+
+template <typename T, int PT, int NT>
+__global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, const T* __restrict__ logits,
+                                                     int V, int Vp) {
+    constexpr int VE = Vec<T>::N;
+    constexpr int NW = NT / 64;
+    __shared__ float sh[NW];
+    const int64_t row = blockIdx.x;
+    const T* x = logits + row * Vp;
+    T* y = probs + row * Vp;
+    const int cv = Vp / VE;
+    float v[PT][VE];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PT; i++) {
+        int idx = threadIdx.x + i * NT;
+        if (idx < cv) {
+            load_vec(x + idx * VE, v[i]);
+#pragma unroll
+            for (int j = 0; j < VE; j++) {
+                if (idx * VE + j >= V) v[i][j] = -INFINITY;
+                m = fmaxf(m, v[i][j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < VE; j++) v[i][j] = -INFINITY;
+        }
+    }
+    m = block_max<NW>(m, sh);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < PT; i++)
+#pragma unroll
+        for (int j = 0; j < VE; j++) {
+            v[i][j] = expf(v[i][j] - m);  // exp(-inf) = 0 for padding
+            s += v[i][j];
+        }
+    s = block_sum<NW>(s, sh);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < PT; i++) {
+        int idx = threadIdx.x + i * NT;
+        if (idx < cv) {
+#pragma unroll
+            for (int j = 0; j < VE; j++) v[i][j] *= inv;
+            store_vec(y + idx * VE, v[i]);
+        }
+    }
+}
+
+template <typename T>
+static void launch_softmax_t(T* probs, const T* logits, int N, int V, int Vp, hipStream_t s) {
+    const int cv = Vp / Vec<T>::N;
+    dim3 grid(N);
+    if (cv <= 256) {
+        softmax_kernel<T, 1, 256><<<grid, 256, 0, s>>>(probs, logits, V, Vp);
+        return;
+    }
+    const int pt = (cv + 1023) / 1024;
+    if (pt <= 1)
+        softmax_kernel<T, 1, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+    else if (pt <= 2)
+        softmax_kernel<T, 2, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+    else if (pt <= 4)
+        softmax_kernel<T, 4, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+    else if (pt <= 7)
+        softmax_kernel<T, 7, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+    else if (pt <= 13)
+        softmax_kernel<T, 13, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+    else if (pt <= 16)
+        softmax_kernel<T, 16, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+    else
+        softmax_kernel<T, 32, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+}
+
+int launch_softmax(void* probs, const void* logits, int N, int V, int Vp, int dtype,
+                   hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_softmax_t<bf16>((bf16*)probs, (const bf16*)logits, N, V, Vp, s);
+    else
+        launch_softmax_t<float>((float*)probs, (const float*)logits, N, V, Vp, s);
+    return launch_status();
+}
+
+}  // namespace gpt2
+
+// ------------------------------------------------------------------ C ABI
+using namespace gpt2;
+
+extern "C" int layernorm_forward(void* out, float* mean, float* rstd, const void* inp,
+                                 const void* gamma, const void* beta, int N, int C, float eps,
+                                 int dtype, void* stream) {
+    if (!valid_dtype(dtype) || N < 0 || C < 0 || !(eps >= 0.f)) return GPT2_ERR_INVALID_ARGUMENT;
+    if (N == 0) return GPT2_OK;
+    if (!out || !inp || !gamma || !beta || C == 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (C % 8 || C > 4096 || !aligned16(out) || !aligned16(inp) || !aligned16(gamma) ||
+        !aligned16(beta))
+        return GPT2_ERR_UNSUPPORTED;
+    if (out == inp) return GPT2_ERR_INVALID_ARGUMENT;
+    return launch_layernorm(out, mean, rstd, inp, gamma, beta, N, C, eps, dtype,
+                            (hipStream_t)stream);
+}
+
+extern "C" int softmax_forward(void* probs, const void* logits, int N, int V, int Vp, int dtype,
+                               void* stream) {
+    if (!valid_dtype(dtype) || N < 0 || V < 0 || Vp < V) return GPT2_ERR_INVALID_ARGUMENT;
+    if (N == 0) return GPT2_OK;
+    if (!probs || !logits || V == 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (Vp % 8 || Vp > 131072 || !aligned16(probs) || !aligned16(logits))
+        return GPT2_ERR_UNSUPPORTED;
+    if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
+    return launch_softmax(probs, logits, N, V, Vp, dtype, (hipStream_t)stream);
+}
