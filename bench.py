@@ -42,22 +42,12 @@ def parse():
     ap.add_argument("--workload", default="small",
                     help="small (fp32 B4 T1024, default), small_bf16_b4, small_bf16_b8, medium, decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--profile-kernel", action="store_true",
+                    help="counter-collection mode: launch only the logits GEMM (3x) and a "
+                         "256 MiB device copy (calibration), print their names and sizes")
     return ap.parse_args()
-
-
-def gemm_tile(M, N):
-    """Tile the library picks for an M x N output (mirrors the launcher)."""
-    def tiles(bm, bn):
-        return -(-M // bm) * -(-N // bn)
-    if M <= 32:
-        return "32x64"
-    if tiles(128, 128) >= 512:
-        return "128x128"
-    if tiles(64, 128) >= 256:
-        return "64x128"
-    return "64x64"
 
 
 class Bench:
@@ -109,16 +99,17 @@ class Bench:
         s = torch.cuda.current_stream()
         recs = []
 
-        def timed(kind, name, fn, flops=0.0, nbytes=0.0):
+        def timed(kind, name, fn, flops=0.0, nbytes=0.0, site=None):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(s)
             fn()
             b.record(s)
-            recs.append([kind, name, flops, nbytes, a, b])
+            recs.append([kind, name, flops, nbytes, a, b, site or name])
 
+        # GEMM launches are named by the kernel configuration the library picks
         gemm = lambda out, inp, wt, bias, M, K, Nc, Nalg, tag: timed(  # noqa: E731
-            "gemm", "gemm_%s_%s" % ("bf16" if es == 2 else "f32", gemm_tile(M, Nc)),
-            lambda: G.matmul_forward(out, inp, wt, bias), 2.0 * M * Nalg * K, 0.0)
+            "gemm", G.matmul_kernel_config(M, K, Nc, w.dtype),
+            lambda: G.matmul_forward(out, inp, wt, bias), 2.0 * M * Nalg * K, 0.0, "gemm_" + tag)
         all_runs = []
         for _ in range(reps):
             recs.clear()
@@ -144,17 +135,20 @@ class Bench:
             timed("hbm", "softmax", lambda: G.softmax_forward(probs, logits, w.V), 0.0,
                   N * w.V * es + N * w.Vp * es)
             torch.cuda.synchronize()
-            all_runs.append([r[:4] + [r[4].elapsed_time(r[5])] for r in recs])
+            all_runs.append([r[:4] + [r[4].elapsed_time(r[5]), r[6]] for r in recs])
         out = []
         for i in range(len(all_runs[0])):
             ms = float(np.median([run[i][4] for run in all_runs]))
-            out.append(all_runs[0][i][:4] + [ms])
+            out.append(all_runs[0][i][:4] + [ms, all_runs[0][i][5]])
         return out
 
 
-def summarize_kernels(recs, dtype_bf16):
+def summarize_kernels(recs, dtype_bf16, key=1):
+    """Group launch records by kernel name (key=1) or by call site (key=5)."""
     groups = {}
-    for kind, name, fl, nb, ms in recs:
+    for r in recs:
+        kind, fl, nb, ms = r[0], r[2], r[3], r[4]
+        name = r[key]
         g = groups.setdefault(name, {"kind": kind, "calls": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
         g["calls"] += 1
         g["ms"] += ms
@@ -214,6 +208,27 @@ def source_sha1():
     return h.hexdigest()
 
 
+def profile_kernel(b):
+    """Launch the vocabulary GEMM three times and one plain device-to-device
+    copy of 256 MiB, for hardware-counter runs (rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE): the copy reads and writes a known number of bytes, which
+    calibrates the counters."""
+    torch, G, I, w = b.torch, b.G, b.I, b.w
+    N = w.B * w.T
+    o, shp = I.param_offsets(w.L, w.C, w.maxT, w.Vp)["wte"]
+    wte = b.params[o:o + int(np.prod(shp))].view(*shp)
+    ln = torch.randn(N, w.C, device="cuda").to(b.tdtype)
+    logits = b.logits.view(N, w.Vp)
+    for _ in range(3):
+        G.matmul_forward(logits, ln, wte, None)
+    src = torch.ones(64 << 20, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"gemm_kernel": G.matmul_kernel_config(N, w.C, w.Vp, w.dtype),
+                      "gemm_shape": [N, w.C, w.Vp], "copy_bytes_each_way": 256 << 20}))
+
+
 def cpu_baseline(b, ntok):
     """The oracle, single-threaded, on the first ntok positions of sequence 0
     (by the causal invariant, exactly those positions of the full workload)."""
@@ -242,6 +257,9 @@ def main():
         raise SystemExit("decode workload: use bench_decode (not yet wired)")
     torch.cuda.set_device(0)
     b = Bench(w)
+    if args.profile_kernel:
+        profile_kernel(b)
+        return
     for _ in range(args.warmup):
         b.step()
     torch.cuda.synchronize()
@@ -272,8 +290,10 @@ def main():
     if not args.no_kernel_timing:
         recs = b.kernel_timing()
         table, roof = summarize_kernels(recs, w.dtype == I.BF16)
+        sites, _ = summarize_kernels(recs, w.dtype == I.BF16, key=5)
         res["roofline"] = roof
         res["kernels"] = table
+        res["sites"] = sites
         res["kernel_sum_ms"] = round(sum(r[4] for r in recs), 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_sample_tokens)

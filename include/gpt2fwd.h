@@ -73,6 +73,12 @@ int layernorm_forward(void* out, float* mean, float* rstd, const void* inp,
 int matmul_forward(void* out, const void* inp, const void* weight, const void* bias,
                    int N, int C, int OC, int dtype, void* stream);
 
+/* Name of the GEMM kernel configuration matmul_forward launches for this
+ * problem (host call; a static string such as "gemm_f32_128x128_bk32", the
+ * tile and k-tile of the launch), so profiles can be attributed to shapes.
+ * Returns "invalid" for negative sizes or an unknown dtype. */
+const char* matmul_kernel_config(int N, int C, int OC, int dtype);
+
 /* Causal multi-head self-attention with its softmax fused (ECE408 kernel
  * table: Attention including Softmax; the tiled online-softmax algorithm of
  * the optdl2025 project "Understand FlashAttention (I)", computing only the

@@ -32,7 +32,7 @@ EXPORTS = (
     "gelu_forward", "residual_forward", "softmax_forward", "gpt2_param_count",
     "gpt2_workspace_bytes", "gpt2_forward", "attention_decode_workspace_bytes",
     "attention_decode_forward", "gpt2_decode_workspace_bytes", "gpt2_decode_step",
-    "gpt2_status_string", "gpt2_last_hip_error",
+    "gpt2_status_string", "gpt2_last_hip_error", "matmul_kernel_config",
 )
 
 
@@ -84,6 +84,7 @@ def load_library(path: str = LIB_PATH):
             "gpt2_decode_step": (I, [P, P, P, I, P, P, P, CP, I, P, I64, P]),
             "gpt2_status_string": (ctypes.c_char_p, [I]),
             "gpt2_last_hip_error": (I, []),
+            "matmul_kernel_config": (ctypes.c_char_p, [I, I, I, I]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -166,6 +167,11 @@ def matmul_forward(out, inp, weight, bias=None, stream=None):
         _dev(out, "out"), _dev(inp, "inp"), _dev(weight, "weight"), _dev(bias, "bias"),
         N, C, OC, _dtype_code(inp), _stream(stream)))
     return out
+
+
+def matmul_kernel_config(N, C, OC, dtype) -> str:
+    """Name of the GEMM kernel configuration matmul_forward uses for this shape."""
+    return load_library().matmul_kernel_config(N, C, OC, dtype).decode()
 
 
 def attention_forward(out, qkv, NH, stream=None):
