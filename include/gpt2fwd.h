@@ -74,9 +74,11 @@ int matmul_forward(void* out, const void* inp, const void* weight, const void* b
                    int N, int C, int OC, int dtype, void* stream);
 
 /* Name of the GEMM kernel configuration matmul_forward launches for this
- * problem (host call; a static string such as "gemm_f32_128x128_bk32", the
- * tile and k-tile of the launch), so profiles can be attributed to shapes.
- * Returns "invalid" for negative sizes or an unknown dtype. */
+ * problem (host call), e.g. "gemm_f32_64x128_p3": dtype, output tile, and
+ * "_p3" for the three-stage load-to-LDS pipeline or "_r" for the
+ * register-staged kernel; so profiles can be attributed to shapes. The string
+ * lives in thread-local storage until this thread's next call. Returns
+ * "invalid" for negative sizes or an unknown dtype. */
 const char* matmul_kernel_config(int N, int C, int OC, int dtype);
 
 /* Causal multi-head self-attention with its softmax fused (ECE408 kernel

@@ -162,6 +162,27 @@ def test_matmul_random(dt, N, C, OC):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,OC", [(8192, 768, 776), (8200, 768, 3000), (8200, 3072, 768), (600, 3072, 776),
+                                    (2100, 768, 1000)])
+def test_matmul_tile_paths_sampled(dt, N, C, OC):
+    """Shapes that select every pipelined tile (64x64 .. 256x128), with ragged
+    row and column tails; the oracle recomputes sampled rows, including the
+    last (partial) row tile."""
+    announce("matmul-tiles", dt, N, C, OC, G.matmul_kernel_config(N, C, OC, DT[dt]))
+    d = DT[dt]
+    a = I.random_tensor(24, (N, C), 1.0, d)
+    w = I.random_tensor(25, (OC, C), 0.02, d)
+    b = I.random_tensor(26, OC, 0.02, d)
+    out = empty((N, OC), d, fill=float("nan"))
+    G.matmul_forward(out, dev(a, d), dev(w, d), dev(b, d))
+    got_all = host(out)
+    assert np.all(np.isfinite(got_all))
+    rows = np.unique(np.array([0, 31, 32, 255, 256, N // 2, N - 257, N - 9, N - 1]).clip(0, N - 1))
+    ref = oracle.matmul(a[rows], w, b)
+    assert rel_err(got_all[rows], ref) <= (1e-2 if d == I.BF16 else 1e-5)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_matmul_full_logits_shape_sampled(dt):
     """GPT-2 small logits GEMM (4096 x 768 -> 50304) in the launch the forward
     uses; the oracle recomputes a sample of rows."""

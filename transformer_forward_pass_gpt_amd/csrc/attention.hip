@@ -48,6 +48,16 @@ template <> struct MfmaS<bf16> {
 static constexpr int kBQ = 128;  // queries per workgroup (4 wavefronts x 32)
 static constexpr int kBKV = 64;  // keys per LDS block
 
+// V is kept TRANSPOSED in LDS (Vt[d][key]) so that the k-slots of the P.V
+// product (which run over keys) are contiguous in LDS for every operand.
+// bf16: within each group of 16 keys, bits 2 and 3 of the key index are
+// swapped, which makes the 8 keys one half-wave feeds into one
+// v_mfma_f32_32x32x16_bf16 k-step (keys 16ks+4h+{0..3} and 16ks+8+4h+{0..3})
+// land in 8 consecutive slots: one 16-byte LDS read per operand.
+__device__ __forceinline__ int vt_slot_bf16(int key) {
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
 template <typename T, int HS>
 __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
                                                         int Tn, int C, int NH, float sl2) {
@@ -57,31 +67,33 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
     constexpr int HSP = DT * 32;
     constexpr int KCH = HS / (2 * VE);  // 16-byte fragments along the head dim
     static_assert(HS % (2 * VE) == 0, "head size must hold whole fragments");
-    constexpr int LDK = HS + VE;                // K block [kBKV][HS], 16-byte row pad
-    constexpr int LDV = F32 ? HSP + 8 : kBKV + 4;  // V: fp32 [key][d], bf16 transposed [d][key]
-    constexpr int VROWS = F32 ? kBKV : HSP;
-    __shared__ __attribute__((aligned(16))) T Ks[kBKV * LDK];
-    __shared__ __attribute__((aligned(16))) T Vs[VROWS * LDV];
+    constexpr int LDK = HS + VE;    // K block [kBKV][HS], 16-byte row pad
+    constexpr int LDV = kBKV + VE;  // V^T block [HSP][kBKV], 16-byte row pad
+    constexpr int RV = HS / VE;                          // 16-byte vectors per key row
+    constexpr int NKV = (kBKV * RV + 255) / 256;         // K vectors per thread
+    constexpr int NVS = (kBKV / 4 * RV + 255) / 256;     // V 4-key sub-blocks per thread
+    __shared__ __attribute__((aligned(16))) T Ks[2][kBKV * LDK];
+    __shared__ __attribute__((aligned(16))) T Vt[2][HSP * LDV];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int h = lane >> 5, r32 = lane & 31;
-    const int qb = gridDim.x - 1 - blockIdx.x;  // longest query blocks start first
-    const int bh = blockIdx.y, b = bh / NH, hd = bh % NH;
+    // Workgroups are dispatched in linear order (x fastest): all (batch, head)
+    // pairs of the last, longest query block first, then the next, so the
+    // causal triangle's long rows never end up in the tail.
+    const int qb = gridDim.y - 1 - blockIdx.y;
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
     const int q0 = qb * kBQ, qw = q0 + wid * 32;
     const int64_t rs = 3 * (int64_t)C;
     const T* base = qkv + (int64_t)b * Tn * rs;
     const int qoff = hd * HS, koff = C + hd * HS, voff = 2 * C + hd * HS;
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    // Padded head columns of V (HS < 32) are never loaded: zero them once.
+    // Padded head rows of V^T (HS < 32) are never loaded: zero them once.
     if (HS < HSP) {
-        for (int i = tid; i < VROWS * LDV; i += 256) {
-            int r = i / LDV, c = i % LDV;
-            bool pad = F32 ? (c >= HS) : (r >= HS);
-            if (pad) {
-                if constexpr (F32) Vs[i] = 0.f;
-                else Vs[i].bits = 0;
-            }
+        for (int i = tid; i < 2 * (HSP - HS) * LDV; i += 256) {
+            const int buf = i / ((HSP - HS) * LDV), j = i % ((HSP - HS) * LDV);
+            if constexpr (F32) Vt[buf][HS * LDV + j] = 0.f;
+            else Vt[buf][HS * LDV + j].bits = 0;
         }
     }
 
@@ -96,6 +108,58 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
                             : zero;
     }
 
+    // ---- K/V block staging: global -> registers -> LDS (double-buffered)
+    u32x4 rk[NKV], rv[NVS][4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < NKV; i++) {
+            const int li = tid + i * 256, r = li / RV, cv = li % RV, key = k0 + r;
+            rk[i] = (li < kBKV * RV && key < Tn)
+                        ? *reinterpret_cast<const u32x4*>(base + key * rs + koff + cv * VE) : zero;
+        }
+#pragma unroll
+        for (int i = 0; i < NVS; i++) {
+            const int li = tid + i * 256, kq = li / RV, cv = li % RV;  // keys 4kq..4kq+3
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int key = k0 + 4 * kq + e;
+                rv[i][e] = (li < kBKV / 4 * RV && key < Tn)
+                               ? *reinterpret_cast<const u32x4*>(base + key * rs + voff + cv * VE) : zero;
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NKV; i++) {
+            const int li = tid + i * 256, r = li / RV, cv = li % RV;
+            if (li < kBKV * RV) *reinterpret_cast<u32x4*>(&Ks[buf][r * LDK + cv * VE]) = rk[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NVS; i++) {
+            const int li = tid + i * 256, kq = li / RV, cv = li % RV;
+            if (li < kBKV / 4 * RV) {
+                // 4 keys x VE head dims -> VE rows of V^T, 4 consecutive slots each
+                if constexpr (F32) {
+#pragma unroll
+                    for (int d = 0; d < 4; d++) {
+                        const u32x4 col = {rv[i][0][d], rv[i][1][d], rv[i][2][d], rv[i][3][d]};
+                        *reinterpret_cast<u32x4*>(&Vt[buf][(cv * 4 + d) * LDV + 4 * kq]) = col;
+                    }
+                } else {
+                    const int slot = vt_slot_bf16(4 * kq);
+#pragma unroll
+                    for (int d = 0; d < 8; d++) {
+                        const int w = d >> 1, sh = 16 * (d & 1);
+                        const uint32_t k0v = (rv[i][0][w] >> sh) & 0xffffu, k1v = (rv[i][1][w] >> sh) & 0xffffu;
+                        const uint32_t k2v = (rv[i][2][w] >> sh) & 0xffffu, k3v = (rv[i][3][w] >> sh) & 0xffffu;
+                        const u32x2 col = {k0v | (k1v << 16), k2v | (k3v << 16)};
+                        *reinterpret_cast<u32x2*>(&Vt[buf][(cv * 8 + d) * LDV + slot]) = col;
+                    }
+                }
+            }
+        }
+    };
+
     f32x16 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) o[dt] = f32x16{};
@@ -103,26 +167,13 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
 
     const int kend = min(Tn, q0 + kBQ);
     const int nkb = (kend + kBKV - 1) / kBKV;
-    constexpr int RV = HS / VE;  // 16-byte vectors per key row
+    gload(0);
+    sstore(0);
+    __syncthreads();
     for (int kb = 0; kb < nkb; kb++) {
+        const int cur = kb & 1;
         const int k0 = kb * kBKV;
-        for (int li = tid; li < kBKV * RV; li += 256) {
-            const int r = li / RV, cv = li % RV, key = k0 + r;
-            u32x4 kx = zero, vx = zero;
-            if (key < Tn) {
-                kx = *reinterpret_cast<const u32x4*>(base + key * rs + koff + cv * VE);
-                vx = *reinterpret_cast<const u32x4*>(base + key * rs + voff + cv * VE);
-            }
-            *reinterpret_cast<u32x4*>(&Ks[r * LDK + cv * VE]) = kx;
-            if constexpr (F32) {
-                *reinterpret_cast<u32x4*>(&Vs[r * LDV + cv * VE]) = vx;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; e++)
-                    Vs[(cv * 8 + e) * LDV + r].bits = (uint16_t)(vx[e >> 1] >> (16 * (e & 1)));
-            }
-        }
-        __syncthreads();
+        if (kb + 1 < nkb) gload(k0 + kBKV);
         if (k0 <= qw + 31) {  // some of this wave's queries see this block
             // S^T tiles: keys k0 + kt*32 + (8*(v/4) + 4*h + v%4), query qw + r32
             f32x16 s[2];
@@ -132,34 +183,34 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
 #pragma unroll
                 for (int kc = 0; kc < KCH; kc++) {
                     const u32x4 ka = *reinterpret_cast<const u32x4*>(
-                        &Ks[(kt * 32 + r32) * LDK + kc * 2 * VE + h * VE]);
+                        &Ks[cur][(kt * 32 + r32) * LDK + kc * 2 * VE + h * VE]);
                     MfmaS<T>::run(s[kt], ka, qf[kc]);
                 }
             }
             const int q = qw + r32;
-            const bool need_mask = (k0 + kBKV - 1 > qw);
             float mx = -INFINITY;
+            if (k0 + kBKV - 1 > qw) {  // diagonal block: mask keys after the query
+#pragma unroll
+                for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        const int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        if (key > q) s[kt][v] = -INFINITY;
+                    }
+            }
 #pragma unroll
             for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    float x = s[kt][v] * sl2;
-                    if (need_mask) {
-                        const int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                        if (key > q) x = -INFINITY;
-                    }
-                    s[kt][v] = x;
-                    mx = fmaxf(mx, x);
-                }
+                for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kt][v]);
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);  // finite: key 0 is in the first block
-            const float alpha = exp2f(m_run - m_new);
+            const float m_new = fmaxf(m_run, mx * sl2);  // finite: key 0 is in the first block
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             float ls = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 2; kt++)
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
-                    const float p = exp2f(s[kt][v] - m_new);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][v], sl2, -m_new));
                     s[kt][v] = p;
                     ls += p;
                 }
@@ -176,13 +227,17 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
 #pragma unroll
                 for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-                    for (int v = 0; v < 16; v++) {
-                        const int kl = kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    for (int g = 0; g < 4; g++)
 #pragma unroll
-                        for (int dt = 0; dt < DT; dt++)
-                            o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[kl * LDV + dt * 32 + r32],
-                                                                        s[kt][v], o[dt], 0, 0, 0);
-                    }
+                        for (int dt = 0; dt < DT; dt++) {
+                            // keys kt*32 + 8g + 4h + e, e = 0..3
+                            const u32x4 va = *reinterpret_cast<const u32x4*>(
+                                &Vt[cur][(dt * 32 + r32) * LDV + kt * 32 + 8 * g + 4 * h]);
+#pragma unroll
+                            for (int e = 0; e < 4; e++)
+                                o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                    __uint_as_float(va[e]), s[kt][4 * g + e], o[dt], 0, 0, 0);
+                        }
             } else {
 #pragma unroll
                 for (int kt = 0; kt < 2; kt++)
@@ -193,18 +248,16 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
 #pragma unroll
                         for (int e = 0; e < 4; e++)
                             pb[e] = pack_bf16x2(s[kt][8 * ks + 2 * e], s[kt][8 * ks + 2 * e + 1]);
-                        const int kl = kt * 32 + 16 * ks + 4 * h;
 #pragma unroll
                         for (int dt = 0; dt < DT; dt++) {
-                            const T* vr = &Vs[(dt * 32 + r32) * LDV + kl];
-                            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-                            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-                            const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                            const u32x4 va = *reinterpret_cast<const u32x4*>(
+                                &Vt[cur][(dt * 32 + r32) * LDV + kt * 32 + 16 * ks + 8 * h]);
                             MfmaS<T>::run(o[dt], va, pb);
                         }
                     }
             }
         }
+        if (kb + 1 < nkb) sstore(cur ^ 1);
         __syncthreads();
     }
 
@@ -236,7 +289,7 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
 template <typename T, int HS>
 static void launch_attn_hs(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)HS);  // log2(e)/sqrt(hs)
-    dim3 grid((Tn + kBQ - 1) / kBQ, B * NH);
+    dim3 grid(B * NH, (Tn + kBQ - 1) / kBQ);
     attention_kernel<T, HS><<<grid, 256, 0, s>>>(out, qkv, Tn, C, NH, sl2);
 }
 

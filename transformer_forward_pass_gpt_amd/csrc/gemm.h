@@ -177,6 +177,179 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* __restrict__ out, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined variant: operand tiles are copied HBM/L2 -> LDS directly by the
+// gfx950 load-to-LDS instruction (global_load_lds_dwordx4: each lane's 16
+// bytes land at M0 + 16*lane), through S = 3 LDS stages, so two k-tiles of
+// loads are always in flight behind the MFMAs and no VGPRs are spent on
+// staging. Rows are stored unpadded (BK elements = 8 x 16-byte chunks); the
+// chunk holding logical k-chunk c of row r sits at slot c ^ (r % 8), which
+// keeps the 16-byte fragment reads of 8 consecutive rows on distinct banks.
+// The copies are issued from inline assembly so the compiler does not track
+// them: its wait-count pass would otherwise drain every outstanding load
+// before some LDS reads. All ordering is explicit instead: vmcnt waits for
+// this wave's own copies, then a bare s_barrier (a __syncthreads fence would
+// also wait for the copies still in flight for later tiles). Every copy is
+// complete before the loop exits. Requires K % BK == 0; rows past M or N read
+// a clamped (valid) row whose results are never stored.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Copy 16 bytes per lane from global memory to LDS: lane i's bytes land at
+// lds + 16*i (lds is wave-uniform; it goes to M0).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void_ptr lds) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0v), "v"(src)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt simm16 on gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+template <typename T, int WM, int WN, int TM, int TN, int BK>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_lds3_kernel(T* __restrict__ out, const T* __restrict__ A,
+                                                                const T* __restrict__ W,
+                                                                const T* __restrict__ bias, int M, int N,
+                                                                int K, int group_m, int remap) {
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int VE = Vec<T>::N;
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    constexpr int CH = BK / VE;  // 16-byte chunks per tile row
+    static_assert(CH == 8, "swizzle assumes 8 chunks (128 bytes) per tile row");
+    constexpr int LA = BM * CH / 64 / NW, LB = BN * CH / 64 / NW;  // DMA instructions per wave
+    static_assert(LA * 64 * NW == BM * CH && LB * 64 * NW == BN * CH, "tile/wave mismatch");
+    constexpr int LPW = LA + LB;
+    __shared__ __attribute__((aligned(16))) T sA0[BM * BK];
+    __shared__ __attribute__((aligned(16))) T sB0[BN * BK];
+    __shared__ __attribute__((aligned(16))) T sA1[BM * BK];
+    __shared__ __attribute__((aligned(16))) T sB1[BN * BK];
+    __shared__ __attribute__((aligned(16))) T sA2[BM * BK];
+    __shared__ __attribute__((aligned(16))) T sB2[BN * BK];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid / WN, wn = wid % WN;
+    const int h = lane >> 5, r32 = lane & 31;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int nwg = tiles_m * tiles_n;
+    int pid = blockIdx.x;
+    if (remap) pid = xcd_contiguous(pid, nwg);
+    const int per_group = group_m * tiles_n;
+    const int g = pid / per_group, first_m = g * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
+    const int in_g = pid - g * per_group;
+    const int m0 = (first_m + in_g % gsz) * BM, n0 = (in_g / gsz) * BN;
+
+    // Per-lane source offsets (element index at k = 0) for this wave's DMA
+    // instructions; chunk q of the tile = row q/8, slot q%8.
+    int64_t offA[LA], offB[LB];
+#pragma unroll
+    for (int j = 0; j < LA; j++) {
+        const int q = (wid * LA + j) * 64 + lane, row = q >> 3, lc = (q & 7) ^ (row & 7);
+        offA[j] = (int64_t)min(m0 + row, M - 1) * K + lc * VE;
+    }
+#pragma unroll
+    for (int j = 0; j < LB; j++) {
+        const int q = (wid * LB + j) * 64 + lane, row = q >> 3, lc = (q & 7) ^ (row & 7);
+        offB[j] = (int64_t)min(n0 + row, N - 1) * K + lc * VE;
+    }
+    auto issue = [&](T* sA, T* sB, int k0) {
+#pragma unroll
+        for (int j = 0; j < LA; j++)
+            copy16_to_lds(A + offA[j] + k0, (lds_void_ptr)(sA + (wid * LA + j) * 64 * VE));
+#pragma unroll
+        for (int j = 0; j < LB; j++)
+            copy16_to_lds(W + offB[j] + k0, (lds_void_ptr)(sB + (wid * LB + j) * 64 * VE));
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) acc[i][j] = f32x16{};
+
+    auto compute = [&](const T* sA, const T* sB) {
+#pragma unroll
+        for (int kc = 0; kc < CH / 2; kc++) {
+            u32x4 fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const int row = wm * TM * 32 + i * 32 + r32;
+                fa[i] = *reinterpret_cast<const u32x4*>(&sA[row * BK + (((2 * kc + h) ^ (row & 7)) * VE)]);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const int row = wn * TN * 32 + j * 32 + r32;
+                fb[j] = *reinterpret_cast<const u32x4*>(&sB[row * BK + (((2 * kc + h) ^ (row & 7)) * VE)]);
+            }
+#pragma unroll
+            for (int e = 0; e < Mfma32<T>::STEPS; e++)
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int j = 0; j < TN; j++) Mfma32<T>::step(acc[i][j], fa[i], fb[j], e);
+        }
+    };
+
+    const int nk = K / BK;
+    issue(sA0, sB0, 0);
+    if (nk > 1) issue(sA1, sB1, BK);
+    // One k-tile per step: wait for this tile's loads (the next tile's may
+    // stay in flight), barrier, launch the tile two ahead into the stage the
+    // previous step just finished reading, compute.
+#define GEMM_LDS3_STEP(SA, SB, SA2, SB2, T_)            \
+    {                                                      \
+        const int t = (T_);                                \
+        if (t + 1 < nk) wait_vmcnt<LPW>();                 \
+        else wait_vmcnt<0>();                              \
+        __builtin_amdgcn_s_barrier();                      \
+        if (t + 2 < nk) issue(SA2, SB2, (t + 2) * BK);     \
+        compute(SA, SB);                                   \
+    }
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {
+        GEMM_LDS3_STEP(sA0, sB0, sA2, sB2, kt)
+        GEMM_LDS3_STEP(sA1, sB1, sA0, sB0, kt + 1)
+        GEMM_LDS3_STEP(sA2, sB2, sA1, sB1, kt + 2)
+    }
+    if (kt < nk) GEMM_LDS3_STEP(sA0, sB0, sA2, sB2, kt)
+    if (kt + 1 < nk) GEMM_LDS3_STEP(sA1, sB1, sA0, sB0, kt + 1)
+#undef GEMM_LDS3_STEP
+
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+        const int col = n0 + wn * TN * 32 + j * 32 + r32;
+        if (col >= N) continue;
+        const float bv = bias ? load_scalar(bias + col) : 0.f;
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (row < M) store_scalar(out + (int64_t)row * N + col, acc[i][j][v] + bv);
+            }
+        }
+    }
+}
+
+template <typename T, int WM, int WN, int TM, int TN>
+static void launch_gemm_lds3(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
+                             int group_m, int remap, hipStream_t s) {
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BK = Vec<T>::N * 8;
+    const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    gemm_lds3_kernel<T, WM, WN, TM, TN, BK><<<nwg, WM * WN * 64, 0, s>>>(out, A, W, bias, M, N, K,
+                                                                         group_m, remap);
+}
+
 template <typename T, int WM, int WN, int TM, int TN, int BK, bool ILV = true>
 static void launch_gemm_cfg(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
                             int group_m, int remap, hipStream_t s) {

@@ -1,31 +1,41 @@
 // Linear layer entry: out[n,o] = sum_c inp[n,c] * W[o,c] + bias[o], on the
 // MFMA GEMM of gemm.h with a tile shape chosen per problem size.
+#include <stdio.h>
+
 #include "gemm.h"
 
 namespace gpt2 {
 
-// Tile shapes, chosen per problem from measurements on MI355X (GPT-2 small and
-// medium layer shapes): wide outputs (the vocabulary projection) take
-// 128x128 tiles; deep reductions take 128x96 with 256-byte k tiles; the
-// rest picks the largest tile that still gives every CU several workgroups.
-enum GemmCfg { G32x64 = 0, G64x64, G64x128, G128x96, G128x96_K2, G128x128, G_NCFG };
-static const char* kCfgName[2][G_NCFG] = {
-    {"gemm_f32_32x64_bk32", "gemm_f32_64x64_bk32", "gemm_f32_64x128_bk32", "gemm_f32_128x96_bk32",
-     "gemm_f32_128x96_bk64", "gemm_f32_128x128_bk32"},
-    {"gemm_bf16_32x64_bk64", "gemm_bf16_64x64_bk64", "gemm_bf16_64x128_bk64",
-     "gemm_bf16_128x96_bk64", "gemm_bf16_128x96_bk128", "gemm_bf16_128x128_bk64"}};
+// Tile shapes, chosen per problem from measurements on MI355X over the GPT-2
+// small and medium layer shapes. When K is a whole number of 128-byte k-tiles
+// the pipelined kernel (three LDS stages filled by load-to-LDS copies) runs;
+// otherwise, and for the 32-row decode problems, the register-staged kernel.
+enum GemmCfg {
+    R32x64 = 0, R64x64, R64x128, R128x96,     // register-staged (gemm_kernel)
+    P64x64, P64x128, P128x96, P128x128, P128x192, P256x128,  // pipelined (gemm_lds3_kernel)
+    G_NCFG
+};
+static const char* kCfgName[G_NCFG] = {"32x64_r", "64x64_r", "64x128_r", "128x96_r", "64x64_p3",
+                                       "64x128_p3", "128x96_p3", "128x128_p3", "128x192_p3",
+                                       "256x128_p3"};
 
 static GemmCfg choose_cfg(int M, int N, int K, int dtype) {
     auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (M <= 32) return G32x64;
-    if (N >= 16384) return G128x128;
-    if (dtype == GPT2_F32) {
-        if (K >= 2048 && tiles(128, 96) >= 256) return G128x96_K2;
-        if (tiles(128, 96) >= 1024) return G128x96;
-        return G64x64;
+    const int bk = dtype == GPT2_BF16 ? 64 : 32;
+    if (M <= 32) return R32x64;
+    if (K % bk != 0) {  // no whole k-tiles: register-staged kernel with a masked tail
+        if (tiles(128, 96) >= 1024) return R128x96;
+        return tiles(64, 128) >= 256 ? R64x128 : R64x64;
     }
-    if (tiles(128, 96) >= 512) return G128x96;
-    return G64x128;
+    if (dtype == GPT2_F32) {
+        if (N >= 16384) return P64x128;                 // vocabulary projection
+        if (K >= 2048 || N <= 1024) return P128x96;     // fcproj, attproj
+        return N >= 3072 ? P64x128 : P64x64;            // fc, qkv
+    }
+    if (N >= 16384) return P256x128;
+    if (K >= 2048) return tiles(128, 192) >= 256 ? P128x192 : P128x128;
+    if (N <= 1024) return tiles(128, 192) >= 256 ? P128x192 : P64x128;
+    return tiles(256, 128) >= 384 ? P256x128 : P64x128;
 }
 
 template <typename T>
@@ -33,19 +43,25 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, int M, 
                           int dtype, hipStream_t s) {
     constexpr int BK = Vec<T>::N * 8;  // 128 bytes of k per row per LDS tile
     switch (choose_cfg(M, N, K, dtype)) {
-        case G32x64: launch_gemm_cfg<T, 1, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 1, 0, s); break;
-        case G64x64: launch_gemm_cfg<T, 2, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 4, 1, s); break;
-        case G64x128: launch_gemm_cfg<T, 2, 2, 1, 2, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case G128x96: launch_gemm_cfg<T, 4, 1, 1, 3, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case G128x96_K2:
-            launch_gemm_cfg<T, 4, 1, 1, 3, 2 * BK>(out, A, W, bias, M, N, K, 4, 1, s);
-            break;
-        default: launch_gemm_cfg<T, 1, 4, 4, 1, BK>(out, A, W, bias, M, N, K, 4, 1, s); break;
+        case R32x64: launch_gemm_cfg<T, 1, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 1, 0, s); break;
+        case R64x64: launch_gemm_cfg<T, 2, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 4, 1, s); break;
+        case R64x128: launch_gemm_cfg<T, 2, 2, 1, 2, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case R128x96: launch_gemm_cfg<T, 4, 1, 1, 3, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P64x64: launch_gemm_lds3<T, 2, 2, 1, 1>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P64x128: launch_gemm_lds3<T, 1, 4, 2, 1>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P128x96: launch_gemm_lds3<T, 4, 1, 1, 3>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P128x128: launch_gemm_lds3<T, 2, 2, 2, 2>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P128x192: launch_gemm_lds3<T, 2, 2, 2, 3>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        default: launch_gemm_lds3<T, 4, 2, 2, 2>(out, A, W, bias, M, N, K, 1, 0, s); break;
     }
 }
 
+static thread_local char g_cfg_name[64];
+
 const char* matmul_config_name(int N, int C, int OC, int dtype) {
-    return kCfgName[dtype == GPT2_BF16 ? 1 : 0][choose_cfg(N, OC, C, dtype)];
+    snprintf(g_cfg_name, sizeof g_cfg_name, "gemm_%s_%s", dtype == GPT2_BF16 ? "bf16" : "f32",
+             kCfgName[choose_cfg(N, OC, C, dtype)]);
+    return g_cfg_name;
 }
 
 int launch_matmul(void* out, const void* inp, const void* weight, const void* bias, int N, int C,
