@@ -18,6 +18,8 @@
 // range is walked in groups of `group_m` row tiles, so the A rows and W
 // columns a CU needs are shared with its XCD neighbours through that XCD's L2.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace gpt2 {
@@ -183,8 +185,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* __restrict__ out, 
 // bytes land at M0 + 16*lane), through S = 3 LDS stages, so two k-tiles of
 // loads are always in flight behind the MFMAs and no VGPRs are spent on
 // staging. Rows are stored unpadded (BK elements = 8 x 16-byte chunks); the
-// chunk holding logical k-chunk c of row r sits at slot c ^ (r % 8), which
-// keeps the 16-byte fragment reads of 8 consecutive rows on distinct banks.
+// chunk holding logical k-chunk c of row r sits at slot c ^ ((r / 2) % 8).
+// LDS serves a 16-byte read for 16 lanes at a time from 64 four-byte banks
+// (256 bytes): with 128-byte rows, rows r and r+1 fall in the two halves, and
+// the swizzle gives the 8 rows of each parity 8 different 16-byte slots, so
+// the 16 rows a fragment read touches hit every bank exactly once.
 // The copies are issued from inline assembly so the compiler does not track
 // them: its wait-count pass would otherwise drain every outstanding load
 // before some LDS reads. All ordering is explicit instead: vmcnt waits for
@@ -207,32 +212,46 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, lds_void_ptr lds)
 }
 #pragma clang diagnostic pop
 
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding AND all of its LDS operations are done (lgkmcnt 0): before the
+// barrier that lets other waves overwrite a stage, this wave's reads of that
+// stage must have completed, not merely been issued.
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+__device__ __forceinline__ void wait_vmcnt_lds() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     // s_waitcnt simm16 on gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
 }
 
-template <typename T, int WM, int WN, int TM, int TN, int BK>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_lds3_kernel(T* __restrict__ out, const T* __restrict__ A,
+// SCHED: 0 = compiler order; 1, 2 = the backend's iglp strategies 0 and 1;
+// 3 = scheduling groups: after the first k-chunk's fragment reads, every MFMA
+// is followed by one fragment read; 4 = hard fences: each segment issues the
+// fragment reads of k-chunk kc+1, then the MFMAs of chunk kc, whose operands
+// were read one segment earlier (so no MFMA waits on a fresh LDS read).
+template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_pipe_kernel(T* __restrict__ out, const T* __restrict__ A,
                                                                 const T* __restrict__ W,
                                                                 const T* __restrict__ bias, int M, int N,
                                                                 int K, int group_m, int remap) {
-    constexpr int NW = WM * WN, NT = NW * 64;
+    // RB: bytes of k per tile row (64 or 128); S: LDS stages (S-1 tiles in flight)
+    constexpr int NW = WM * WN;
     constexpr int VE = Vec<T>::N;
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-    constexpr int CH = BK / VE;  // 16-byte chunks per tile row
-    static_assert(CH == 8, "swizzle assumes 8 chunks (128 bytes) per tile row");
-    constexpr int LA = BM * CH / 64 / NW, LB = BN * CH / 64 / NW;  // DMA instructions per wave
+    constexpr int BK = RB / (int)sizeof(T);  // k elements per tile
+    constexpr int CH = RB / 16;              // 16-byte chunks per tile row
+    constexpr int RP = 256 / RB;             // rows sharing one 256-byte bank line
+    static_assert(CH == 4 || CH == 8, "64- or 128-byte tile rows");
+    static_assert(S >= 3 && S <= 6, "stages");
+    constexpr int LA = BM * CH / 64 / NW, LB = BN * CH / 64 / NW;  // copies per wave per tile
     static_assert(LA * 64 * NW == BM * CH && LB * 64 * NW == BN * CH, "tile/wave mismatch");
     constexpr int LPW = LA + LB;
-    __shared__ __attribute__((aligned(16))) T sA0[BM * BK];
-    __shared__ __attribute__((aligned(16))) T sB0[BN * BK];
-    __shared__ __attribute__((aligned(16))) T sA1[BM * BK];
-    __shared__ __attribute__((aligned(16))) T sB1[BN * BK];
-    __shared__ __attribute__((aligned(16))) T sA2[BM * BK];
-    __shared__ __attribute__((aligned(16))) T sB2[BN * BK];
+    static_assert(LPW * (S - 2) < 64, "vmcnt range");
+    constexpr int STAGE = (BM + BN) * BK;  // elements per stage (A tile then W tile)
+    constexpr int LDO = BN + VE;           // row stride of the output tile in the epilogue
+    // stage the output tile through LDS when it fits in 160 KiB
+    constexpr bool STAGED = BM * LDO * (int)sizeof(T) <= 160 * 1024;
+    constexpr int SMEM = (STAGED && BM * LDO > S * STAGE) ? BM * LDO : S * STAGE;
+    __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -249,20 +268,22 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds3_kernel(T* __restrict__ 
     const int in_g = pid - g * per_group;
     const int m0 = (first_m + in_g % gsz) * BM, n0 = (in_g / gsz) * BN;
 
-    // Per-lane source offsets (element index at k = 0) for this wave's DMA
-    // instructions; chunk q of the tile = row q/8, slot q%8.
+    // Chunk q of a tile = row q / CH, slot q % CH; the slot holds logical
+    // k-chunk slot ^ ((row / RP) % CH).
     int64_t offA[LA], offB[LB];
 #pragma unroll
     for (int j = 0; j < LA; j++) {
-        const int q = (wid * LA + j) * 64 + lane, row = q >> 3, lc = (q & 7) ^ (row & 7);
+        const int q = (wid * LA + j) * 64 + lane, row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
         offA[j] = (int64_t)min(m0 + row, M - 1) * K + lc * VE;
     }
 #pragma unroll
     for (int j = 0; j < LB; j++) {
-        const int q = (wid * LB + j) * 64 + lane, row = q >> 3, lc = (q & 7) ^ (row & 7);
+        const int q = (wid * LB + j) * 64 + lane, row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
         offB[j] = (int64_t)min(n0 + row, N - 1) * K + lc * VE;
     }
-    auto issue = [&](T* sA, T* sB, int k0) {
+    auto issue = [&](int stage, int k0) {
+        T* sA = smem + stage * STAGE;
+        T* sB = sA + BM * BK;
 #pragma unroll
         for (int j = 0; j < LA; j++)
             copy16_to_lds(A + offA[j] + k0, (lds_void_ptr)(sA + (wid * LA + j) * 64 * VE));
@@ -277,77 +298,148 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds3_kernel(T* __restrict__ 
 #pragma unroll
         for (int j = 0; j < TN; j++) acc[i][j] = f32x16{};
 
-    auto compute = [&](const T* sA, const T* sB) {
+    auto load_frags = [&](const T* sA, const T* sB, int kc, u32x4 (&fa)[TM], u32x4 (&fb)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+            const int row = wm * TM * 32 + i * 32 + r32;
+            fa[i] = *reinterpret_cast<const u32x4*>(&sA[row * BK + (((2 * kc + h) ^ ((row / RP) % CH)) * VE)]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int row = wn * TN * 32 + j * 32 + r32;
+            fb[j] = *reinterpret_cast<const u32x4*>(&sB[row * BK + (((2 * kc + h) ^ ((row / RP) % CH)) * VE)]);
+        }
+    };
+    auto compute = [&](const int stage) {
+        const T* sA = smem + stage * STAGE;
+        const T* sB = sA + BM * BK;
+        u32x4 fa[2][TM], fb[2][TN];
+        load_frags(sA, sB, 0, fa[0], fb[0]);
+        if constexpr (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
+        if constexpr (SCHED == 2) __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
         for (int kc = 0; kc < CH / 2; kc++) {
-            u32x4 fa[TM], fb[TN];
-#pragma unroll
-            for (int i = 0; i < TM; i++) {
-                const int row = wm * TM * 32 + i * 32 + r32;
-                fa[i] = *reinterpret_cast<const u32x4*>(&sA[row * BK + (((2 * kc + h) ^ (row & 7)) * VE)]);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const int row = wn * TN * 32 + j * 32 + r32;
-                fb[j] = *reinterpret_cast<const u32x4*>(&sB[row * BK + (((2 * kc + h) ^ (row & 7)) * VE)]);
-            }
+            if constexpr (SCHED == 4) __builtin_amdgcn_sched_barrier(0);
+            if (kc + 1 < CH / 2) load_frags(sA, sB, kc + 1, fa[(kc + 1) & 1], fb[(kc + 1) & 1]);
+            if constexpr (SCHED == 4) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 0; e < Mfma32<T>::STEPS; e++)
 #pragma unroll
                 for (int i = 0; i < TM; i++)
 #pragma unroll
-                    for (int j = 0; j < TN; j++) Mfma32<T>::step(acc[i][j], fa[i], fb[j], e);
+                    for (int j = 0; j < TN; j++)
+                        Mfma32<T>::step(acc[i][j], fa[kc & 1][i], fb[kc & 1][j], e);
         }
     };
 
     const int nk = K / BK;
-    issue(sA0, sB0, 0);
-    if (nk > 1) issue(sA1, sB1, BK);
-    // One k-tile per step: wait for this tile's loads (the next tile's may
-    // stay in flight), barrier, launch the tile two ahead into the stage the
-    // previous step just finished reading, compute.
-#define GEMM_LDS3_STEP(SA, SB, SA2, SB2, T_)            \
-    {                                                      \
-        const int t = (T_);                                \
-        if (t + 1 < nk) wait_vmcnt<LPW>();                 \
-        else wait_vmcnt<0>();                              \
-        __builtin_amdgcn_s_barrier();                      \
-        if (t + 2 < nk) issue(SA2, SB2, (t + 2) * BK);     \
-        compute(SA, SB);                                   \
-    }
+#pragma unroll
+    for (int t = 0; t < S - 1; t++)
+        if (t < nk) issue(t, t * BK);
+    // One k-tile per step: wait until only the later tiles' copies may still
+    // be in flight (and this wave's LDS reads are done), barrier, launch the
+    // tile S-1 ahead into the stage the previous step finished reading,
+    // compute. Steps are unrolled S at a time so every stage offset is a
+    // compile-time constant.
+    auto step = [&](auto stage_c, int t) {
+        constexpr int st = decltype(stage_c)::value;
+        if (t + S - 2 < nk) {
+            wait_vmcnt_lds<(S - 2) * LPW>();
+        } else {
+            const int ahead = nk - 1 - t;  // < S - 2 here
+            if constexpr (S - 2 > 3) { if (ahead == 3) wait_vmcnt_lds<3 * LPW>(); }
+            if constexpr (S - 2 > 2) { if (ahead == 2) wait_vmcnt_lds<2 * LPW>(); }
+            if (ahead == 1) wait_vmcnt_lds<LPW>();
+            if (ahead <= 0) wait_vmcnt_lds<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        if (t + S - 1 < nk) issue((st + S - 1) % S, (t + S - 1) * BK);
+        compute(st);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
     int kt = 0;
-    for (; kt + 3 <= nk; kt += 3) {
-        GEMM_LDS3_STEP(sA0, sB0, sA2, sB2, kt)
-        GEMM_LDS3_STEP(sA1, sB1, sA0, sB0, kt + 1)
-        GEMM_LDS3_STEP(sA2, sB2, sA1, sB1, kt + 2)
+    for (; kt + S <= nk; kt += S) {
+        step(I0{}, kt);
+        step(I1{}, kt + 1);
+        step(I2{}, kt + 2);
+        if constexpr (S > 3) step(I3{}, kt + 3);
+        if constexpr (S > 4) step(I4{}, kt + 4);
+        if constexpr (S > 5) step(I5{}, kt + 5);
     }
-    if (kt < nk) GEMM_LDS3_STEP(sA0, sB0, sA2, sB2, kt)
-    if (kt + 1 < nk) GEMM_LDS3_STEP(sA1, sB1, sA0, sB0, kt + 1)
-#undef GEMM_LDS3_STEP
+    if (kt < nk) step(I0{}, kt);
+    if (kt + 1 < nk) step(I1{}, kt + 1);
+    if constexpr (S > 3) { if (kt + 2 < nk) step(I2{}, kt + 2); }
+    if constexpr (S > 4) { if (kt + 3 < nk) step(I3{}, kt + 3); }
+    if constexpr (S > 5) { if (kt + 4 < nk) step(I4{}, kt + 4); }
 
+    // Epilogue through LDS: every copy has landed (the last step waited for
+    // vmcnt 0); once all waves are past this barrier the stage memory is
+    // free. Each wave adds the bias, rounds to T and writes its tiles into a
+    // row-major [BM][BN] tile (rows padded by 16 bytes); the workgroup then
+    // stores whole 16-byte row chunks, so a wavefront writes 1 KiB of
+    // contiguous rows per instruction instead of 2- or 4-byte scattered
+    // elements.
+    if constexpr (STAGED) {
+        __builtin_amdgcn_s_barrier();
+        T* so = smem;
 #pragma unroll
-    for (int j = 0; j < TN; j++) {
-        const int col = n0 + wn * TN * 32 + j * 32 + r32;
-        if (col >= N) continue;
-        const float bv = bias ? load_scalar(bias + col) : 0.f;
+        for (int j = 0; j < TN; j++) {
+            const int cl = wn * TN * 32 + j * 32 + r32;
+            const float bv = (bias && n0 + cl < N) ? load_scalar(bias + n0 + cl) : 0.f;
 #pragma unroll
-        for (int i = 0; i < TM; i++) {
+            for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (row < M) store_scalar(out + (int64_t)row * N + col, acc[i][j][v] + bv);
-            }
+                for (int v = 0; v < 16; v++) {
+                    const int rl = wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    store_scalar(&so[rl * LDO + cl], acc[i][j][v] + bv);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt((0xF) | (7 << 4) | (0x0 << 8) | (3 << 14));  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        constexpr int CPR = BN / VE;  // 16-byte chunks per tile row
+#pragma unroll 4
+        for (int c = tid; c < BM * CPR; c += NW * 64) {
+            const int rl = c / CPR, cv = c % CPR;
+            const int row = m0 + rl, col = n0 + cv * VE;
+            if (row < M && col < N)
+                *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) =
+                    *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int col = n0 + wn * TN * 32 + j * 32 + r32;
+            if (col >= N) continue;
+            const float bv = bias ? load_scalar(bias + col) : 0.f;
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (row < M) store_scalar(out + (int64_t)row * N + col, acc[i][j][v] + bv);
+                }
         }
     }
 }
 
-template <typename T, int WM, int WN, int TM, int TN>
+template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED>
+static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
+                             int group_m, int remap, hipStream_t s) {
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED><<<nwg, WM * WN * 64, 0, s>>>(
+        out, A, W, bias, M, N, K, group_m, remap);
+}
+
+template <typename T, int WM, int WN, int TM, int TN, int SCHED = 4>
 static void launch_gemm_lds3(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
                              int group_m, int remap, hipStream_t s) {
-    constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BK = Vec<T>::N * 8;
-    const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_lds3_kernel<T, WM, WN, TM, TN, BK><<<nwg, WM * WN * 64, 0, s>>>(out, A, W, bias, M, N, K,
-                                                                         group_m, remap);
+    launch_gemm_pipe<T, WM, WN, TM, TN, 128, 3, SCHED>(out, A, W, bias, M, N, K, group_m, remap, s);
 }
 
 template <typename T, int WM, int WN, int TM, int TN, int BK, bool ILV = true>

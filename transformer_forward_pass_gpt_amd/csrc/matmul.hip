@@ -6,36 +6,50 @@
 
 namespace gpt2 {
 
-// Tile shapes, chosen per problem from measurements on MI355X over the GPT-2
-// small and medium layer shapes. When K is a whole number of 128-byte k-tiles
-// the pipelined kernel (three LDS stages filled by load-to-LDS copies) runs;
-// otherwise, and for the 32-row decode problems, the register-staged kernel.
+// Tile shapes, chosen per problem from on-box sweeps (MI355X) over the GPT-2
+// small and medium layer shapes. The pipelined kernel (S LDS stages filled by
+// load-to-LDS copies, k-tile rows of RB bytes) runs whenever K is a whole
+// number of k-tiles; otherwise, and for the 32-row decode problems, the
+// register-staged kernel with a masked k tail.
+struct PipeCfg {
+    const char* name;
+    int bk_bytes;  // RB: bytes of k per tile row
+};
 enum GemmCfg {
-    R32x64 = 0, R64x64, R64x128, R128x96,     // register-staged (gemm_kernel)
-    P64x64, P64x128, P128x96, P128x128, P128x192, P256x128,  // pipelined (gemm_lds3_kernel)
+    R32x64 = 0, R64x64, R64x128, R128x96,
+    P64x64, P128x96_S4, P128x96_S5, P128x128, P128x192, P256x128_S3A, P256x128_S3B, P256x256,
     G_NCFG
 };
-static const char* kCfgName[G_NCFG] = {"32x64_r", "64x64_r", "64x128_r", "128x96_r", "64x64_p3",
-                                       "64x128_p3", "128x96_p3", "128x128_p3", "128x192_p3",
-                                       "256x128_p3"};
+static const PipeCfg kCfg[G_NCFG] = {
+    {"32x64_r", 0},         {"64x64_r", 0},          {"64x128_r", 0},      {"128x96_r", 0},
+    {"64x64_p6", 64},       {"128x96_p4", 128},      {"128x96_p5", 128},   {"128x128_p6", 64},
+    {"128x192_p5", 64},     {"256x128_p3", 128},     {"256x128_p3s", 128}, {"256x256_p4", 64},
+};
+
+static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
+    auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (dtype == GPT2_F32) {
+        if (N >= 16384) return P256x128_S3A;                 // vocabulary projection
+        if (K >= 2048) return P128x96_S5;                    // fcproj
+        if (N <= 1024) return P128x96_S4;                    // attproj
+        return N >= 3072 ? P128x192 : P64x64;                // fc, qkv
+    }
+    if (N >= 16384) return P256x256;
+    if (K >= 2048 || N <= 1024) return tiles(256, 128) >= 192 ? P256x128_S3A : P128x128;
+    if (M <= 4096 && tiles(256, 256) >= 192) return P256x256;
+    return tiles(256, 128) >= 256 ? P256x128_S3B : P128x128;
+}
 
 static GemmCfg choose_cfg(int M, int N, int K, int dtype) {
     auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    const int bk = dtype == GPT2_BF16 ? 64 : 32;
-    if (M <= 32) return R32x64;
-    if (K % bk != 0) {  // no whole k-tiles: register-staged kernel with a masked tail
+    if (M > 32) {
+        const GemmCfg p = choose_pipe(M, N, K, dtype);
+        const int bk = kCfg[p].bk_bytes / (dtype == GPT2_BF16 ? 2 : 4);
+        if (K % bk == 0) return p;
         if (tiles(128, 96) >= 1024) return R128x96;
         return tiles(64, 128) >= 256 ? R64x128 : R64x64;
     }
-    if (dtype == GPT2_F32) {
-        if (N >= 16384) return P64x128;                 // vocabulary projection
-        if (K >= 2048 || N <= 1024) return P128x96;     // fcproj, attproj
-        return N >= 3072 ? P64x128 : P64x64;            // fc, qkv
-    }
-    if (N >= 16384) return P256x128;
-    if (K >= 2048) return tiles(128, 192) >= 256 ? P128x192 : P128x128;
-    if (N <= 1024) return tiles(128, 192) >= 256 ? P128x192 : P64x128;
-    return tiles(256, 128) >= 384 ? P256x128 : P64x128;
+    return R32x64;
 }
 
 template <typename T>
@@ -47,12 +61,15 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, int M, 
         case R64x64: launch_gemm_cfg<T, 2, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 4, 1, s); break;
         case R64x128: launch_gemm_cfg<T, 2, 2, 1, 2, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
         case R128x96: launch_gemm_cfg<T, 4, 1, 1, 3, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P64x64: launch_gemm_lds3<T, 2, 2, 1, 1>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P64x128: launch_gemm_lds3<T, 1, 4, 2, 1>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P128x96: launch_gemm_lds3<T, 4, 1, 1, 3>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P128x128: launch_gemm_lds3<T, 2, 2, 2, 2>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P128x192: launch_gemm_lds3<T, 2, 2, 2, 3>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        default: launch_gemm_lds3<T, 4, 2, 2, 2>(out, A, W, bias, M, N, K, 1, 0, s); break;
+        // launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SCHED>(..., group_m, remap, s)
+        case P64x64: launch_gemm_pipe<T, 2, 2, 1, 1, 64, 6, 1>(out, A, W, bias, M, N, K, 4, 1, s); break;
+        case P128x96_S4: launch_gemm_pipe<T, 4, 1, 1, 3, 128, 4, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P128x96_S5: launch_gemm_pipe<T, 4, 1, 1, 3, 128, 5, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P128x128: launch_gemm_pipe<T, 2, 2, 2, 2, 64, 6, 2>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P128x192: launch_gemm_pipe<T, 2, 2, 2, 3, 64, 5, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P256x128_S3A: launch_gemm_pipe<T, 4, 2, 2, 2, 128, 3, 2>(out, A, W, bias, M, N, K, 1, 0, s); break;
+        case P256x128_S3B: launch_gemm_pipe<T, 4, 2, 2, 2, 128, 3, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        default: launch_gemm_pipe<T, 2, 4, 4, 2, 64, 4, 2>(out, A, W, bias, M, N, K, 4, 1, s); break;
     }
 }
 
@@ -60,7 +77,7 @@ static thread_local char g_cfg_name[64];
 
 const char* matmul_config_name(int N, int C, int OC, int dtype) {
     snprintf(g_cfg_name, sizeof g_cfg_name, "gemm_%s_%s", dtype == GPT2_BF16 ? "bf16" : "f32",
-             kCfgName[choose_cfg(N, OC, C, dtype)]);
+             kCfg[choose_cfg(N, OC, C, dtype)].name);
     return g_cfg_name;
 }
 
