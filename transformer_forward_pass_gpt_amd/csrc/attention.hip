@@ -58,8 +58,14 @@ __device__ __forceinline__ int vt_slot_bf16(int key) {
     return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
+// Workgroup: 8 wavefronts = 4 query chunks of 32 x 2 key parities. Wave
+// (c, p) owns queries q0 + 32c .. +31 and the key blocks 2i + p, so the two
+// waves of a query chunk split its key range; their partial (o, m, l) merge
+// through LDS at the end, in a fixed order. Each iteration stages two key
+// blocks (the even and the odd one); when two iterations' worth fits in LDS
+// the next pair is loaded while the current one is computed.
 template <typename T, int HS>
-__global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
+__global__ __launch_bounds__(512) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
                                                         int Tn, int C, int NH, float sl2) {
     constexpr bool F32 = std::is_same<T, float>::value;
     constexpr int VE = Vec<T>::N;
@@ -69,31 +75,40 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
     static_assert(HS % (2 * VE) == 0, "head size must hold whole fragments");
     constexpr int LDK = HS + VE;    // K block [kBKV][HS], 16-byte row pad
     constexpr int LDV = kBKV + VE;  // V^T block [HSP][kBKV], 16-byte row pad
-    constexpr int RV = HS / VE;                          // 16-byte vectors per key row
-    constexpr int NKV = (kBKV * RV + 255) / 256;         // K vectors per thread
-    constexpr int NVS = (kBKV / 4 * RV + 255) / 256;     // V 4-key sub-blocks per thread
-    __shared__ __attribute__((aligned(16))) T Ks[2][kBKV * LDK];
-    __shared__ __attribute__((aligned(16))) T Vt[2][HSP * LDV];
+    constexpr int KSZ = kBKV * LDK, VSZ = HSP * LDV;  // elements per block
+    constexpr int PAIR = 2 * (KSZ + VSZ);             // one iteration: even + odd block
+    constexpr bool DB = 2 * PAIR * (int)sizeof(T) <= 160 * 1024;  // double-buffered
+    constexpr int NBUF = DB ? 2 : 1;
+    constexpr int RV = HS / VE;                                  // 16-byte vectors per key row
+    constexpr int NKV = (2 * kBKV * RV + 511) / 512;             // K vectors per thread
+    constexpr int NVS = (2 * kBKV / 4 * RV + 511) / 512;         // V 4-key sub-blocks per thread
+    constexpr int MERGE = 4 * 64 * (DT * 16 + 2);                // floats for the parity merge
+    static_assert(MERGE * 4 <= NBUF * PAIR * (int)sizeof(T), "merge area");
+    __shared__ __attribute__((aligned(16))) T smem[NBUF * PAIR];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int qc = wid & 3, par = wid >> 2;
     const int h = lane >> 5, r32 = lane & 31;
     // Workgroups are dispatched in linear order (x fastest): all (batch, head)
     // pairs of the last, longest query block first, then the next, so the
     // causal triangle's long rows never end up in the tail.
     const int qb = gridDim.y - 1 - blockIdx.y;
     const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
-    const int q0 = qb * kBQ, qw = q0 + wid * 32;
+    const int q0 = qb * kBQ, qw = q0 + qc * 32;
     const int64_t rs = 3 * (int64_t)C;
     const T* base = qkv + (int64_t)b * Tn * rs;
     const int qoff = hd * HS, koff = C + hd * HS, voff = 2 * C + hd * HS;
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    auto Kblk = [&](int buf, int p) { return smem + buf * PAIR + p * KSZ; };
+    auto Vblk = [&](int buf, int p) { return smem + buf * PAIR + 2 * KSZ + p * VSZ; };
 
     // Padded head rows of V^T (HS < 32) are never loaded: zero them once.
     if (HS < HSP) {
-        for (int i = tid; i < 2 * (HSP - HS) * LDV; i += 256) {
-            const int buf = i / ((HSP - HS) * LDV), j = i % ((HSP - HS) * LDV);
-            if constexpr (F32) Vt[buf][HS * LDV + j] = 0.f;
-            else Vt[buf][HS * LDV + j].bits = 0;
+        for (int i = tid; i < NBUF * 2 * (HSP - HS) * LDV; i += 512) {
+            const int blk = i / ((HSP - HS) * LDV), j = i % ((HSP - HS) * LDV);
+            T* vb = Vblk(blk >> 1, blk & 1) + HS * LDV + j;
+            if constexpr (F32) *vb = 0.f;
+            else vb->bits = 0;
         }
     }
 
@@ -108,22 +123,22 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
                             : zero;
     }
 
-    // ---- K/V block staging: global -> registers -> LDS (double-buffered)
+    // ---- staging of a block pair: global -> registers -> LDS
     u32x4 rk[NKV], rv[NVS][4];
-    auto gload = [&](int k0) {
+    auto gload = [&](int k0) {  // keys k0 .. k0 + 127
 #pragma unroll
         for (int i = 0; i < NKV; i++) {
-            const int li = tid + i * 256, r = li / RV, cv = li % RV, key = k0 + r;
-            rk[i] = (li < kBKV * RV && key < Tn)
+            const int li = tid + i * 512, r = li / RV, cv = li % RV, key = k0 + r;
+            rk[i] = (li < 2 * kBKV * RV && key < Tn)
                         ? *reinterpret_cast<const u32x4*>(base + key * rs + koff + cv * VE) : zero;
         }
 #pragma unroll
         for (int i = 0; i < NVS; i++) {
-            const int li = tid + i * 256, kq = li / RV, cv = li % RV;  // keys 4kq..4kq+3
+            const int li = tid + i * 512, kq = li / RV, cv = li % RV;  // keys 4kq..4kq+3
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int key = k0 + 4 * kq + e;
-                rv[i][e] = (li < kBKV / 4 * RV && key < Tn)
+                rv[i][e] = (li < 2 * kBKV / 4 * RV && key < Tn)
                                ? *reinterpret_cast<const u32x4*>(base + key * rs + voff + cv * VE) : zero;
             }
         }
@@ -131,29 +146,32 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < NKV; i++) {
-            const int li = tid + i * 256, r = li / RV, cv = li % RV;
-            if (li < kBKV * RV) *reinterpret_cast<u32x4*>(&Ks[buf][r * LDK + cv * VE]) = rk[i];
+            const int li = tid + i * 512, r = li / RV, cv = li % RV;
+            if (li < 2 * kBKV * RV)
+                *reinterpret_cast<u32x4*>(&Kblk(buf, r / kBKV)[(r % kBKV) * LDK + cv * VE]) = rk[i];
         }
 #pragma unroll
         for (int i = 0; i < NVS; i++) {
-            const int li = tid + i * 256, kq = li / RV, cv = li % RV;
-            if (li < kBKV / 4 * RV) {
+            const int li = tid + i * 512, kq = li / RV, cv = li % RV;
+            if (li < 2 * kBKV / 4 * RV) {
+                T* vb = Vblk(buf, (4 * kq) / kBKV);
+                const int kl = (4 * kq) % kBKV;
                 // 4 keys x VE head dims -> VE rows of V^T, 4 consecutive slots each
                 if constexpr (F32) {
 #pragma unroll
                     for (int d = 0; d < 4; d++) {
                         const u32x4 col = {rv[i][0][d], rv[i][1][d], rv[i][2][d], rv[i][3][d]};
-                        *reinterpret_cast<u32x4*>(&Vt[buf][(cv * 4 + d) * LDV + 4 * kq]) = col;
+                        *reinterpret_cast<u32x4*>(&vb[(cv * 4 + d) * LDV + kl]) = col;
                     }
                 } else {
-                    const int slot = vt_slot_bf16(4 * kq);
+                    const int slot = vt_slot_bf16(kl);
 #pragma unroll
                     for (int d = 0; d < 8; d++) {
                         const int w = d >> 1, sh = 16 * (d & 1);
                         const uint32_t k0v = (rv[i][0][w] >> sh) & 0xffffu, k1v = (rv[i][1][w] >> sh) & 0xffffu;
                         const uint32_t k2v = (rv[i][2][w] >> sh) & 0xffffu, k3v = (rv[i][3][w] >> sh) & 0xffffu;
                         const u32x2 col = {k0v | (k1v << 16), k2v | (k3v << 16)};
-                        *reinterpret_cast<u32x2*>(&Vt[buf][(cv * 8 + d) * LDV + slot]) = col;
+                        *reinterpret_cast<u32x2*>(&vb[(cv * 8 + d) * LDV + slot]) = col;
                     }
                 }
             }
@@ -165,107 +183,149 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
     for (int dt = 0; dt < DT; dt++) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;  // for query qw + r32, in log2 units
 
-    const int kend = min(Tn, q0 + kBQ);
-    const int nkb = (kend + kBKV - 1) / kBKV;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; kb++) {
-        const int cur = kb & 1;
-        const int k0 = kb * kBKV;
-        if (kb + 1 < nkb) gload(k0 + kBKV);
-        if (k0 <= qw + 31) {  // some of this wave's queries see this block
-            // S^T tiles: keys k0 + kt*32 + (8*(v/4) + 4*h + v%4), query qw + r32
-            f32x16 s[2];
+    // One key block (keys k0..k0+63) for this wave's 32 queries.
+    auto block = [&](const T* Ks, const T* Vt, int k0) {
+        // S^T tiles: keys k0 + kt*32 + (8*(v/4) + 4*h + v%4), query qw + r32.
+        // The two key tiles' MFMAs alternate, so neither chain waits on itself.
+        f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int kt = 0; kt < 2; kt++) {
-                s[kt] = f32x16{};
+        for (int kc = 0; kc < KCH; kc++) {
+            const u32x4 ka0 = *reinterpret_cast<const u32x4*>(&Ks[r32 * LDK + kc * 2 * VE + h * VE]);
+            const u32x4 ka1 = *reinterpret_cast<const u32x4*>(&Ks[(32 + r32) * LDK + kc * 2 * VE + h * VE]);
+            if constexpr (F32) {
 #pragma unroll
-                for (int kc = 0; kc < KCH; kc++) {
-                    const u32x4 ka = *reinterpret_cast<const u32x4*>(
-                        &Ks[cur][(kt * 32 + r32) * LDK + kc * 2 * VE + h * VE]);
-                    MfmaS<T>::run(s[kt], ka, qf[kc]);
+                for (int e = 0; e < 4; e++) {
+                    s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ka0[e]), __uint_as_float(qf[kc][e]),
+                                                               s[0], 0, 0, 0);
+                    s[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ka1[e]), __uint_as_float(qf[kc][e]),
+                                                               s[1], 0, 0, 0);
                 }
+            } else {
+                MfmaS<T>::run(s[0], ka0, qf[kc]);
+                MfmaS<T>::run(s[1], ka1, qf[kc]);
             }
-            const int q = qw + r32;
-            float mx = -INFINITY;
-            if (k0 + kBKV - 1 > qw) {  // diagonal block: mask keys after the query
-#pragma unroll
-                for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-                    for (int v = 0; v < 16; v++) {
-                        const int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                        if (key > q) s[kt][v] = -INFINITY;
-                    }
-            }
-#pragma unroll
-            for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-                for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kt][v]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx * sl2);  // finite: key 0 is in the first block
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            float ls = 0.f;
+        }
+        const int q = qw + r32;
+        float mx = -INFINITY;
+        if (k0 + kBKV - 1 > qw) {  // diagonal block: mask keys after the query
 #pragma unroll
             for (int kt = 0; kt < 2; kt++)
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][v], sl2, -m_new));
-                    s[kt][v] = p;
-                    ls += p;
+                    const int key = k0 + kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (key > q) s[kt][v] = -INFINITY;
                 }
-            ls += __shfl_xor(ls, 32, 64);
-            l_run = l_run * alpha + ls;
-            m_run = m_new;
+        }
 #pragma unroll
-            for (int dt = 0; dt < DT; dt++)
+        for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-                for (int v = 0; v < 16; v++) o[dt][v] *= alpha;
+            for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kt][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // finite: a processed block always holds key k0 <= every query here
+        const float m_new = fmaxf(m_run, mx * sl2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][v], sl2, -m_new));
+                s[kt][v] = p;
+                ls += p;
+            }
+        ls += __shfl_xor(ls, 32, 64);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) o[dt][v] *= alpha;
 
-            // O^T += V^T P^T. The k slots of both operands name the same keys.
-            if constexpr (F32) {
+        // O^T += V^T P^T. The k slots of both operands name the same keys.
+        if constexpr (F32) {
 #pragma unroll
-                for (int kt = 0; kt < 2; kt++)
+            for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-                    for (int g = 0; g < 4; g++)
+                for (int g = 0; g < 4; g++)
 #pragma unroll
-                        for (int dt = 0; dt < DT; dt++) {
-                            // keys kt*32 + 8g + 4h + e, e = 0..3
-                            const u32x4 va = *reinterpret_cast<const u32x4*>(
-                                &Vt[cur][(dt * 32 + r32) * LDV + kt * 32 + 8 * g + 4 * h]);
-#pragma unroll
-                            for (int e = 0; e < 4; e++)
-                                o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                    __uint_as_float(va[e]), s[kt][4 * g + e], o[dt], 0, 0, 0);
-                        }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-                    for (int ks = 0; ks < 2; ks++) {
-                        // slot (h, e): key 16ks + 4h + e (e<4), 16ks + 8 + 4h + e-4 (e>=4)
-                        u32x4 pb;
+                    for (int dt = 0; dt < DT; dt++) {
+                        // keys kt*32 + 8g + 4h + e, e = 0..3
+                        const u32x4 va = *reinterpret_cast<const u32x4*>(
+                            &Vt[(dt * 32 + r32) * LDV + kt * 32 + 8 * g + 4 * h]);
 #pragma unroll
                         for (int e = 0; e < 4; e++)
-                            pb[e] = pack_bf16x2(s[kt][8 * ks + 2 * e], s[kt][8 * ks + 2 * e + 1]);
-#pragma unroll
-                        for (int dt = 0; dt < DT; dt++) {
-                            const u32x4 va = *reinterpret_cast<const u32x4*>(
-                                &Vt[cur][(dt * 32 + r32) * LDV + kt * 32 + 16 * ks + 8 * h]);
-                            MfmaS<T>::run(o[dt], va, pb);
-                        }
+                            o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(va[e]), s[kt][4 * g + e],
+                                                                        o[dt], 0, 0, 0);
                     }
-            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) {
+                    // slot (h, e): key 16ks + 4h + e (e<4), 16ks + 8 + 4h + e-4 (e>=4)
+                    u32x4 pb;
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        pb[e] = pack_bf16x2(s[kt][8 * ks + 2 * e], s[kt][8 * ks + 2 * e + 1]);
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt++) {
+                        const u32x4 va = *reinterpret_cast<const u32x4*>(
+                            &Vt[(dt * 32 + r32) * LDV + kt * 32 + 16 * ks + 8 * h]);
+                        MfmaS<T>::run(o[dt], va, pb);
+                    }
+                }
         }
-        if (kb + 1 < nkb) sstore(cur ^ 1);
+    };
+
+    const int kend = min(Tn, q0 + kBQ);
+    const int nkb = (kend + kBKV - 1) / kBKV;  // key blocks this workgroup needs
+    const int npair = (nkb + 1) / 2;
+    auto compute_pair = [&](int buf, int i) {
+        const int kb = 2 * i + par, k0 = kb * kBKV;
+        if (kb < nkb && k0 <= qw + 31) block(Kblk(buf, par), Vblk(buf, par), k0);
+    };
+    if constexpr (DB) {
+        gload(0);
+        sstore(0);
         __syncthreads();
+        for (int i = 0; i < npair; i++) {
+            const int cur = i & 1;
+            if (i + 1 < npair) gload((i + 1) * 2 * kBKV);
+            compute_pair(cur, i);
+            if (i + 1 < npair) sstore(cur ^ 1);
+            __syncthreads();
+        }
+    } else {
+        for (int i = 0; i < npair; i++) {
+            gload(i * 2 * kBKV);
+            sstore(0);
+            __syncthreads();
+            compute_pair(0, i);
+            __syncthreads();
+        }
     }
+
+    // Merge the two parities of each query chunk (fixed order: even + odd).
+    float* mg = reinterpret_cast<float*>(smem) + qc * 64 * (DT * 16 + 2);
+    if (par == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) mg[(dt * 16 + v) * 64 + lane] = o[dt][v];
+        mg[(DT * 16) * 64 + lane] = m_run;
+        mg[(DT * 16 + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (par == 1) return;
+    const float m1 = mg[(DT * 16) * 64 + lane], l1 = mg[(DT * 16 + 1) * 64 + lane];
+    const float m = fmaxf(m_run, m1);  // m_run is finite: the even half holds key block 0
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float inv = 1.0f / (l_run * a0 + l1 * a1);
 
     // O^T register v of lane (h, r32): head dim dt*32 + 8*(v/4) + 4*h + v%4,
     // query qw + r32. Four consecutive head dims per store.
     const int q = qw + r32;
     if (q < Tn) {
-        const float inv = 1.0f / l_run;
         T* orow = out + ((int64_t)b * Tn + q) * C + hd * HS;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)
@@ -273,12 +333,14 @@ __global__ __launch_bounds__(256) void attention_kernel(T* __restrict__ out, con
             for (int g = 0; g < 4; g++) {
                 const int d0 = dt * 32 + 8 * g + 4 * h;
                 if (d0 < HS) {
-                    const float x0 = o[dt][4 * g] * inv, x1 = o[dt][4 * g + 1] * inv;
-                    const float x2 = o[dt][4 * g + 2] * inv, x3 = o[dt][4 * g + 3] * inv;
+                    float x[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        x[e] = (o[dt][4 * g + e] * a0 + mg[(dt * 16 + 4 * g + e) * 64 + lane] * a1) * inv;
                     if constexpr (F32) {
-                        *reinterpret_cast<float4*>(orow + d0) = make_float4(x0, x1, x2, x3);
+                        *reinterpret_cast<float4*>(orow + d0) = make_float4(x[0], x[1], x[2], x[3]);
                     } else {
-                        u32x2 pk = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+                        u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
                         *reinterpret_cast<u32x2*>(orow + d0) = pk;
                     }
                 }
@@ -290,7 +352,7 @@ template <typename T, int HS>
 static void launch_attn_hs(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)HS);  // log2(e)/sqrt(hs)
     dim3 grid(B * NH, (Tn + kBQ - 1) / kBQ);
-    attention_kernel<T, HS><<<grid, 256, 0, s>>>(out, qkv, Tn, C, NH, sl2);
+    attention_kernel<T, HS><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2);
 }
 
 template <typename T>
