@@ -132,9 +132,13 @@ __global__ __launch_bounds__(512) void attention_kernel(T* __restrict__ out, con
             rk[i] = (li < 2 * kBKV * RV && key < Tn)
                         ? *reinterpret_cast<const u32x4*>(base + key * rs + koff + cv * VE) : zero;
         }
+        // V sub-block li: keys 4kq..4kq+3, head dims cv*VE..; consecutive lanes
+        // take consecutive key quads, so the 16 lanes of one LDS write cycle
+        // fill one contiguous run of a V^T row (no bank conflicts).
 #pragma unroll
         for (int i = 0; i < NVS; i++) {
-            const int li = tid + i * 512, kq = li / RV, cv = li % RV;  // keys 4kq..4kq+3
+            const int li = tid + i * 512, rest = li >> 4;
+            const int kq = (rest / RV) * 16 + (li & 15), cv = rest % RV;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int key = k0 + 4 * kq + e;
@@ -152,7 +156,8 @@ __global__ __launch_bounds__(512) void attention_kernel(T* __restrict__ out, con
         }
 #pragma unroll
         for (int i = 0; i < NVS; i++) {
-            const int li = tid + i * 512, kq = li / RV, cv = li % RV;
+            const int li = tid + i * 512, rest = li >> 4;
+            const int kq = (rest / RV) * 16 + (li & 15), cv = rest % RV;
             if (li < 2 * kBKV / 4 * RV) {
                 T* vb = Vblk(buf, (4 * kq) / kBKV);
                 const int kl = (4 * kq) % kBKV;
