@@ -5,12 +5,15 @@
 
 One step = one gpt2_forward (encoder, 12 blocks, final LayerNorm, logits GEMM,
 vocabulary softmax) over one batch of synthetic tokens, with weights, tokens,
-workspace and outputs already resident in HBM. Prints ONE JSON line.
+workspace and outputs already resident in HBM. Prints ONE JSON line. With
+``--workload decode`` a step is one gpt2_decode_step instead: one new token
+for each of 32 sequences against a prefilled key/value cache.
 
 Besides the end-to-end rate it times every kernel of one forward with HIP
 events (the same launches gpt2_forward makes, issued one entry at a time on
-the same stream) to report the dominant kernel against its roofline, and it
-times the CPU oracle on a bounded sample of the same workload.
+the same stream, queued behind a GPU spin so that they run back to back) to
+report the dominant kernel against its roofline, and it times the CPU oracle
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -43,6 +46,8 @@ def parse():
                     help="small (fp32 B4 T1024, default), small_bf16_b4, small_bf16_b8, medium, decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=32,
+                    help="decode workload: sequences the CPU oracle steps")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--profile-kernel", action="store_true",
                     help="counter-collection mode: launch only the logits GEMM (3x) and a "
@@ -51,7 +56,7 @@ def parse():
 
 
 class Bench:
-    def __init__(self, w):
+    def __init__(self, w, keep_host_cache=False):
         import torch
         import transformer_forward_pass_gpt_amd as G
         from transformer_forward_pass_gpt_amd import inputs as I
@@ -69,14 +74,52 @@ class Bench:
         self.tokens_np = I.make_tokens(w)
         self.tokens = torch.from_numpy(self.tokens_np).cuda()
         B, T = w.B, w.T
-        self.logits = torch.empty((B, T, w.Vp), dtype=self.tdtype, device="cuda")
+        self.decode = w.decode_pos >= 0
+        if self.decode:
+            kc, vc = I.make_kv_cache(w)
+            self.kcache, self.vcache = self.to_dev(kc), self.to_dev(vc)
+            self.kc_np, self.vc_np = (kc, vc) if keep_host_cache else (None, None)
+            del kc, vc
+            self.logits = torch.empty((B, w.Vp), dtype=self.tdtype, device="cuda")
+            ws = G.decode_workspace_bytes(self.cfg, B)
+        else:
+            self.logits = torch.empty((B, T, w.Vp), dtype=self.tdtype, device="cuda")
+            ws = G.workspace_bytes(self.cfg, B, T)
         self.probs = torch.empty_like(self.logits)
-        self.ws = torch.empty(G.workspace_bytes(self.cfg, B, T), dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+
+    def to_dev(self, a):
+        if self.w.dtype == self.I.BF16:
+            bits = self.I.to_bf16_bits(a).view(np.int16)
+            return self.torch.from_numpy(bits).cuda().view(self.torch.bfloat16)
+        return self.torch.from_numpy(a).cuda()
 
     def step(self):
-        self.G.gpt2_forward(self.logits, self.probs, self.tokens, self.params, self.cfg, self.ws)
+        if self.decode:
+            self.G.gpt2_decode_step(self.logits, self.probs, self.tokens, self.w.decode_pos, self.kcache,
+                                    self.vcache, self.params, self.cfg, self.ws)
+        else:
+            self.G.gpt2_forward(self.logits, self.probs, self.tokens, self.params, self.cfg, self.ws)
 
     # ------------------------------------------------------------ per-kernel timing
+    def gpu_hold(self, ms):
+        """Queue a spin kernel that keeps the stream busy for about `ms`, so the
+        launches enqueued behind it run back to back and the HIP events between
+        them measure GPU time, not host launch gaps."""
+        torch = self.torch
+        if not hasattr(self, "_cycles_per_ms"):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(1000)
+            a.record()
+            torch.cuda._sleep(2_000_000)
+            b.record()
+            torch.cuda.synchronize()
+            cpm = 2_000_000 / max(a.elapsed_time(b), 1e-6)
+            # a counter between 10 MHz and 10 GHz; anything else: no hold
+            self._cycles_per_ms = cpm if 1e4 <= cpm <= 1e7 else 0.0
+        if self._cycles_per_ms:
+            torch.cuda._sleep(int(min(ms, 200.0) * self._cycles_per_ms))
+
     def kernel_timing(self, reps=3):
         """Issue one forward entry by entry, HIP events around each launch on
         the current stream; returns per-launch records (median over reps)."""
@@ -100,9 +143,14 @@ class Bench:
         recs = []
 
         def timed(kind, name, fn, flops=0.0, nbytes=0.0, site=None):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(s)
+            # consecutive launches share the event between them
+            if not recs:
+                a = torch.cuda.Event(enable_timing=True)
+                a.record(s)
+            else:
+                a = recs[-1][5]
             fn()
+            b = torch.cuda.Event(enable_timing=True)
             b.record(s)
             recs.append([kind, name, flops, nbytes, a, b, site or name])
 
@@ -111,8 +159,11 @@ class Bench:
             "gemm", G.matmul_kernel_config(M, K, Nc, w.dtype),
             lambda: G.matmul_forward(out, inp, wt, bias), 2.0 * M * Nalg * K, 0.0, "gemm_" + tag)
         all_runs = []
-        for _ in range(reps):
+        host_ms = 50.0
+        for _ in range(reps + 1):  # the first pass measures the host enqueue time
             recs.clear()
+            self.gpu_hold(1.2 * host_ms)
+            t0 = time.perf_counter()
             timed("hbm", "encoder", lambda: G.encoder_forward(x.view(B, T, C), self.tokens, P("wte"), P("wpe")),
                   0.0, 4 * N + 2 * N * C * es + T * C * es)
             for l in range(L):
@@ -134,8 +185,104 @@ class Bench:
             gemm(logits, ln, P("wte"), None, N, C, w.Vp, w.V, "logits")
             timed("hbm", "softmax", lambda: G.softmax_forward(probs, logits, w.V), 0.0,
                   N * w.V * es + N * w.Vp * es)
+            host_ms = (time.perf_counter() - t0) * 1e3
             torch.cuda.synchronize()
             all_runs.append([r[:4] + [r[4].elapsed_time(r[5]), r[6]] for r in recs])
+        all_runs = all_runs[1:]
+        out = []
+        for i in range(len(all_runs[0])):
+            ms = float(np.median([run[i][4] for run in all_runs]))
+            out.append(all_runs[0][i][:4] + [ms, all_runs[0][i][5]])
+        return out
+
+
+    def decode_kernel_timing(self, reps=3):
+        """The launches of one gpt2_decode_step (batches of at most 32
+        sequences), entry by entry, HIP events around each. Every kernel of a
+        decode step is bound by HBM (the GEMMs stream their weights once for
+        32 rows), so each record carries the algorithmic bytes: operands read
+        once, results written once."""
+        torch, G, I, w = self.torch, self.G, self.I, self.w
+        B, C, L, NH, pos = w.B, w.C, w.L, w.NH, w.decode_pos
+        es = self.es
+        offs = I.param_offsets(L, C, w.maxT, w.Vp)
+
+        def P(name, l=None):
+            o, shp = offs[name]
+            n = int(np.prod(shp))
+            t = self.params[o:o + n].view(*shp)
+            return t if l is None else t[l]
+
+        mk = lambda *s: torch.empty(s, dtype=self.tdtype, device="cuda")  # noqa: E731
+        x, ln, qkv, att, tmp, fc = mk(B, C), mk(B, C), mk(B, 3 * C), mk(B, C), mk(B, C), mk(B, 4 * C)
+        aws = torch.empty(G.attention_decode_workspace_bytes(B, C, NH, w.maxT), dtype=torch.uint8,
+                          device="cuda")
+        s = torch.cuda.current_stream()
+        recs = []
+
+        def timed(name, fn, nbytes, site=None):
+            # consecutive launches share the event between them
+            if not recs:
+                a = torch.cuda.Event(enable_timing=True)
+                a.record(s)
+            else:
+                a = recs[-1][5]
+            fn()
+            b = torch.cuda.Event(enable_timing=True)
+            b.record(s)
+            recs.append(["hbm", name, 0.0, float(nbytes), a, b, site or name])
+
+        def gemm(out, inp, wt, bias, K, Nc, tag):
+            nb = (Nc * K + B * K + B * Nc + (Nc if bias is not None else 0)) * es
+            timed(G.matmul_kernel_config(B, K, Nc, w.dtype), lambda: G.matmul_forward(out, inp, wt, bias), nb,
+                  "gemm_" + tag)
+
+        att_bytes = (B * (pos + 1) * C * 2 + B * 3 * C + B * C) * es
+        s_ap = G.matmul_splitk_count(C, C, w.dtype)
+        s_fp = G.matmul_splitk_count(4 * C, C, w.dtype)
+        part = torch.empty(max(s_ap, s_fp) * B * C, dtype=torch.float32, device="cuda")
+        pap, pfp = part[:s_ap * B * C].view(s_ap, B, C), part[:s_fp * B * C].view(s_fp, B, C)
+
+        def splitk(pt, inp, wt, K, Nc, tag):
+            nb = (Nc * K + B * K) * es + pt.numel() * 4
+            timed("gemm_%s_splitk%d" % ("bf16" if w.dtype == I.BF16 else "f32", pt.shape[0]),
+                  lambda: G.matmul_splitk_forward(pt, inp, wt, pt.shape[0]), nb, "gemm_" + tag)
+
+        def res_ln(pt, bias, g, b_, tag):
+            nb = 3 * B * C * es + pt.numel() * 4 + 3 * C * es
+            timed("residual_layernorm", lambda: G.residual_layernorm_forward(ln, x, pt, bias, g, b_, w.ln_eps), nb,
+                  tag)
+
+        all_runs = []
+        host_ms = 50.0
+        for _ in range(reps + 1):  # the first pass measures the host enqueue time
+            recs.clear()
+            self.gpu_hold(1.2 * host_ms)
+            t0 = time.perf_counter()
+            timed("encoder", lambda: G.encoder_forward(x.view(B, 1, C), self.tokens.view(B, 1), P("wte"),
+                                                       P("wpe")[pos:pos + 1]),
+                  4 * B + 2 * B * C * es + C * es)
+            timed("layernorm", lambda: G.layernorm_forward(ln, x, P("ln1_g", 0), P("ln1_b", 0), w.ln_eps),
+                  2 * B * C * es + 2 * C * es)
+            for l in range(L):
+                gemm(qkv, ln, P("qkv_w", l), P("qkv_b", l), C, 3 * C, "qkv")
+                timed("attention_decode", lambda: G.attention_decode_forward(
+                    att, qkv, self.kcache[l], self.vcache[l], pos, NH, aws), att_bytes)
+                splitk(pap, att, P("attproj_w", l), C, C, "attproj")
+                res_ln(pap, P("attproj_b", l), P("ln2_g", l), P("ln2_b", l), "residual_ln2")
+                timed(G.matmul_kernel_config(B, C, 4 * C, w.dtype) + "_gelu",
+                      lambda: G.matmul_gelu_forward(fc, ln, P("fc_w", l), P("fc_b", l)),
+                      (4 * C * C + B * C + B * 4 * C + 4 * C) * es, "gemm_fc_gelu")
+                splitk(pfp, fc, P("fcproj_w", l), 4 * C, C, "fcproj")
+                last = l == L - 1
+                res_ln(pfp, P("fcproj_b", l), P("lnf_g") if last else P("ln1_g", l + 1),
+                       P("lnf_b") if last else P("ln1_b", l + 1), "residual_ln1")
+            gemm(self.logits, ln, P("wte"), None, C, w.Vp, "logits")
+            timed("softmax", lambda: G.softmax_forward(self.probs, self.logits, w.V), B * w.V * es + B * w.Vp * es)
+            host_ms = (time.perf_counter() - t0) * 1e3
+            torch.cuda.synchronize()
+            all_runs.append([r[:4] + [r[4].elapsed_time(r[5]), r[6]] for r in recs])
+        all_runs = all_runs[1:]
         out = []
         for i in range(len(all_runs[0])):
             ms = float(np.median([run[i][4] for run in all_runs]))
@@ -243,6 +390,23 @@ def cpu_baseline(b, ntok):
                       "single-threaded C oracle)" % (ntok - 1, ntok, dt)}
 
 
+def cpu_baseline_decode(b, nseq):
+    """The oracle's decode step, single-threaded, for the first nseq of the 32
+    sequences (sequences are independent, so this is exactly their share of
+    the workload)."""
+    import oracle
+    w = b.w
+    kc = np.ascontiguousarray(b.kc_np[:, :nseq])
+    vc = np.ascontiguousarray(b.vc_np[:, :nseq])
+    tok = b.tokens_np[:nseq]
+    t0 = time.perf_counter()
+    oracle.decode_step(tok, w.decode_pos, kc, vc, b.params_np, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps)
+    dt = time.perf_counter() - t0
+    return {"value": round(nseq / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "decode step for sequences 0..%d of the 32 at position %d (%d tokens, %.1f s, "
+                      "single-threaded C oracle)" % (nseq - 1, w.decode_pos, nseq, dt)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -253,11 +417,12 @@ def main():
     import torch
     from transformer_forward_pass_gpt_amd import inputs as I
     w = I.WORKLOADS[args.workload]
-    if w.decode_pos >= 0:
-        raise SystemExit("decode workload: use bench_decode (not yet wired)")
+    decode = w.decode_pos >= 0
     torch.cuda.set_device(0)
-    b = Bench(w)
+    b = Bench(w, keep_host_cache=decode and not args.no_cpu_baseline)
     if args.profile_kernel:
+        if decode:
+            raise SystemExit("--profile-kernel runs the prefill logits GEMM; use a forward workload")
         profile_kernel(b)
         return
     for _ in range(args.warmup):
@@ -269,9 +434,20 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt / args.steps * 1e3
-    tokens = w.B * w.T
+    tokens = w.B * (1 if decode else w.T)
+    prec = "bf16" if w.dtype == I.BF16 else "fp32"
+    size = "124M" if w.C == 768 else "350M"
+    if decode:
+        metric = "decode tokens/s GPT-2 124M bf16, 32 sequences at position %d; HBM GB/s" % w.decode_pos
+        wl = "GPT-2 %s %s decode step, %d sequences, KV cache of %d positions (logits + softmax)" % (
+            size, prec, w.B, w.decode_pos)
+        data = "synthetic (seeded uniform tokens, N(0,0.02) weights, N(0,1) key/value cache)"
+    else:
+        metric = METRIC
+        wl = "GPT-2 %s %s forward B%d T%d (logits + softmax)" % (size, prec, w.B, w.T)
+        data = "synthetic (seeded uniform tokens, N(0,0.02) weights)"
     res = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(tokens * args.steps / dt, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -282,13 +458,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == I.BF16 else "f32",
-        "data": "synthetic (seeded uniform tokens, N(0,0.02) weights)",
-        "config": {"workload": "GPT-2 %s %s forward B%d T%d (logits + softmax)" % (
-            "124M" if w.C == 768 else "350M", "bf16" if w.dtype == I.BF16 else "fp32", w.B, w.T),
-            "B": w.B, "T": w.T, "L": w.L, "C": w.C, "NH": w.NH, "V": w.V, "Vp": w.Vp},
+        "data": data,
+        "config": {"workload": wl, "B": w.B, "T": w.T, "L": w.L, "C": w.C, "NH": w.NH, "V": w.V, "Vp": w.Vp},
     }
+    if decode:
+        res["config"]["pos"] = w.decode_pos
     if not args.no_kernel_timing:
-        recs = b.kernel_timing()
+        recs = b.decode_kernel_timing() if decode else b.kernel_timing()
         table, roof = summarize_kernels(recs, w.dtype == I.BF16)
         sites, _ = summarize_kernels(recs, w.dtype == I.BF16, key=5)
         res["roofline"] = roof
@@ -296,7 +472,8 @@ def main():
         res["sites"] = sites
         res["kernel_sum_ms"] = round(sum(r[4] for r in recs), 4)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(b, args.cpu_sample_tokens)
+        res["cpu_baseline"] = (cpu_baseline_decode(b, args.cpu_sample_seqs) if decode
+                               else cpu_baseline(b, args.cpu_sample_tokens))
     print(json.dumps(res), flush=True)
 
 

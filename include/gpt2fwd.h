@@ -153,6 +153,44 @@ int attention_decode_forward(void* out, const void* qkv_new, void* kcache, void*
                              int B, int pos, int maxT, int C, int NH, int dtype,
                              void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Decode-step building blocks. gpt2_decode_step on B <= 32 sequences runs
+ * each layer as: matmul_forward (qkv) -> attention_decode_forward ->
+ * matmul_splitk_forward (attproj) -> residual_layernorm_forward (ln2) ->
+ * matmul_gelu_forward (fc) -> matmul_splitk_forward (fcproj) ->
+ * residual_layernorm_forward (ln1 of the next layer, or lnf), i.e. the block
+ * of the forward with the residual adds and the GELU fused into neighbours.
+ *
+ * Split-k linear layer without bias, for N <= 32 rows:
+ *   part[s][n][o] = sum over c in k-range s of inp[n,c] * weight[o,c]
+ * with the C columns cut into `splits` consecutive ranges of whole 128-byte
+ * chunks (a range may be empty, giving zeros). part fp32 [splits,N,OC];
+ * inp [N,C]; weight [OC,C]. 1 <= splits <= 8, C % 8 == 0, OC % 8 == 0;
+ * N > 32 returns GPT2_ERR_UNSUPPORTED. */
+int matmul_splitk_forward(float* part, const void* inp, const void* weight, int N, int C, int OC,
+                          int splits, int dtype, void* stream);
+
+/* The split count gpt2_decode_step uses for a C -> OC projection (host
+ * call): enough workgroups to cover the chip, >= 2 chunks each; 1..8. */
+int matmul_splitk_count(int C, int OC, int dtype);
+
+/* Linear layer followed by GELU (tanh form), as fc + gelu of a block:
+ *   out[n,o] = gelu(sum_c inp[n,c] * weight[o,c] + bias[o])
+ * Shapes and rules as matmul_forward (bias nullable). For N <= 32 the GELU
+ * is applied to the fp32 accumulator before rounding (one launch); for
+ * larger N it runs on the stored product (matmul_forward, gelu_forward). */
+int matmul_gelu_forward(void* out, const void* inp, const void* weight, const void* bias,
+                        int N, int C, int OC, int dtype, void* stream);
+
+/* Residual add of a split-k projection, then LayerNorm:
+ *   x[n,:] <- x[n,:] + (bias + sum_{s<splits} part[s][n][:])   (in place;
+ *            the partial sums are added in split order, in fp32)
+ *   out[n,:] = LayerNorm(x[n,:]; gamma, beta, eps)      (of the stored x)
+ * x, out [N,C] (distinct); part fp32 [splits,N,C]; bias, gamma, beta [C].
+ * 1 <= splits <= 8; C as layernorm_forward. */
+int residual_layernorm_forward(void* out, void* x, const float* part, int splits,
+                               const void* bias, const void* gamma, const void* beta,
+                               int N, int C, float eps, int dtype, void* stream);
+
 /* Bytes of workspace gpt2_decode_step needs (host call); -1 if invalid. */
 int64_t gpt2_decode_workspace_bytes(const gpt2_config* cfg /* host */, int B);
 

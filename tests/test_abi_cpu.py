@@ -100,6 +100,18 @@ def test_validation_rejects_before_launch():
         == G.ERR_INVALID_ARGUMENT  # pos >= maxT
     assert lib.attention_decode_forward(p16, p16, p16, p16, 2, 5, 1024, 768, 12, 1, ws, 16, None) \
         == G.ERR_WORKSPACE_TOO_SMALL
+    q1, q2, q3 = ctypes.c_void_p(1 << 16), ctypes.c_void_p(1 << 18), ctypes.c_void_p(1 << 20)
+    assert lib.matmul_splitk_forward(q1, q2, q3, 4, 64, 64, 9, 0, None) == G.ERR_INVALID_ARGUMENT  # splits > 8
+    assert lib.matmul_splitk_forward(q1, q2, q3, 4, 64, 64, 0, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.matmul_splitk_forward(q1, q2, q3, 33, 64, 64, 2, 0, None) == G.ERR_UNSUPPORTED  # N > 32
+    assert lib.matmul_splitk_forward(q1, q2, q3, 4, 60, 64, 2, 0, None) == G.ERR_UNSUPPORTED  # C % 8
+    assert lib.matmul_gelu_forward(q1, q1, q3, None, 4, 64, 64, 0, None) == G.ERR_INVALID_ARGUMENT  # alias
+    assert lib.residual_layernorm_forward(q1, q2, q3, 9, p16, p16, p16, 4, 64, 1e-5, 0, None) \
+        == G.ERR_INVALID_ARGUMENT  # splits > 8
+    assert lib.residual_layernorm_forward(q1, q1, q3, 2, p16, p16, p16, 4, 64, 1e-5, 0, None) \
+        == G.ERR_INVALID_ARGUMENT  # out aliases x
+    assert lib.residual_layernorm_forward(q1, q2, q3, 2, odd, p16, p16, 4, 64, 1e-5, 0, None) \
+        == G.ERR_UNSUPPORTED  # misaligned bias
 
 
 def test_zero_sized_calls_are_noops():
@@ -111,6 +123,24 @@ def test_zero_sized_calls_are_noops():
     assert lib.softmax_forward(None, None, 0, 5, 8, 0, None) == G.OK
     assert lib.attention_forward(None, None, 0, 4, 64, 4, 0, None) == G.OK
     assert lib.layernorm_forward(None, None, None, None, None, None, 0, 64, 1e-5, 0, None) == G.OK
+    assert lib.matmul_splitk_forward(None, None, None, 0, 64, 64, 2, 0, None) == G.OK
+    assert lib.matmul_gelu_forward(None, None, None, None, 0, 64, 64, 1, None) == G.OK
+    assert lib.residual_layernorm_forward(None, None, None, 1, None, None, None, 0, 64, 1e-5, 0, None) == G.OK
+
+
+def test_splitk_count_rule():
+    """Decode projections: GPT-2 small attproj (768 -> 768) and fcproj
+    (3072 -> 768); enough workgroups for 256 CUs, >= 2 chunks per split."""
+    assert G.matmul_splitk_count(768, 768, 1) == 4
+    assert G.matmul_splitk_count(3072, 768, 1) == 8
+    assert G.matmul_splitk_count(768, 768, 0) == 8  # fp32: twice the chunks
+    assert G.matmul_splitk_count(64, 64, 0) == 1
+    assert G.matmul_splitk_count(768, 50304, 1) == 1
+    for C in (8, 64, 200, 768, 3072, 4096):
+        for OC in (8, 64, 768, 2304):
+            for dt in (0, 1):
+                s = G.matmul_splitk_count(C, OC, dt)
+                assert 1 <= s <= 8
 
 
 def test_model_validation():

@@ -251,3 +251,38 @@ def test_decode_matches_forward_tiny_fp32():
     wsd = torch.empty(G.decode_workspace_bytes(cfg, w.B), dtype=torch.uint8, device="cuda")
     G.gpt2_decode_step(dl, None, dev_int(tok[:, pos]), pos, dev(kc, I.F32), dev(vc, I.F32), pt, cfg, wsd)
     assert max_abs(host(dl), host(lf)[:, pos]) <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["tiny_affine", "tiny_bf16"])
+@pytest.mark.parametrize("B", [7, 32, 40])
+def test_decode_batch_sizes(name, B):
+    """Decode step against the oracle for batches that take the skinny path
+    (B <= 32: split-k projections with fused residual+LayerNorm and fc+GELU
+    epilogue) and the general path (B > 32), on a random prefilled cache."""
+    announce("decode-batch", name, B)
+    import torch
+    w = I.WORKLOADS[name]
+    params = I.make_params(w)
+    pos = 17
+    rng = np.random.default_rng(900 + B)
+    tok = rng.integers(0, w.V, size=B).astype(np.int32)
+    shape = (w.L, B, w.NH, w.maxT, w.hs)
+    kc = rng.standard_normal(shape, dtype=np.float32)
+    vc = rng.standard_normal(shape, dtype=np.float32)
+    kc[:, :, :, pos:] = 0.0
+    vc[:, :, :, pos:] = 0.0
+    if w.dtype == I.BF16:
+        kc, vc = I.round_to_bf16(kc), I.round_to_bf16(vc)
+    cfg = cfg_of(w)
+    tk, tv = dev(kc, w.dtype), dev(vc, w.dtype)
+    logits = empty((B, w.Vp), w.dtype, fill=float("nan"))
+    probs = empty((B, w.Vp), w.dtype, fill=float("nan"))
+    ws = torch.empty(G.decode_workspace_bytes(cfg, B), dtype=torch.uint8, device="cuda")
+    G.gpt2_decode_step(logits, probs, dev_int(tok), pos, tk, tv, dev(params, w.dtype), cfg, ws)
+    rl, rp = oracle.decode_step(tok, pos, kc.copy(), vc.copy(), params, w.L, w.C, w.NH, w.V, w.Vp, w.maxT,
+                                w.ln_eps)
+    check_logits(w, host(logits), rl)
+    if w.dtype == I.F32:
+        assert max_abs(host(probs), rp) <= 1e-6
+    else:
+        assert rel_err(host(probs), rp) <= 2e-2

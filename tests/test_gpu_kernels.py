@@ -120,6 +120,7 @@ def test_layernorm(dt, N, C):
 MM_SHAPES = [
     (64, 64, 192), (64, 256, 64), (65, 72, 200), (4097, 64, 40), (300, 768, 2304),
     (32, 768, 2304), (32, 3072, 768), (7, 768, 256), (1000, 1024, 4096),
+    (1, 8, 8), (17, 200, 40), (32, 136, 1000),
 ]
 
 
@@ -159,6 +160,103 @@ def test_matmul_random(dt, N, C, OC):
     G.matmul_forward(out, dev(a, d), dev(w, d), dev(b, d))
     ref = oracle.matmul(a, w, b)
     assert rel_err(host(out), ref) <= (1e-2 if d == I.BF16 else 1e-5)
+
+
+# ----------------------------------------------- decode building blocks
+SPLITK_CASES = [(32, 768, 768, 4), (32, 3072, 768, 8), (7, 136, 40, 3), (1, 8, 8, 2), (17, 200, 1000, 8),
+                (32, 64, 64, 1)]
+
+
+def splitk_ranges(C, es, splits):
+    """k-ranges of the split-k entry: whole 128-byte chunks, ceil(chunks/splits) per split."""
+    ck = 128 // es
+    nchunk = -(-C // ck)
+    cps = -(-nchunk // splits)
+    return [(min(y * cps * ck, C), min((y + 1) * cps * ck, C)) for y in range(splits)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,OC,splits", SPLITK_CASES)
+def test_matmul_splitk_integer_exact(dt, N, C, OC, splits):
+    """Small integers: each split's partial sum over its k-range is exact, so
+    part[y] equals the oracle's product of the matching column slices, bit
+    for bit (an empty range gives zeros)."""
+    announce("splitk-int", dt, N, C, OC, splits)
+    import torch
+    d = DT[dt]
+    a = I.random_int_tensor(30, (N, C), -3, 3)
+    w = I.random_int_tensor(31, (OC, C), -3, 3)
+    part = torch.full((splits, N, OC), float("nan"), dtype=torch.float32, device="cuda")
+    G.matmul_splitk_forward(part, dev(a, d), dev(w, d), splits)
+    got = part.cpu().numpy()
+    for y, (k0, k1) in enumerate(splitk_ranges(C, 2 if d == I.BF16 else 4, splits)):
+        ref = oracle.matmul(a[:, k0:k1], w[:, k0:k1], None) if k1 > k0 else np.zeros((N, OC), np.float32)
+        assert np.array_equal(got[y], ref), y
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,OC,splits", SPLITK_CASES)
+def test_matmul_splitk_random(dt, N, C, OC, splits):
+    announce("splitk-rand", dt, N, C, OC, splits)
+    import torch
+    d = DT[dt]
+    a = I.random_tensor(32, (N, C), 1.0, d)
+    w = I.random_tensor(33, (OC, C), 0.02, d)
+    part = torch.full((splits, N, OC), float("nan"), dtype=torch.float32, device="cuda")
+    G.matmul_splitk_forward(part, dev(a, d), dev(w, d), splits)
+    got = part.sum(0).cpu().numpy()
+    ref = oracle.matmul(a, w, None)
+    assert rel_err(got, ref) <= 1e-6  # fp32 partial sums of exact products
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,OC", [(32, 768, 3072), (7, 64, 256), (1, 8, 8), (40, 64, 256), (300, 768, 1000)])
+def test_matmul_gelu(dt, N, C, OC):
+    """fc + GELU: skinny epilogue (N <= 32) and the two-launch path (N > 32)."""
+    announce("matmul-gelu", dt, N, C, OC)
+    d = DT[dt]
+    a = I.random_tensor(34, (N, C), 1.0, d)
+    w = I.random_tensor(35, (OC, C), 0.05, d)
+    b = I.random_tensor(36, OC, 0.05, d)
+    out = empty((N, OC), d, fill=float("nan"))
+    G.matmul_gelu_forward(out, dev(a, d), dev(w, d), dev(b, d))
+    ref = oracle.gelu(oracle.matmul(a, w, b))
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    assert rel_err(got, ref) <= (1e-2 if d == I.BF16 else 1e-5)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,splits", [(32, 768, 4), (32, 768, 8), (7, 64, 1), (1, 1024, 3), (32, 4096, 2)])
+def test_residual_layernorm(dt, N, C, splits):
+    """x += bias + sum of split partials, then LayerNorm of the stored x; the
+    oracle's residual and LayerNorm give the reference."""
+    announce("residual-ln", dt, N, C, splits)
+    import torch
+    d = DT[dt]
+    x = I.random_tensor(40, (N, C), 1.0, d)
+    p = I.random_tensor(41, (splits, N, C), 0.5, I.F32)
+    bias = I.random_tensor(42, C, 0.1, d)
+    g = I.random_tensor(43, C, 0.1, d) + np.float32(1.0)
+    g = bf16_round(g) if d == I.BF16 else g
+    beta = I.random_tensor(44, C, 0.1, d)
+    tx = dev(x, d)
+    out = empty((N, C), d, fill=float("nan"))
+    G.residual_layernorm_forward(out, tx, torch.from_numpy(p).cuda(), dev(bias, d), dev(g, d), dev(beta, d),
+                                 1e-5)
+    # the entry's definition: fp32 additions in split order, then the residual
+    delta = np.broadcast_to(bias.astype(np.float32), (N, C)).copy()
+    for sp in range(splits):
+        delta = delta + p[sp]
+    xref = oracle.residual(x, delta)
+    xgot = host(tx)
+    assert np.array_equal(xgot, bf16_round(xref) if d == I.BF16 else xref)
+    ref = oracle.layernorm(xgot, g, beta, 1e-5)  # of the stored x
+    got = host(out)
+    if d == I.BF16:
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-3)
+    else:
+        assert max_abs(got, ref) <= 1e-5
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])

@@ -33,6 +33,7 @@ EXPORTS = (
     "gpt2_workspace_bytes", "gpt2_forward", "attention_decode_workspace_bytes",
     "attention_decode_forward", "gpt2_decode_workspace_bytes", "gpt2_decode_step",
     "gpt2_status_string", "gpt2_last_hip_error", "matmul_kernel_config",
+    "matmul_splitk_forward", "matmul_splitk_count", "matmul_gelu_forward", "residual_layernorm_forward",
 )
 
 
@@ -85,6 +86,10 @@ def load_library(path: str = LIB_PATH):
             "gpt2_status_string": (ctypes.c_char_p, [I]),
             "gpt2_last_hip_error": (I, []),
             "matmul_kernel_config": (ctypes.c_char_p, [I, I, I, I]),
+            "matmul_splitk_forward": (I, [P, P, P, I, I, I, I, I, P]),
+            "matmul_splitk_count": (I, [I, I, I]),
+            "matmul_gelu_forward": (I, [P, P, P, P, I, I, I, I, P]),
+            "residual_layernorm_forward": (I, [P, P, P, I, P, P, P, I, I, F, I, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -172,6 +177,47 @@ def matmul_forward(out, inp, weight, bias=None, stream=None):
 def matmul_kernel_config(N, C, OC, dtype) -> str:
     """Name of the GEMM kernel configuration matmul_forward uses for this shape."""
     return load_library().matmul_kernel_config(N, C, OC, dtype).decode()
+
+
+def matmul_splitk_forward(part, inp, weight, splits, stream=None):
+    """part fp32 [splits,N,OC]: k-range partial sums of inp [N,C] @ weight[OC,C]^T (N <= 32)."""
+    lib = load_library()
+    C = inp.shape[-1]
+    N = inp.numel() // C if C else 0
+    OC = weight.shape[0]
+    _check("matmul_splitk_forward", lib.matmul_splitk_forward(
+        _dev(part, "part"), _dev(inp, "inp"), _dev(weight, "weight"), N, C, OC, int(splits),
+        _dtype_code(inp), _stream(stream)))
+    return part
+
+
+def matmul_splitk_count(C, OC, dtype) -> int:
+    """Split count the decode step uses for a C -> OC projection."""
+    return int(load_library().matmul_splitk_count(C, OC, dtype))
+
+
+def matmul_gelu_forward(out, inp, weight, bias=None, stream=None):
+    """out [N,OC] = gelu(inp [N,C] @ weight[OC,C]^T + bias)."""
+    lib = load_library()
+    C = inp.shape[-1]
+    N = inp.numel() // C if C else 0
+    OC = weight.shape[0]
+    _check("matmul_gelu_forward", lib.matmul_gelu_forward(
+        _dev(out, "out"), _dev(inp, "inp"), _dev(weight, "weight"), _dev(bias, "bias"),
+        N, C, OC, _dtype_code(inp), _stream(stream)))
+    return out
+
+
+def residual_layernorm_forward(out, x, part, bias, gamma, beta, eps=1e-5, stream=None):
+    """x [N,C] += bias + sum_s part[s] (in place); out = LayerNorm(x)."""
+    lib = load_library()
+    C = x.shape[-1]
+    N = x.numel() // C if C else 0
+    splits = part.shape[0]
+    _check("residual_layernorm_forward", lib.residual_layernorm_forward(
+        _dev(out, "out"), _dev(x, "x"), _dev(part, "part"), splits, _dev(bias, "bias"), _dev(gamma, "gamma"),
+        _dev(beta, "beta"), N, C, float(eps), _dtype_code(x), _stream(stream)))
+    return out
 
 
 def attention_forward(out, qkv, NH, stream=None):

@@ -58,10 +58,25 @@ __device__ __forceinline__ void store_vec(bf16* p, const float (&v)[8]) {
     *reinterpret_cast<uint4*>(p) = x;
 }
 
+// The value a store of v into T's storage keeps (identity for fp32).
+__device__ __forceinline__ float storage_round(const float*, float v) { return v; }
+__device__ __forceinline__ float storage_round(const bf16*, float v) { return bf16_to_f32(f32_to_bf16(v)); }
+
 __device__ __forceinline__ float load_scalar(const float* p) { return *p; }
 __device__ __forceinline__ float load_scalar(const bf16* p) { return bf16_to_f32(p->bits); }
 __device__ __forceinline__ void store_scalar(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_scalar(bf16* p, float v) { p->bits = (uint16_t)f32_to_bf16(v); }
+
+// GELU, tanh form: x/2 (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+// Evaluated through the identity 1 + tanh(u) = 2 / (1 + e^{-2u}), so
+// g(x) = x / (1 + e^{-2u}): no cancellation for u << 0, and e^{-2u} = inf
+// gives the correct limit -0.
+// (ECE408 Milestone 1, kernel table: GELU.)
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float k2 = -2.0f * 0.7978845608028654f;  // -2 sqrt(2/pi)
+    float u = x * (1.0f + 0.044715f * x * x);
+    return x / (1.0f + expf(k2 * u));
+}
 
 // Reductions across the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_sum(float x) {
@@ -80,6 +95,8 @@ __device__ __forceinline__ float wave_max(float x) {
 // ------------------------------------------------------------------ host side
 namespace gpt2 {
 void set_last_hip_error(int e);
+// Epilogues of the skinny (decode) GEMM: bias, or bias then GELU.
+enum SkinnyEpilogue { SKINNY_BIAS = 0, SKINNY_BIAS_GELU = 1 };
 // Status after a launch: GPT2_OK, or GPT2_ERR_HIP with the code recorded.
 int launch_status();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -61,17 +61,6 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(T* out, const T* a, 
         store_scalar(out + i, load_scalar(a + i) + load_scalar(b + i));
 }
 
-// GELU, tanh form: x/2 (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
-// Evaluated through the identity 1 + tanh(u) = 2 / (1 + e^{-2u}), so
-// g(x) = x / (1 + e^{-2u}): no cancellation for u << 0, and e^{-2u} = inf
-// gives the correct limit -0.
-// (ECE408 Milestone 1, kernel table: GELU.)
-__device__ __forceinline__ float gelu_tanh(float x) {
-    const float k2 = -2.0f * 0.7978845608028654f;  // -2 sqrt(2/pi)
-    float u = x * (1.0f + 0.044715f * x * x);
-    return x / (1.0f + expf(k2 * u));
-}
-
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gelu_kernel(T* out, const T* inp, int64_t n) {
     constexpr int V = Vec<T>::N;

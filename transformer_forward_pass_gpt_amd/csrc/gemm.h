@@ -451,4 +451,160 @@ static void launch_gemm_cfg(T* out, const T* A, const T* W, const T* bias, int M
                                                                           group_m, remap);
 }
 
+// 16x16 MFMA step: bf16 16x16x32 (one 16-byte piece per lane) or fp32
+// 16x16x4 (one float of the piece per step). Lane l supplies row l%16 of its
+// operand at k-group l/16; accumulator element i of lane l is row 4*(l/16)+i,
+// column l%16.
+template <typename T> struct Mfma16;
+template <> struct Mfma16<float> {
+    static constexpr int STEPS = 4;
+    static __device__ __forceinline__ void step(f32x4& acc, const u32x4& a, const u32x4& b, int e) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc, 0, 0, 0);
+    }
+};
+template <> struct Mfma16<bf16> {
+    static constexpr int STEPS = 1;
+    static __device__ __forceinline__ void step(f32x4& acc, const u32x4& a, const u32x4& b, int) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                      acc, 0, 0, 0);
+    }
+};
+
+// Skinny GEMM for M <= 32 rows (a decode step: one row per sequence). Its
+// cost is one pass over W plus fixed latency. Every operand byte arrives
+// through direct-to-LDS copies in which eight consecutive lanes fetch one
+// 128-byte line of a row (each copy instruction moves eight whole lines);
+// each lane then reads its 16x16 MFMA pieces from LDS. Rows are stored with
+// their 16-byte slots permuted by (row/2) mod 8, so the sixteen rows one
+// fragment read touches fall in distinct bank groups. Piece (s, g) of a
+// 128-byte chunk is slot 4s + g for both operands: one k map, so the
+// contraction is unchanged. Rows past M or N read row 0 (their results are
+// never stored); k past K reads a clamped address and is zeroed at use.
+//
+// Grid (column tiles of 32, splits): workgroup (x, y) reduces k-chunks
+// [y*cps, (y+1)*cps) with cps = ceil(chunks/splits); within it each of the NW
+// wavefronts takes a contiguous run, PF chunks per batch, in its own LDS
+// stages (PF x 8 KiB per wave); the NW partial tiles are summed through LDS
+// in wave order. With part == nullptr (then splits == 1) it writes
+// out = EPI(bias + sum); otherwise it writes the fp32 partial sums
+// part[y][M][N] (no bias), which the consumer adds in split order.
+template <typename T, int NW, int PF, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_lds_kernel(T* __restrict__ out, float* __restrict__ part,
+                                                                  const T* __restrict__ A,
+                                                                  const T* __restrict__ W,
+                                                                  const T* __restrict__ bias, int M, int N,
+                                                                  int K) {
+    constexpr int VE = Vec<T>::N;
+    constexpr int CK = 128 / (int)sizeof(T);  // k per chunk: one 128-byte line per row
+    constexpr int TILE = 32 * 128;            // bytes of one 32-row chunk tile
+    static_assert(NW * PF * 2 * TILE <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) char smem[NW * PF * 2 * TILE];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int n0 = blockIdx.x * 32;
+    const int splits = gridDim.y;
+    const int nchunk = (K + CK - 1) / CK;
+    const int cps = (nchunk + splits - 1) / splits;
+    const int kb = min((int)blockIdx.y * cps, nchunk), ke = min(kb + cps, nchunk);
+    const int per = (ke - kb + NW - 1) / NW;
+    const int c_begin = min(kb + w * per, ke), c_end = min(c_begin + per, ke);
+
+    // Copy q (0..3) of a tile: lane i fetches slot (i%8) ^ ((row/2)%8) of row
+    // 8q + i/8 into LDS byte 1024q + 16i.
+    const T* srcA[4];
+    const T* srcW[4];
+    int gsl[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int row = 8 * q + (lane >> 3);
+        gsl[q] = ((lane & 7) ^ ((row >> 1) & 7)) * VE;
+        srcA[q] = A + (int64_t)(row < M ? row : 0) * K;
+        srcW[q] = W + (int64_t)(n0 + row < N ? n0 + row : 0) * K;
+    }
+    float bcol[2] = {0.f, 0.f};
+    if (bias && !part) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int col = n0 + 16 * j + (lane & 15);
+            const float bv = load_scalar(bias + min(col, N - 1));  // unconditional: no wait here
+            bcol[j] = col < N ? bv : 0.f;
+        }
+    }
+    char* wbase = smem + w * (PF * 2 * TILE);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = c_begin; c0 < c_end; c0 += PF) {
+        wait_vmcnt_lds<0>();  // the previous batch's fragment reads are complete
+#pragma unroll
+        for (int p = 0; p < PF; p++) {
+            const int c = min(c0 + p, c_end - 1);
+            char* st = wbase + p * 2 * TILE;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int off = min(c * CK + gsl[q], K - VE);  // K % 8 == 0: slots are whole
+                copy16_to_lds(srcA[q] + off, (lds_void_ptr)(st + q * 1024));
+                copy16_to_lds(srcW[q] + off, (lds_void_ptr)(st + TILE + q * 1024));
+            }
+        }
+        wait_vmcnt_lds<0>();
+#pragma unroll
+        for (int p = 0; p < PF; p++) {
+            const char* st = wbase + p * 2 * TILE;
+#pragma unroll
+            for (int sh = 0; sh < 2; sh++) {
+                const int slot = sh * 4 + g;
+                const bool ok = c0 + p < c_end && (c0 + p) * CK + slot * VE < K;
+                u32x4 a[2], b[2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    const int row = 16 * i + r16;
+                    const int sw = (slot ^ ((row >> 1) & 7)) * 16;
+                    a[i] = *reinterpret_cast<const u32x4*>(st + row * 128 + sw);
+                    b[i] = *reinterpret_cast<const u32x4*>(st + TILE + row * 128 + sw);
+                    a[i] = ok ? a[i] : zero;
+                    b[i] = ok ? b[i] : zero;
+                }
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int j = 0; j < 2; j++)
+#pragma unroll
+                        for (int e = 0; e < Mfma16<T>::STEPS; e++) Mfma16<T>::step(acc[i][j], a[i], b[j], e);
+            }
+        }
+    }
+    __syncthreads();  // the reduction buffer reuses the stages
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) red[(w * 16 + (i * 2 + j) * 4 + v) * 64 + lane] = acc[i][j][v];
+    __syncthreads();
+    // Entry (i, j, v) of lane l is row 16i + 4*(l/16) + v, column 16j + l%16.
+#pragma unroll
+    for (int idx = tid; idx < 16 * 64; idx += NW * 64) {
+        const int q = idx / 64;
+        const int i = q >> 3, j = (q >> 2) & 1, v = q & 3;
+        const int row = 16 * i + 4 * (lane >> 4) + v, col = n0 + 16 * j + (lane & 15);
+        if (row < M && col < N) {
+            float x = 0.f;
+            for (int ww = 0; ww < NW; ww++) x += red[(ww * 16 + q) * 64 + lane];
+            if (part) {
+                part[((int64_t)blockIdx.y * M + row) * N + col] = x;
+            } else {
+                x += bcol[j];
+                if (EPI == SKINNY_BIAS_GELU) x = gelu_tanh(x);
+                store_scalar(out + (int64_t)row * N + col, x);
+            }
+        }
+    }
+}
+
 }  // namespace gpt2

@@ -6,22 +6,36 @@
 
 namespace gpt2 {
 
+static constexpr int kMaxSplits = 8;  // split-k ranges of the decode projections
+
+// Skinny (M <= 32) problems: the LDS-staged kernel, 8 wavefronts, one chunk
+// per load batch (the fastest variant on every decode shape swept on MI355X).
+template <typename T>
+static void launch_skinny(T* out, float* part, const T* A, const T* W, const T* bias, int M, int N, int K,
+                          int splits, int epi, hipStream_t s) {
+    const dim3 grid((N + 31) / 32, splits);
+    if (epi == SKINNY_BIAS_GELU)
+        gemm_skinny_lds_kernel<T, 8, 1, SKINNY_BIAS_GELU><<<grid, 512, 0, s>>>(out, part, A, W, bias, M, N, K);
+    else
+        gemm_skinny_lds_kernel<T, 8, 1, SKINNY_BIAS><<<grid, 512, 0, s>>>(out, part, A, W, bias, M, N, K);
+}
+
 // Tile shapes, chosen per problem from on-box sweeps (MI355X) over the GPT-2
 // small and medium layer shapes. The pipelined kernel (S LDS stages filled by
 // load-to-LDS copies, k-tile rows of RB bytes) runs whenever K is a whole
-// number of k-tiles; otherwise, and for the 32-row decode problems, the
-// register-staged kernel with a masked k tail.
+// number of k-tiles; otherwise the register-staged kernel with a masked k
+// tail. Problems of at most 32 rows (decode) stream W with the skinny kernel.
 struct PipeCfg {
     const char* name;
     int bk_bytes;  // RB: bytes of k per tile row
 };
 enum GemmCfg {
-    R32x64 = 0, R64x64, R64x128, R128x96,
+    S32 = 0, R64x64, R64x128, R128x96,
     P64x64, P128x96_S4, P128x96_S5, P128x128, P128x192, P256x128_S3A, P256x128_S3B, P256x256,
     G_NCFG
 };
 static const PipeCfg kCfg[G_NCFG] = {
-    {"32x64_r", 0},         {"64x64_r", 0},          {"64x128_r", 0},      {"128x96_r", 0},
+    {"skinny32", 0},        {"64x64_r", 0},          {"64x128_r", 0},      {"128x96_r", 0},
     {"64x64_p6", 64},       {"128x96_p4", 128},      {"128x96_p5", 128},   {"128x128_p6", 64},
     {"128x192_p5", 64},     {"256x128_p3", 128},     {"256x128_p3s", 128}, {"256x256_p4", 64},
 };
@@ -49,7 +63,7 @@ static GemmCfg choose_cfg(int M, int N, int K, int dtype) {
         if (tiles(128, 96) >= 1024) return R128x96;
         return tiles(64, 128) >= 256 ? R64x128 : R64x64;
     }
-    return R32x64;
+    return S32;
 }
 
 template <typename T>
@@ -57,7 +71,7 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, int M, 
                           int dtype, hipStream_t s) {
     constexpr int BK = Vec<T>::N * 8;  // 128 bytes of k per row per LDS tile
     switch (choose_cfg(M, N, K, dtype)) {
-        case R32x64: launch_gemm_cfg<T, 1, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 1, 0, s); break;
+        case S32: launch_skinny<T>(out, nullptr, A, W, bias, M, N, K, 1, SKINNY_BIAS, s); break;
         case R64x64: launch_gemm_cfg<T, 2, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 4, 1, s); break;
         case R64x128: launch_gemm_cfg<T, 2, 2, 1, 2, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
         case R128x96: launch_gemm_cfg<T, 4, 1, 1, 3, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
@@ -92,18 +106,81 @@ int launch_matmul(void* out, const void* inp, const void* weight, const void* bi
     return launch_status();
 }
 
+// Decode-step GEMM on at most 32 rows (K % 8 == 0). part == nullptr:
+// out = epi(inp W^T + bias) in one split; otherwise fp32 partial sums over
+// `splits` k-ranges into part[splits][M][N], bias and epilogue left to the
+// consumer (out must then be nullptr).
+int launch_skinny_gemm(void* out, float* part, const void* inp, const void* weight, const void* bias, int M,
+                       int K, int N, int splits, int epi, int dtype, hipStream_t s) {
+    // exactly one destination: out (one split) or the partial-sum buffer
+    if (M < 1 || M > 32 || K % 8 || splits < 1 || (part ? out != nullptr : (out == nullptr || splits != 1)))
+        return GPT2_ERR_INVALID_ARGUMENT;
+    if (dtype == GPT2_BF16)
+        launch_skinny<bf16>((bf16*)out, part, (const bf16*)inp, (const bf16*)weight, (const bf16*)bias, M, N, K,
+                            splits, epi, s);
+    else
+        launch_skinny<float>((float*)out, part, (const float*)inp, (const float*)weight, (const float*)bias, M,
+                             N, K, splits, epi, s);
+    return launch_status();
+}
+
+// Splits for a decode-step projection of K-deep rows onto N columns: enough
+// workgroups to cover the chip (256 CUs), each keeping >= 2 k-chunks of 128
+// bytes; at most kMaxSplits.
+int skinny_split_count(int K, int N, int es) {
+    const int tiles = (N + 31) / 32;
+    const int chunks = (K * es + 127) / 128;
+    int s = 1;
+    while (s < kMaxSplits && tiles * s * 2 <= 256 && chunks >= 4 * s) s *= 2;
+    return s;
+}
+
+int launch_gelu(void*, const void*, int64_t, int, hipStream_t);
+
 }  // namespace gpt2
 
 using namespace gpt2;
 
-extern "C" int matmul_forward(void* out, const void* inp, const void* weight, const void* bias,
-                              int N, int C, int OC, int dtype, void* stream) {
+static int check_linear(const void* out, const void* inp, const void* weight, int N, int C, int OC, int dtype) {
     if (!valid_dtype(dtype) || N < 0 || C < 0 || OC < 0) return GPT2_ERR_INVALID_ARGUMENT;
     if ((int64_t)N * OC == 0) return GPT2_OK;
     if (!out || !inp || !weight || C == 0) return GPT2_ERR_INVALID_ARGUMENT;
     if (C % 8 || OC % 8 || !aligned16(out) || !aligned16(inp) || !aligned16(weight))
         return GPT2_ERR_UNSUPPORTED;
     if (out == inp || out == weight) return GPT2_ERR_INVALID_ARGUMENT;
+    return 1;  // valid, non-empty
+}
+
+extern "C" int matmul_splitk_forward(float* part, const void* inp, const void* weight, int N, int C, int OC,
+                                     int splits, int dtype, void* stream) {
+    if (splits < 1 || splits > kMaxSplits) return GPT2_ERR_INVALID_ARGUMENT;
+    const int rc = check_linear(part, inp, weight, N, C, OC, dtype);
+    if (rc <= 0) return rc;
+    if (N > 32) return GPT2_ERR_UNSUPPORTED;
+    return launch_skinny_gemm(nullptr, part, inp, weight, nullptr, N, C, OC, splits, SKINNY_BIAS, dtype,
+                              (hipStream_t)stream);
+}
+
+extern "C" int matmul_splitk_count(int C, int OC, int dtype) {
+    if (!valid_dtype(dtype) || C <= 0 || OC <= 0) return GPT2_ERR_INVALID_ARGUMENT;
+    return skinny_split_count(C, OC, elem_size(dtype));
+}
+
+extern "C" int matmul_gelu_forward(void* out, const void* inp, const void* weight, const void* bias, int N,
+                                   int C, int OC, int dtype, void* stream) {
+    const int rc = check_linear(out, inp, weight, N, C, OC, dtype);
+    if (rc <= 0) return rc;
+    const hipStream_t s = (hipStream_t)stream;
+    if (N <= 32)
+        return launch_skinny_gemm(out, nullptr, inp, weight, bias, N, C, OC, 1, SKINNY_BIAS_GELU, dtype, s);
+    const int r = launch_matmul(out, inp, weight, bias, N, C, OC, dtype, s);
+    return r != GPT2_OK ? r : launch_gelu(out, out, (int64_t)N * OC, dtype, s);
+}
+
+extern "C" int matmul_forward(void* out, const void* inp, const void* weight, const void* bias,
+                              int N, int C, int OC, int dtype, void* stream) {
+    const int rc = check_linear(out, inp, weight, N, C, OC, dtype);
+    if (rc <= 0) return rc;
     return launch_matmul(out, inp, weight, bias, N, C, OC, dtype, (hipStream_t)stream);
 }
 

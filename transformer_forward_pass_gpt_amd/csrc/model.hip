@@ -35,6 +35,24 @@ int launch_attention_decode(void*, const void*, void*, void*, int, int, int, int
                             hipStream_t);
 int64_t decode_workspace_bytes(int B, int C, int NH, int maxT);
 bool attention_head_size_ok(int hs);
+int launch_skinny_gemm(void*, float*, const void*, const void*, const void*, int, int, int, int, int, int,
+                       hipStream_t);
+int launch_residual_layernorm(void*, void*, const float*, int, const void*, const void*, const void*, int, int,
+                              float, int, hipStream_t);
+
+int skinny_split_count(int K, int N, int es);
+
+// Decode steps on at most kSkinnyRows sequences run the projections as skinny
+// GEMMs; attproj and fcproj split k over up to kMaxSplits workgroups per
+// column tile and leave fp32 partial sums for the fused residual+LayerNorm.
+static constexpr int kSkinnyRows = 32;
+static constexpr int kMaxSplits = 8;
+
+static int64_t decode_part_bytes(int B, int C, int NH, int maxT) {
+    const int64_t att = decode_workspace_bytes(B, C, NH, maxT);
+    const int64_t split = B <= kSkinnyRows ? (int64_t)kMaxSplits * B * C * 4 : 0;
+    return att > split ? att : split;
+}
 
 // Element offsets into the flat parameter buffer.
 struct ParamOffsets {
@@ -182,8 +200,7 @@ extern "C" int gpt2_forward(void* logits, void* probs, const int32_t* tokens, co
 
 extern "C" int64_t gpt2_decode_workspace_bytes(const gpt2_config* cfg, int B) {
     if (!config_ok(cfg) || B < 0) return -1;
-    return carve(nullptr, B, cfg->C, elem_size(cfg->dtype),
-                 decode_workspace_bytes(B, cfg->C, cfg->NH, cfg->maxT))
+    return carve(nullptr, B, cfg->C, elem_size(cfg->dtype), decode_part_bytes(B, cfg->C, cfg->NH, cfg->maxT))
         .bytes;
 }
 
@@ -201,7 +218,7 @@ extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens
         return GPT2_ERR_UNSUPPORTED;
     if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
     const int C = cfg->C, L = cfg->L, NH = cfg->NH, dt = cfg->dtype, es = elem_size(dt);
-    Workspace w = carve((char*)workspace, B, C, es, decode_workspace_bytes(B, C, NH, cfg->maxT));
+    Workspace w = carve((char*)workspace, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT));
     if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     const ParamOffsets po = param_offsets(*cfg);
     const char* P = (const char*)params;
@@ -211,6 +228,37 @@ extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens
     const int64_t layer_elems = (int64_t)B * NH * cfg->maxT * (C / NH);
 
     CHECK(launch_encoder(w.x, tokens, at(po.wte), at(po.wpe + (int64_t)pos * C64), B, 1, C, dt, s));
+    if (B <= kSkinnyRows && C % 8 == 0) {
+        // Skinny path: per layer qkv, attention (2 launches), attproj, residual+ln2,
+        // fc+GELU, fcproj, residual+ln1 of the next layer (or lnf).
+        const int s_ap = skinny_split_count(C, C, es), s_fp = skinny_split_count(4 * C, C, es);
+        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln1_g), at(po.ln1_b), B, C, cfg->ln_eps,
+                               dt, s));
+        for (int l = 0; l < L; l++) {
+            CHECK(launch_skinny_gemm(w.qkv, nullptr, w.ln, at(po.qkv_w + l * 3 * C64 * C64),
+                                     at(po.qkv_b + l * 3 * C64), B, C, 3 * C, 1, SKINNY_BIAS, dt, s));
+            CHECK(launch_attention_decode(w.att, w.qkv, (char*)kcache + l * layer_elems * es,
+                                          (char*)vcache + l * layer_elems * es, B, pos, cfg->maxT, C, NH,
+                                          dt, w.part, s));
+            CHECK(launch_skinny_gemm(nullptr, w.part, w.att, at(po.ap_w + l * C64 * C64), nullptr, B, C, C,
+                                     s_ap, SKINNY_BIAS, dt, s));
+            CHECK(launch_residual_layernorm(w.ln, w.x, w.part, s_ap, at(po.ap_b + l * C64),
+                                            at(po.ln2_g + l * C64), at(po.ln2_b + l * C64), B, C,
+                                            cfg->ln_eps, dt, s));
+            CHECK(launch_skinny_gemm(w.fc, nullptr, w.ln, at(po.fc_w + l * 4 * C64 * C64),
+                                     at(po.fc_b + l * 4 * C64), B, C, 4 * C, 1, SKINNY_BIAS_GELU, dt, s));
+            CHECK(launch_skinny_gemm(nullptr, w.part, w.fc, at(po.fp_w + l * 4 * C64 * C64), nullptr, B,
+                                     4 * C, C, s_fp, SKINNY_BIAS, dt, s));
+            const bool last = l == L - 1;
+            CHECK(launch_residual_layernorm(w.ln, w.x, w.part, s_fp, at(po.fp_b + l * C64),
+                                            at(last ? po.lnf_g : po.ln1_g + (l + 1) * C64),
+                                            at(last ? po.lnf_b : po.ln1_b + (l + 1) * C64), B, C,
+                                            cfg->ln_eps, dt, s));
+        }
+        CHECK(launch_matmul(logits, w.ln, at(po.wte), nullptr, B, C, cfg->Vp, dt, s));
+        if (probs) CHECK(launch_softmax(probs, logits, B, cfg->V, cfg->Vp, dt, s));
+        return GPT2_OK;
+    }
     for (int l = 0; l < L; l++) {
         CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln1_g + l * C64),
                                at(po.ln1_b + l * C64), B, C, cfg->ln_eps, dt, s));

@@ -15,32 +15,75 @@ namespace gpt2 {
 // (ECE408 Final Project - GPT-2, Milestone 1, kernel table: LayerNorm;
 // llm.c "State of the Union [April 22, 2024]", kernel summaries:
 // layernorm_forward_kernel3.)
-template <typename T, int VPL>
+//
+// RES (decode step): the row is first updated in place as
+// x <- x + (bias + sum_s part[s]), the split-k partial sums of the preceding
+// projection added in split order; LayerNorm then runs on the stored
+// (rounded) row, as it would after a separate residual add.
+static constexpr int kMaxResSplits = 8;
+
+template <typename T, int VPL, bool RES>
 __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, float* __restrict__ mean,
-                                                        float* __restrict__ rstd,
-                                                        const T* __restrict__ inp,
+                                                        float* __restrict__ rstd, T* __restrict__ inp,
                                                         const T* __restrict__ gamma,
                                                         const T* __restrict__ beta, int N, int C,
-                                                        float eps) {
+                                                        float eps, const float* __restrict__ part,
+                                                        int splits, const T* __restrict__ bias) {
     constexpr int V = Vec<T>::N;
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (row >= N) return;  // wave-uniform
-    const T* x = inp + (int64_t)row * C;
+    T* x = inp + (int64_t)row * C;
     const int cv = C / V;
     float v[VPL][V];
     float s = 0.f;
+    // Loads are unconditional (vector index clamped to the row), so every
+    // load of the row is in flight before the first use.
+#pragma unroll
+    for (int i = 0; i < VPL; i++) load_vec(x + min(lane + i * 64, cv - 1) * V, v[i]);
+    if constexpr (RES) {
+        // x <- x + (bias + partials in split order); unused splits read a
+        // clamped split and are selected to zero
+        float4 q[VPL][kMaxResSplits][V / 4];
+        float d[VPL][V];
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+            const int idx = min(lane + i * 64, cv - 1);
+            load_vec(bias + idx * V, d[i]);
+#pragma unroll
+            for (int sp = 0; sp < kMaxResSplits; sp++) {
+                const float* p = part + ((int64_t)min(sp, splits - 1) * N + row) * C + idx * V;
+#pragma unroll
+                for (int j = 0; j < V / 4; j++) q[i][sp][j] = *reinterpret_cast<const float4*>(p + 4 * j);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+#pragma unroll
+            for (int sp = 0; sp < kMaxResSplits; sp++) {
+                const bool on = sp < splits;
+#pragma unroll
+                for (int j = 0; j < V / 4; j++) {
+                    d[i][4 * j] += on ? q[i][sp][j].x : 0.f;
+                    d[i][4 * j + 1] += on ? q[i][sp][j].y : 0.f;
+                    d[i][4 * j + 2] += on ? q[i][sp][j].z : 0.f;
+                    d[i][4 * j + 3] += on ? q[i][sp][j].w : 0.f;
+                }
+            }
+            // LayerNorm continues from the stored (rounded) row
+#pragma unroll
+            for (int j = 0; j < V; j++) v[i][j] = storage_round(x, v[i][j] + d[i][j]);
+            if (lane + i * 64 < cv) store_vec(x + (lane + i * 64) * V, v[i]);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
-        int idx = lane + i * 64;
-        if (idx < cv) {
-            load_vec(x + idx * V, v[i]);
-#pragma unroll
-            for (int j = 0; j < V; j++) s += v[i][j];
-        } else {
+        if (lane + i * 64 >= cv) {
 #pragma unroll
             for (int j = 0; j < V; j++) v[i][j] = 0.f;
         }
+#pragma unroll
+        for (int j = 0; j < V; j++) s += v[i][j];
     }
     s = wave_sum(s);
     const float mu = s / (float)C;
@@ -76,33 +119,47 @@ __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, flo
     }
 }
 
-template <typename T>
-static void launch_ln_t(T* out, float* mean, float* rstd, const T* inp, const T* g, const T* b,
-                        int N, int C, float eps, hipStream_t s) {
+template <typename T, bool RES>
+static void launch_ln_t(T* out, float* mean, float* rstd, T* inp, const T* g, const T* b, int N, int C,
+                        float eps, const float* part, int splits, const T* bias, hipStream_t s) {
     const int vpl = (C / Vec<T>::N + 63) / 64;
-    dim3 grid((N + 3) / 4), block(256);
-    if (vpl <= 1)
-        layernorm_kernel<T, 1><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
-    else if (vpl <= 2)
-        layernorm_kernel<T, 2><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
-    else if (vpl <= 3)
-        layernorm_kernel<T, 3><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
-    else if (vpl <= 4)
-        layernorm_kernel<T, 4><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
-    else if (vpl <= 8)
-        layernorm_kernel<T, 8><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
-    else
-        layernorm_kernel<T, 16><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps);
+    // RES runs on decode-sized batches: one row per workgroup spreads them over CUs
+    const int rows = RES ? 1 : 4;
+    const dim3 grid((N + rows - 1) / rows), block(64 * rows);
+#define LN_LAUNCH(P) \
+    layernorm_kernel<T, P, RES><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps, part, splits, bias)
+    if (vpl <= 1) LN_LAUNCH(1);
+    else if (vpl <= 2) LN_LAUNCH(2);
+    else if (vpl <= 3) LN_LAUNCH(3);
+    else if (vpl <= 4) LN_LAUNCH(4);
+    else if (vpl <= 8) LN_LAUNCH(8);
+    else LN_LAUNCH(16);
+#undef LN_LAUNCH
 }
 
 int launch_layernorm(void* out, float* mean, float* rstd, const void* inp, const void* gamma,
                      const void* beta, int N, int C, float eps, int dtype, hipStream_t s) {
+    // the input is only read on this path
     if (dtype == GPT2_BF16)
-        launch_ln_t<bf16>((bf16*)out, mean, rstd, (const bf16*)inp, (const bf16*)gamma,
-                          (const bf16*)beta, N, C, eps, s);
+        launch_ln_t<bf16, false>((bf16*)out, mean, rstd, (bf16*)inp, (const bf16*)gamma, (const bf16*)beta, N,
+                                 C, eps, nullptr, 0, nullptr, s);
     else
-        launch_ln_t<float>((float*)out, mean, rstd, (const float*)inp, (const float*)gamma,
-                           (const float*)beta, N, C, eps, s);
+        launch_ln_t<float, false>((float*)out, mean, rstd, (float*)inp, (const float*)gamma,
+                                  (const float*)beta, N, C, eps, nullptr, 0, nullptr, s);
+    return launch_status();
+}
+
+// x <- x + bias + sum_s part[s][N][C] (in place), then out = LayerNorm(x).
+int launch_residual_layernorm(void* out, void* x, const float* part, int splits, const void* bias,
+                              const void* gamma, const void* beta, int N, int C, float eps, int dtype,
+                              hipStream_t s) {
+    if (splits < 1 || splits > kMaxResSplits) return GPT2_ERR_INVALID_ARGUMENT;
+    if (dtype == GPT2_BF16)
+        launch_ln_t<bf16, true>((bf16*)out, nullptr, nullptr, (bf16*)x, (const bf16*)gamma, (const bf16*)beta,
+                                N, C, eps, part, splits, (const bf16*)bias, s);
+    else
+        launch_ln_t<float, true>((float*)out, nullptr, nullptr, (float*)x, (const float*)gamma,
+                                 (const float*)beta, N, C, eps, part, splits, (const float*)bias, s);
     return launch_status();
 }
 
@@ -236,6 +293,21 @@ extern "C" int layernorm_forward(void* out, float* mean, float* rstd, const void
     if (out == inp) return GPT2_ERR_INVALID_ARGUMENT;
     return launch_layernorm(out, mean, rstd, inp, gamma, beta, N, C, eps, dtype,
                             (hipStream_t)stream);
+}
+
+extern "C" int residual_layernorm_forward(void* out, void* x, const float* part, int splits, const void* bias,
+                                          const void* gamma, const void* beta, int N, int C, float eps,
+                                          int dtype, void* stream) {
+    if (!valid_dtype(dtype) || N < 0 || C < 0 || !(eps >= 0.f) || splits < 1 || splits > kMaxResSplits)
+        return GPT2_ERR_INVALID_ARGUMENT;
+    if (N == 0) return GPT2_OK;
+    if (!out || !x || !part || !bias || !gamma || !beta || C == 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (C % 8 || C > 4096 || !aligned16(out) || !aligned16(x) || !aligned16(part) || !aligned16(bias) ||
+        !aligned16(gamma) || !aligned16(beta))
+        return GPT2_ERR_UNSUPPORTED;
+    if (out == x) return GPT2_ERR_INVALID_ARGUMENT;
+    return launch_residual_layernorm(out, x, part, splits, bias, gamma, beta, N, C, eps, dtype,
+                                     (hipStream_t)stream);
 }
 
 extern "C" int softmax_forward(void* probs, const void* logits, int N, int V, int Vp, int dtype,
