@@ -358,7 +358,10 @@ def test_softmax(dt, N, V, Vp):
 # ----------------------------------------------------------------- decode attention
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("B,C,NH,maxT,pos", [(2, 256, 4, 1024, 1023), (3, 256, 4, 1024, 0),
-                                              (2, 128, 8, 300, 257), (1, 768, 12, 1024, 700)])
+                                              (2, 128, 8, 300, 257), (1, 768, 12, 1024, 700),
+                                              # several key chunks per head, merged by the combine kernel
+                                              (2, 256, 4, 3000, 2500), (1, 256, 2, 2048, 1500),
+                                              (1, 128, 4, 4100, 4099)])
 def test_attention_decode(dt, B, C, NH, maxT, pos):
     announce("attention-decode", dt, B, C, NH, maxT, pos)
     d = DT[dt]

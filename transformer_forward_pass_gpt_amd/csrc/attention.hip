@@ -384,101 +384,129 @@ bool attention_head_size_ok(int hs) { return hs == 16 || hs == 32 || hs == 64 ||
 // ------------------------------------------------------------------ decode
 // One new query per sequence against a KV cache (optdl2025 NanoGPT project:
 // KV caching for autoregressive prediction). The keys 0..pos of each
-// (sequence, head) are split into chunks of kDecChunk; each workgroup streams
-// one chunk of K and V once with 16-byte loads and leaves an unnormalised
-// partial (o, m, l); a second kernel merges the partials in a fixed order,
-// so the result does not depend on scheduling.
-static constexpr int kDecChunk = 256;
+// (sequence, head) are cut into chunks of decode_chunk<T, HS> keys, one
+// 512-thread workgroup per chunk. Each thread owns a 16-byte slice of
+// kDecPasses key rows and the matching value rows and issues all of those
+// loads before the first use, so a workgroup waits on memory once. Scores
+// stay in registers: the TPK threads of a key row end the dot product with
+// the same value, the chunk's max and sum-of-exponentials are block
+// reductions, and the weighted value rows are summed across key groups by
+// shuffles and then across wavefronts through LDS in a fixed order. A chunk
+// that covers every key writes the normalised output; otherwise it leaves an
+// unnormalised partial (o, m, l) that decode_combine_kernel merges in chunk
+// order, so the result does not depend on scheduling.
+static constexpr int kDecThreads = 512;
+static constexpr int kDecPasses = 8;
+static constexpr int kDecMinChunk = 64;  // smallest chunk a launch may use (bounds the workspace)
 
-template <typename T, int HS>
-__global__ __launch_bounds__(256) void decode_partial_kernel(float* __restrict__ part,
-                                                             const T* __restrict__ qkv_new,
-                                                             T* __restrict__ kc, T* __restrict__ vc,
-                                                             int pos, int maxT, int C, int NH,
-                                                             float sl2) {
+template <typename T, int HS, int NT = kDecThreads, int NP = kDecPasses>
+constexpr int decode_chunk() {
+    return NP * NT / (HS / Vec<T>::N);
+}
+
+template <typename T, int HS, int NT = kDecThreads, int NP = kDecPasses>
+__global__ __launch_bounds__(NT) void decode_attn_kernel(T* __restrict__ out, float* __restrict__ part,
+                                                                  const T* __restrict__ qkv_new,
+                                                                  T* __restrict__ kc, T* __restrict__ vc,
+                                                                  int pos, int maxT, int C, int NH, float sl2) {
     constexpr int VE = Vec<T>::N;
-    constexpr int TPK = HS / VE;   // threads per key row
-    constexpr int KPP = 256 / TPK;  // keys per pass
+    constexpr int TPK = HS / VE;             // threads per key row
+    constexpr int KPP = NT / TPK;   // key rows per pass
+    constexpr int CHUNK = KPP * NP;
+    constexpr int NW = NT / 64;
     static_assert(HS % VE == 0 && 64 % TPK == 0, "head size");
-    __shared__ float sc[kDecChunk];
-    __shared__ float red[KPP * HS];
-    __shared__ float sh[4];
+    __shared__ float red[NW * HS];
+    __shared__ float shm[NW], shl[NW];
 
     const int split = blockIdx.x, nsplit = gridDim.x, bh = blockIdx.y;
     const int b = bh / NH, hd = bh % NH;
-    const int j0 = split * kDecChunk, j1 = min(j0 + kDecChunk, pos + 1);
-    float* pp = part + ((int64_t)bh * nsplit + split) * (HS + 2);
+    const int j0 = split * CHUNK, j1 = min(j0 + CHUNK, pos + 1);  // j0 <= pos: the grid covers 0..pos
     const int tid = threadIdx.x, sub = tid % TPK, kg = tid / TPK;
     const int lane = tid & 63, w = tid >> 6;
     const T* qrow = qkv_new + (int64_t)b * 3 * C;
-    const T* knew = qrow + C + hd * HS;
-    const T* vnew = qrow + 2 * C + hd * HS;
-    T* K = kc + (int64_t)bh * maxT * HS;
-    T* Vc = vc + (int64_t)bh * maxT * HS;
+    const T* knew = qrow + C + hd * HS + sub * VE;
+    const T* vnew = qrow + 2 * C + hd * HS + sub * VE;
+    T* K = kc + (int64_t)bh * maxT * HS + sub * VE;
+    T* Vc = vc + (int64_t)bh * maxT * HS + sub * VE;
 
-    if (j0 >= j1) {  // empty chunk: neutral partial
-        if (tid < HS) pp[tid] = 0.f;
-        if (tid == 0) { pp[HS] = -INFINITY; pp[HS + 1] = 0.f; }
-        return;
-    }
     if (pos >= j0 && pos < j1 && tid < TPK) {  // this step's k, v into the cache
-        *reinterpret_cast<u32x4*>(K + (int64_t)pos * HS + sub * VE) =
-            *reinterpret_cast<const u32x4*>(knew + sub * VE);
-        *reinterpret_cast<u32x4*>(Vc + (int64_t)pos * HS + sub * VE) =
-            *reinterpret_cast<const u32x4*>(vnew + sub * VE);
+        *reinterpret_cast<u32x4*>(K + (int64_t)pos * HS) = *reinterpret_cast<const u32x4*>(knew);
+        *reinterpret_cast<u32x4*>(Vc + (int64_t)pos * HS) = *reinterpret_cast<const u32x4*>(vnew);
+    }
+    // every load first: key row j (the new one from qkv_new, never from the
+    // cache slot being written); rows past the chunk read row j0 and are masked
+    u32x4 kr[NP], vr[NP];
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+        const int j = j0 + kg + p * KPP;
+        const int jc = j < j1 ? j : j0;
+        kr[p] = *reinterpret_cast<const u32x4*>(jc == pos ? knew : K + (int64_t)jc * HS);
+        vr[p] = *reinterpret_cast<const u32x4*>(jc == pos ? vnew : Vc + (int64_t)jc * HS);
     }
     float q[VE];
     load_vec(qrow + hd * HS + sub * VE, q);
-    for (int j = j0 + kg; j < j1; j += KPP) {
+    float sc[NP];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
         float k[VE];
-        load_vec(j == pos ? knew + sub * VE : K + (int64_t)j * HS + sub * VE, k);
+        unpack_vec<T>(kr[p], k);
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < VE; e++) d += q[e] * k[e];
 #pragma unroll
         for (int o = TPK / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
-        if (sub == 0) sc[j - j0] = d * sl2;
+        sc[p] = j0 + kg + p * KPP < j1 ? d * sl2 : -INFINITY;
+        mx = fmaxf(mx, sc[p]);
     }
-    __syncthreads();
-    const int n = j1 - j0;
-    float mx = -INFINITY;
-    for (int i = tid; i < n; i += 256) mx = fmaxf(mx, sc[i]);
     mx = wave_max(mx);
-    if (lane == 0) sh[w] = mx;
+    if (lane == 0) shm[w] = mx;
     __syncthreads();
-    mx = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-    __syncthreads();
-    float ls = 0.f;
-    for (int i = tid; i < n; i += 256) {
-        const float p = exp2f(sc[i] - mx);
-        sc[i] = p;
-        ls += p;
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) sh[w] = ls;
-    __syncthreads();
-    ls = (sh[0] + sh[1]) + (sh[2] + sh[3]);
-    float acc[VE];
+    mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NW; i++) mx = fmaxf(mx, shm[i]);  // finite: key j0 is valid
+    float ls = 0.f, acc[VE];
 #pragma unroll
     for (int e = 0; e < VE; e++) acc[e] = 0.f;
-    for (int j = j0 + kg; j < j1; j += KPP) {
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+        const float pw = exp2f(sc[p] - mx);  // 0 for masked rows
+        ls += pw;
         float v[VE];
-        load_vec(j == pos ? vnew + sub * VE : Vc + (int64_t)j * HS + sub * VE, v);
-        const float p = sc[j - j0];
+        unpack_vec<T>(vr[p], v);
 #pragma unroll
-        for (int e = 0; e < VE; e++) acc[e] += p * v[e];
+        for (int e = 0; e < VE; e++) acc[e] += pw * v[e];
     }
+    // key groups of a wavefront: lanes that differ in the bits above TPK
 #pragma unroll
-    for (int e = 0; e < VE; e++) red[kg * HS + sub * VE + e] = acc[e];
+    for (int o = TPK; o < 64; o <<= 1) {
+        ls += __shfl_xor(ls, o, 64);
+#pragma unroll
+        for (int e = 0; e < VE; e++) acc[e] += __shfl_xor(acc[e], o, 64);
+    }
+    if (lane < TPK) {
+#pragma unroll
+        for (int e = 0; e < VE; e++) red[w * HS + sub * VE + e] = acc[e];
+        if (lane == 0) shl[w] = ls;  // the wave's key groups, each key once
+    }
     __syncthreads();
     if (tid < HS) {
-        float s = 0.f;
-        for (int g = 0; g < KPP; g++) s += red[g * HS + tid];
-        pp[tid] = s;
-    }
-    if (tid == 0) {
-        pp[HS] = mx;
-        pp[HS + 1] = ls;
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; i++) {
+            o += red[i * HS + tid];
+            l += shl[i];
+        }
+        if (nsplit == 1) {
+            store_scalar(out + (int64_t)b * C + hd * HS + tid, o / l);
+        } else {
+            float* pp = part + ((int64_t)bh * nsplit + split) * (HS + 2);
+            pp[tid] = o;
+            if (tid == 0) {
+                pp[HS] = mx;
+                pp[HS + 1] = l;
+            }
+        }
     }
 }
 
@@ -502,18 +530,20 @@ __global__ __launch_bounds__(HS) void decode_combine_kernel(T* __restrict__ out,
 
 int64_t decode_workspace_bytes(int B, int C, int NH, int maxT) {
     const int hs = C / NH;
-    const int64_t nsplit = (maxT + kDecChunk - 1) / kDecChunk;
+    const int64_t nsplit = (maxT + kDecMinChunk - 1) / kDecMinChunk;
     return (int64_t)B * NH * nsplit * (hs + 2) * 4;
 }
 
 template <typename T, int HS>
 static void launch_decode_hs(T* out, const T* qkv_new, T* kc, T* vc, int B, int pos, int maxT,
                              int C, int NH, float* part, hipStream_t s) {
+    constexpr int CHUNK = decode_chunk<T, HS>();
+    static_assert(CHUNK >= kDecMinChunk, "workspace bound");
     const float sl2 = 1.4426950408889634f / sqrtf((float)HS);
-    const int nsplit = (pos + 1 + kDecChunk - 1) / kDecChunk;
-    decode_partial_kernel<T, HS><<<dim3(nsplit, B * NH), 256, 0, s>>>(part, qkv_new, kc, vc, pos,
-                                                                       maxT, C, NH, sl2);
-    decode_combine_kernel<T, HS><<<B * NH, HS, 0, s>>>(out, part, nsplit, C, NH);
+    const int nsplit = (pos + 1 + CHUNK - 1) / CHUNK;
+    decode_attn_kernel<T, HS><<<dim3(nsplit, B * NH), kDecThreads, 0, s>>>(out, part, qkv_new, kc, vc, pos,
+                                                                           maxT, C, NH, sl2);
+    if (nsplit > 1) decode_combine_kernel<T, HS><<<B * NH, HS, 0, s>>>(out, part, nsplit, C, NH);
 }
 
 template <typename T>

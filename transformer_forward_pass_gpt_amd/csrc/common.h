@@ -48,6 +48,19 @@ __device__ __forceinline__ void load_vec(const bf16* p, float (&v)[8]) {
     v[4] = bf16_to_f32(x.z & 0xffffu); v[5] = bf16_to_f32(x.z >> 16);
     v[6] = bf16_to_f32(x.w & 0xffffu); v[7] = bf16_to_f32(x.w >> 16);
 }
+// A 16-byte vector already in registers, widened to fp32.
+template <typename T> __device__ __forceinline__ void unpack_vec(const u32x4& x, float (&v)[Vec<T>::N]);
+template <> __device__ __forceinline__ void unpack_vec<float>(const u32x4& x, float (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = __uint_as_float(x[i]);
+}
+template <> __device__ __forceinline__ void unpack_vec<bf16>(const u32x4& x, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        v[2 * i] = bf16_to_f32(x[i] & 0xffffu);
+        v[2 * i + 1] = bf16_to_f32(x[i] >> 16);
+    }
+}
 __device__ __forceinline__ void store_vec(float* p, const float (&v)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
