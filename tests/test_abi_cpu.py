@@ -66,7 +66,8 @@ def test_workspace_sizes():
     N = w.B * w.T
     ws = G.workspace_bytes(cfg, w.B, w.T)
     assert ws >= 11 * N * w.C * 4 and ws < 11 * N * w.C * 4 + 7 * 256
-    assert G.attention_decode_workspace_bytes(32, 768, 12, 1024) == 32 * 12 * 4 * 66 * 4
+    # partials (o[hs], m, l) fp32 for up to maxT/64 key chunks per (sequence, head)
+    assert G.attention_decode_workspace_bytes(32, 768, 12, 1024) == 32 * 12 * 16 * 66 * 4
     assert G.decode_workspace_bytes(cfg, 32) > 11 * 32 * 768 * 4
 
 
