@@ -50,8 +50,8 @@ def parse():
                     help="decode workload: sequences the CPU oracle steps")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--profile-kernel", action="store_true",
-                    help="counter-collection mode: launch only the logits GEMM (3x) and a "
-                         "256 MiB device copy (calibration), print their names and sizes")
+                    help="counter-collection mode: launch only the dominant kernel (3x: the logits "
+                         "GEMM, or the decode attention) and a 256 MiB device copy (calibration)")
     return ap.parse_args()
 
 
@@ -356,24 +356,35 @@ def source_sha1():
 
 
 def profile_kernel(b):
-    """Launch the vocabulary GEMM three times and one plain device-to-device
-    copy of 256 MiB, for hardware-counter runs (rocprofv3 --pmc FETCH_SIZE /
-    WRITE_SIZE): the copy reads and writes a known number of bytes, which
-    calibrates the counters."""
+    """Counter-collection mode (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE): launch
+    the workload's dominant kernel three times, then one plain 256 MiB
+    device-to-device copy whose known bytes calibrate the counters. Forward
+    workloads: the vocabulary GEMM; decode: attention over the KV cache of
+    layers 0..2 (one decode_attn launch, plus its combine when it splits)."""
     torch, G, I, w = b.torch, b.G, b.I, b.w
-    N = w.B * w.T
-    o, shp = I.param_offsets(w.L, w.C, w.maxT, w.Vp)["wte"]
-    wte = b.params[o:o + int(np.prod(shp))].view(*shp)
-    ln = torch.randn(N, w.C, device="cuda").to(b.tdtype)
-    logits = b.logits.view(N, w.Vp)
-    for _ in range(3):
-        G.matmul_forward(logits, ln, wte, None)
+    if b.decode:
+        B, C, NH = w.B, w.C, w.NH
+        qkv = torch.randn(B, 3 * C, device="cuda").to(b.tdtype)
+        att = torch.empty(B, C, dtype=b.tdtype, device="cuda")
+        aws = torch.empty(G.attention_decode_workspace_bytes(B, C, NH, w.maxT), dtype=torch.uint8, device="cuda")
+        for l in range(3):
+            G.attention_decode_forward(att, qkv, b.kcache[l], b.vcache[l], w.decode_pos, NH, aws)
+        info = {"kernel": "attention_decode", "shape": [B, NH, w.decode_pos + 1, w.hs]}
+    else:
+        N = w.B * w.T
+        o, shp = I.param_offsets(w.L, w.C, w.maxT, w.Vp)["wte"]
+        wte = b.params[o:o + int(np.prod(shp))].view(*shp)
+        ln = torch.randn(N, w.C, device="cuda").to(b.tdtype)
+        logits = b.logits.view(N, w.Vp)
+        for _ in range(3):
+            G.matmul_forward(logits, ln, wte, None)
+        info = {"kernel": G.matmul_kernel_config(N, w.C, w.Vp, w.dtype), "shape": [N, w.C, w.Vp]}
     src = torch.ones(64 << 20, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"gemm_kernel": G.matmul_kernel_config(N, w.C, w.Vp, w.dtype),
-                      "gemm_shape": [N, w.C, w.Vp], "copy_bytes_each_way": 256 << 20}))
+    info["copy_bytes_each_way"] = 256 << 20
+    print(json.dumps(info))
 
 
 def cpu_baseline(b, ntok):
@@ -421,8 +432,6 @@ def main():
     torch.cuda.set_device(0)
     b = Bench(w, keep_host_cache=decode and not args.no_cpu_baseline)
     if args.profile_kernel:
-        if decode:
-            raise SystemExit("--profile-kernel runs the prefill logits GEMM; use a forward workload")
         profile_kernel(b)
         return
     for _ in range(args.warmup):
