@@ -228,8 +228,12 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 // is followed by one fragment read; 4 = hard fences: each segment issues the
 // fragment reads of k-chunk kc+1, then the MFMAs of chunk kc, whose operands
 // were read one segment earlier (so no MFMA waits on a fresh LDS read).
-template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_pipe_kernel(T* __restrict__ out, const T* __restrict__ A,
+// WPE: minimum wavefronts per SIMD the register allocation must allow (0: no
+// constraint); 2 workgroups of 8 wavefronts per CU need WPE = 4. DIRECT:
+// store the output straight from the accumulators (no LDS staging), which
+// keeps the LDS footprint at the stages alone.
+template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false>
+__global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* __restrict__ out, const T* __restrict__ A,
                                                                 const T* __restrict__ W,
                                                                 const T* __restrict__ bias, int M, int N,
                                                                 int K, int group_m, int remap) {
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_pipe_kernel(T* __restrict__ 
     constexpr int STAGE = (BM + BN) * BK;  // elements per stage (A tile then W tile)
     constexpr int LDO = BN + VE;           // row stride of the output tile in the epilogue
     // stage the output tile through LDS when it fits in 160 KiB
-    constexpr bool STAGED = BM * LDO * (int)sizeof(T) <= 160 * 1024;
+    constexpr bool STAGED = !DIRECT && BM * LDO * (int)sizeof(T) <= 160 * 1024;
     constexpr int SMEM = (STAGED && BM * LDO > S * STAGE) ? BM * LDO : S * STAGE;
     __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
@@ -427,12 +431,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_pipe_kernel(T* __restrict__ 
     }
 }
 
-template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED>
+template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false>
 static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
                              int group_m, int remap, hipStream_t s) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED><<<nwg, WM * WN * 64, 0, s>>>(
+    gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT><<<nwg, WM * WN * 64, 0, s>>>(
         out, A, W, bias, M, N, K, group_m, remap);
 }
 

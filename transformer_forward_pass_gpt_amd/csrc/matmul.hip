@@ -31,27 +31,34 @@ struct PipeCfg {
 };
 enum GemmCfg {
     S32 = 0, R64x64, R64x128, R128x96,
-    P64x64, P128x96_S4, P128x96_S5, P128x128, P128x192, P256x128_S3A, P256x128_S3B, P256x256,
+    P128x96_S4, P128x96_S5, P256x128_S3A,                                 // fp32
+    P128x128_O2,                                                          // fp32 and bf16
+    P128x128_O3, P128x256_O4, P256x128_S3G, P256x256_W16,                 // bf16
     G_NCFG
 };
+// "_p<S>" = S-stage pipeline; "_o<n>" = registers capped so n wavefronts fit per SIMD (2 or 3
+// workgroups per CU); "_w16" = 16 wavefronts per workgroup.
 static const PipeCfg kCfg[G_NCFG] = {
-    {"skinny32", 0},        {"64x64_r", 0},          {"64x128_r", 0},      {"128x96_r", 0},
-    {"64x64_p6", 64},       {"128x96_p4", 128},      {"128x96_p5", 128},   {"128x128_p6", 64},
-    {"128x192_p5", 64},     {"256x128_p3", 128},     {"256x128_p3s", 128}, {"256x256_p4", 64},
+    {"skinny32", 0},          {"64x64_r", 0},          {"64x128_r", 0},         {"128x96_r", 0},
+    {"128x96_p4", 128},       {"128x96_p5", 128},      {"256x128_p3", 128},     {"128x128_p4_o2", 64},
+    {"128x128_p3_o3", 64},    {"128x256_p3_o4", 64},   {"256x128_p3g", 128},    {"256x256_p3_w16", 64},
 };
 
 static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
-    auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (dtype == GPT2_F32) {
         if (N >= 16384) return P256x128_S3A;                 // vocabulary projection
         if (K >= 2048) return P128x96_S5;                    // fcproj
         if (N <= 1024) return P128x96_S4;                    // attproj
-        return N >= 3072 ? P128x192 : P64x64;                // fc, qkv
+        return N >= 3072 ? P128x128_O2 : P128x96_S5;         // fc, qkv
     }
-    if (N >= 16384) return P256x256;
-    if (K >= 2048 || N <= 1024) return tiles(256, 128) >= 192 ? P256x128_S3A : P128x128;
-    if (M <= 4096 && tiles(256, 256) >= 192) return P256x256;
-    return tiles(256, 128) >= 256 ? P256x128_S3B : P128x128;
+    // bf16: K = 768 or 1024 gives each output tile only a few microseconds of
+    // MFMA work, so below the vocabulary projection the tiles are sized for
+    // two or three resident workgroups per CU (one's fill and epilogue
+    // overlap the others' math).
+    if (N >= 16384) return P256x256_W16;                       // vocabulary projection
+    if (K >= 2048) return M >= 8192 ? P256x128_S3G : P128x128_O2;  // fcproj
+    if (N <= 1024) return M >= 8192 ? P128x256_O4 : P128x128_O3;   // attproj
+    return M >= 8192 ? P128x256_O4 : P256x256_W16;             // qkv, fc
 }
 
 static GemmCfg choose_cfg(int M, int N, int K, int dtype) {
@@ -75,15 +82,20 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, int M, 
         case R64x64: launch_gemm_cfg<T, 2, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 4, 1, s); break;
         case R64x128: launch_gemm_cfg<T, 2, 2, 1, 2, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
         case R128x96: launch_gemm_cfg<T, 4, 1, 1, 3, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        // launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SCHED>(..., group_m, remap, s)
-        case P64x64: launch_gemm_pipe<T, 2, 2, 1, 1, 64, 6, 1>(out, A, W, bias, M, N, K, 4, 1, s); break;
+        // launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SCHED, WPE>(..., group_m, remap, s)
         case P128x96_S4: launch_gemm_pipe<T, 4, 1, 1, 3, 128, 4, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
         case P128x96_S5: launch_gemm_pipe<T, 4, 1, 1, 3, 128, 5, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P128x128: launch_gemm_pipe<T, 2, 2, 2, 2, 64, 6, 2>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P128x192: launch_gemm_pipe<T, 2, 2, 2, 3, 64, 5, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
         case P256x128_S3A: launch_gemm_pipe<T, 4, 2, 2, 2, 128, 3, 2>(out, A, W, bias, M, N, K, 1, 0, s); break;
-        case P256x128_S3B: launch_gemm_pipe<T, 4, 2, 2, 2, 128, 3, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        default: launch_gemm_pipe<T, 2, 4, 4, 2, 64, 4, 2>(out, A, W, bias, M, N, K, 4, 1, s); break;
+        case P128x128_O3: launch_gemm_pipe<T, 2, 2, 2, 2, 64, 3, 2, 3>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P128x128_O2: launch_gemm_pipe<T, 2, 2, 2, 2, 64, 4, 2, 2>(out, A, W, bias, M, N, K, 4, 1, s); break;
+        case P128x256_O4: launch_gemm_pipe<T, 2, 4, 2, 2, 64, 3, 2, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case P256x128_S3G: launch_gemm_pipe<T, 4, 2, 2, 2, 128, 3, 2>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        default:
+            if (N >= 16384)  // vocabulary: column sweep within each row band
+                launch_gemm_pipe<T, 4, 4, 2, 2, 64, 3, 2>(out, A, W, bias, M, N, K, 1, 0, s);
+            else
+                launch_gemm_pipe<T, 4, 4, 2, 2, 64, 3, 2>(out, A, W, bias, M, N, K, 4, 1, s);
+            break;
     }
 }
 
