@@ -3,8 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small]
 
-One step = one gpt2_forward (encoder, 12 blocks, final LayerNorm, logits GEMM,
-vocabulary softmax) over one batch of synthetic tokens, with weights, tokens,
+One step = one gpt2_forward (encoder, 12 blocks with GELU and the residual
+adds fused into the GEMM epilogues, final LayerNorm, logits GEMM, vocabulary
+softmax) over one batch of synthetic tokens, with weights, tokens,
 workspace and outputs already resident in HBM. Prints ONE JSON line. With
 ``--workload decode`` a step is one gpt2_decode_step instead: one new token
 for each of 32 sequences against a prefilled key/value cache.
@@ -136,7 +137,7 @@ class Bench:
             return t if l is None else t[l]
 
         mk = lambda *s: torch.empty(s, dtype=self.tdtype, device="cuda")  # noqa: E731
-        x, ln, qkv, att, tmp, fc = mk(N, C), mk(N, C), mk(N, 3 * C), mk(N, C), mk(N, C), mk(N, 4 * C)
+        x, ln, qkv, att, fc = mk(N, C), mk(N, C), mk(N, 3 * C), mk(N, C), mk(N, 4 * C)
         logits = self.logits.view(N, w.Vp)
         probs = self.probs.view(N, w.Vp)
         s = torch.cuda.current_stream()
@@ -155,9 +156,16 @@ class Bench:
             recs.append([kind, name, flops, nbytes, a, b, site or name])
 
         # GEMM launches are named by the kernel configuration the library picks
-        gemm = lambda out, inp, wt, bias, M, K, Nc, Nalg, tag: timed(  # noqa: E731
-            "gemm", G.matmul_kernel_config(M, K, Nc, w.dtype),
-            lambda: G.matmul_forward(out, inp, wt, bias), 2.0 * M * Nalg * K, 0.0, "gemm_" + tag)
+        # (plus the epilogue fused into it)
+        def gemm(out, inp, wt, bias, M, K, Nc, Nalg, tag, epi=""):
+            if epi == "residual":
+                fn = lambda: G.matmul_residual_forward(out, inp, wt, bias, out)  # noqa: E731
+            elif epi == "gelu":
+                fn = lambda: G.matmul_gelu_forward(out, inp, wt, bias)  # noqa: E731
+            else:
+                fn = lambda: G.matmul_forward(out, inp, wt, bias)  # noqa: E731
+            name = G.matmul_kernel_config(M, K, Nc, w.dtype) + ("+" + epi if epi else "")
+            timed("gemm", name, fn, 2.0 * M * Nalg * K, 0.0, "gemm_" + tag + ("+" + epi if epi else ""))
         all_runs = []
         host_ms = 50.0
         for _ in range(reps + 1):  # the first pass measures the host enqueue time
@@ -172,14 +180,11 @@ class Bench:
                 gemm(qkv, ln, P("qkv_w", l), P("qkv_b", l), N, C, 3 * C, 3 * C, "qkv")
                 timed("mfma", "attention", lambda: G.attention_forward(att.view(B, T, C), qkv.view(B, T, 3 * C), NH),
                       4.0 * B * NH * (C // NH) * T * (T + 1) / 2, 0.0)
-                gemm(tmp, att, P("attproj_w", l), P("attproj_b", l), N, C, C, C, "attproj")
-                timed("hbm", "residual", lambda: G.residual_forward(x, x, tmp), 0.0, 3 * N * C * es)
+                gemm(x, att, P("attproj_w", l), P("attproj_b", l), N, C, C, C, "attproj", "residual")
                 timed("hbm", "layernorm", lambda: G.layernorm_forward(ln, x, P("ln2_g", l), P("ln2_b", l), w.ln_eps),
                       0.0, 2 * N * C * es + 2 * C * es)
-                gemm(fc, ln, P("fc_w", l), P("fc_b", l), N, C, 4 * C, 4 * C, "fc")
-                timed("hbm", "gelu", lambda: G.gelu_forward(fc, fc), 0.0, 2 * N * 4 * C * es)
-                gemm(tmp, fc, P("fcproj_w", l), P("fcproj_b", l), N, 4 * C, C, C, "fcproj")
-                timed("hbm", "residual", lambda: G.residual_forward(x, x, tmp), 0.0, 3 * N * C * es)
+                gemm(fc, ln, P("fc_w", l), P("fc_b", l), N, C, 4 * C, 4 * C, "fc", "gelu")
+                gemm(x, fc, P("fcproj_w", l), P("fcproj_b", l), N, 4 * C, C, C, "fcproj", "residual")
             timed("hbm", "layernorm", lambda: G.layernorm_forward(ln, x, P("lnf_g"), P("lnf_b"), w.ln_eps),
                   0.0, 2 * N * C * es + 2 * C * es)
             gemm(logits, ln, P("wte"), None, N, C, w.Vp, w.V, "logits")
@@ -214,7 +219,7 @@ class Bench:
             return t if l is None else t[l]
 
         mk = lambda *s: torch.empty(s, dtype=self.tdtype, device="cuda")  # noqa: E731
-        x, ln, qkv, att, tmp, fc = mk(B, C), mk(B, C), mk(B, 3 * C), mk(B, C), mk(B, C), mk(B, 4 * C)
+        x, ln, qkv, att, fc = mk(B, C), mk(B, C), mk(B, 3 * C), mk(B, C), mk(B, 4 * C)
         aws = torch.empty(G.attention_decode_workspace_bytes(B, C, NH, w.maxT), dtype=torch.uint8,
                           device="cuda")
         s = torch.cuda.current_stream()

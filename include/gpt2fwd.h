@@ -156,7 +156,7 @@ int attention_decode_forward(void* out, const void* qkv_new, void* kcache, void*
 /* Decode-step building blocks. gpt2_decode_step on B <= 32 sequences runs
  * each layer as: matmul_forward (qkv) -> attention_decode_forward ->
  * matmul_splitk_forward (attproj) -> residual_layernorm_forward (ln2) ->
- * matmul_gelu_forward (fc) -> matmul_splitk_forward (fcproj) ->
+ * matmul_gelu_forward (fc, below) -> matmul_splitk_forward (fcproj) ->
  * residual_layernorm_forward (ln1 of the next layer, or lnf), i.e. the block
  * of the forward with the residual adds and the GELU fused into neighbours.
  *
@@ -173,13 +173,18 @@ int matmul_splitk_forward(float* part, const void* inp, const void* weight, int 
  * call): enough workgroups to cover the chip, >= 2 chunks each; 1..8. */
 int matmul_splitk_count(int C, int OC, int dtype);
 
-/* Linear layer followed by GELU (tanh form), as fc + gelu of a block:
- *   out[n,o] = gelu(sum_c inp[n,c] * weight[o,c] + bias[o])
- * Shapes and rules as matmul_forward (bias nullable). For N <= 32 the GELU
- * is applied to the fp32 accumulator before rounding (one launch); for
- * larger N it runs on the stored product (matmul_forward, gelu_forward). */
+/* Linear layer with the next step of a block fused into its epilogue (the
+ * "kernel fusion" item of llm.c "State of the Union", big stones):
+ *   matmul_gelu_forward:     out[n,o] = gelu(y[n,o])             (fc + GELU)
+ *   matmul_residual_forward: out[n,o] = res[n,o] + y[n,o]        (attproj/fcproj + residual)
+ * with y = sum_c inp[n,c] * weight[o,c] + bias[o] rounded to the dtype first,
+ * so the result is bit-identical to matmul_forward followed by gelu_forward
+ * or residual_forward. Shapes and rules as matmul_forward (bias nullable);
+ * res [N,OC] may be out itself (x += ...); out must not alias inp or weight. One launch. */
 int matmul_gelu_forward(void* out, const void* inp, const void* weight, const void* bias,
                         int N, int C, int OC, int dtype, void* stream);
+int matmul_residual_forward(void* out, const void* inp, const void* weight, const void* bias,
+                            const void* res, int N, int C, int OC, int dtype, void* stream);
 
 /* Residual add of a split-k projection, then LayerNorm:
  *   x[n,:] <- x[n,:] + (bias + sum_{s<splits} part[s][n][:])   (in place;

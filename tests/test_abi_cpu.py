@@ -65,10 +65,11 @@ def test_workspace_sizes():
     cfg = cfg_of(w)
     N = w.B * w.T
     ws = G.workspace_bytes(cfg, w.B, w.T)
-    assert ws >= 11 * N * w.C * 4 and ws < 11 * N * w.C * 4 + 7 * 256
+    # x, ln, att [N,C]; qkv [N,3C]; fc [N,4C]
+    assert ws >= 10 * N * w.C * 4 and ws < 10 * N * w.C * 4 + 6 * 256
     # partials (o[hs], m, l) fp32 for up to maxT/64 key chunks per (sequence, head)
     assert G.attention_decode_workspace_bytes(32, 768, 12, 1024) == 32 * 12 * 16 * 66 * 4
-    assert G.decode_workspace_bytes(cfg, 32) > 11 * 32 * 768 * 4
+    assert G.decode_workspace_bytes(cfg, 32) > 10 * 32 * 768 * 4
 
 
 def test_status_strings():
@@ -107,6 +108,8 @@ def test_validation_rejects_before_launch():
     assert lib.matmul_splitk_forward(q1, q2, q3, 33, 64, 64, 2, 0, None) == G.ERR_UNSUPPORTED  # N > 32
     assert lib.matmul_splitk_forward(q1, q2, q3, 4, 60, 64, 2, 0, None) == G.ERR_UNSUPPORTED  # C % 8
     assert lib.matmul_gelu_forward(q1, q1, q3, None, 4, 64, 64, 0, None) == G.ERR_INVALID_ARGUMENT  # alias
+    assert lib.matmul_residual_forward(q1, q2, q3, None, None, 4, 64, 64, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.matmul_residual_forward(q1, q2, q3, None, odd, 4, 64, 64, 0, None) == G.ERR_UNSUPPORTED
     assert lib.residual_layernorm_forward(q1, q2, q3, 9, p16, p16, p16, 4, 64, 1e-5, 0, None) \
         == G.ERR_INVALID_ARGUMENT  # splits > 8
     assert lib.residual_layernorm_forward(q1, q1, q3, 2, p16, p16, p16, 4, 64, 1e-5, 0, None) \
@@ -126,6 +129,7 @@ def test_zero_sized_calls_are_noops():
     assert lib.layernorm_forward(None, None, None, None, None, None, 0, 64, 1e-5, 0, None) == G.OK
     assert lib.matmul_splitk_forward(None, None, None, 0, 64, 64, 2, 0, None) == G.OK
     assert lib.matmul_gelu_forward(None, None, None, None, 0, 64, 64, 1, None) == G.OK
+    assert lib.matmul_residual_forward(None, None, None, None, None, 0, 64, 64, 0, None) == G.OK
     assert lib.residual_layernorm_forward(None, None, None, 1, None, None, None, 0, 64, 1e-5, 0, None) == G.OK
 
 

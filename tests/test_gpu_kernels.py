@@ -226,6 +226,55 @@ def test_matmul_gelu(dt, N, C, OC):
     assert rel_err(got, ref) <= (1e-2 if d == I.BF16 else 1e-5)
 
 
+# every GEMM path: skinny (<= 32 rows), register-staged (ragged k), and each pipelined tile shape
+FUSED_SHAPES = [(7, 768, 256), (32, 136, 1000), (65, 72, 200), (64, 64, 192), (300, 768, 2304),
+                (1000, 1024, 4096), (8192, 768, 776), (8200, 3072, 768), (600, 3072, 776), (2100, 768, 1000),
+                (256, 64, 16384)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,OC", FUSED_SHAPES)
+def test_fused_epilogues_bitwise(dt, N, C, OC):
+    """GELU and residual in the GEMM epilogue equal the separate kernels on the
+    stored product bit for bit, including the in-place residual (x += ...)."""
+    announce("fused-epilogue", dt, N, C, OC, G.matmul_kernel_config(N, C, OC, DT[dt]))
+    d = DT[dt]
+    a = dev(I.random_tensor(50, (N, C), 1.0, d), d)
+    w = dev(I.random_tensor(51, (OC, C), 0.05, d), d)
+    b = dev(I.random_tensor(52, OC, 0.05, d), d)
+    r = dev(I.random_tensor(53, (N, OC), 1.0, d), d)
+    y = empty((N, OC), d, fill=float("nan"))
+    G.matmul_forward(y, a, w, b)
+    g_ref = empty((N, OC), d)
+    G.gelu_forward(g_ref, y)
+    r_ref = empty((N, OC), d)
+    G.residual_forward(r_ref, r, y)
+    g = empty((N, OC), d, fill=float("nan"))
+    G.matmul_gelu_forward(g, a, w, b)
+    assert np.array_equal(host_bits(g), host_bits(g_ref))
+    o = empty((N, OC), d, fill=float("nan"))
+    G.matmul_residual_forward(o, a, w, b, r)
+    assert np.array_equal(host_bits(o), host_bits(r_ref))
+    x = r.clone()
+    G.matmul_residual_forward(x, a, w, b, x)  # in place
+    assert np.array_equal(host_bits(x), host_bits(r_ref))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,OC", [(32, 768, 768), (4096, 768, 768), (600, 3072, 776)])
+def test_matmul_residual_vs_oracle(dt, N, C, OC):
+    announce("matmul-residual", dt, N, C, OC)
+    d = DT[dt]
+    a = I.random_tensor(54, (N, C), 1.0, d)
+    w = I.random_tensor(55, (OC, C), 0.05, d)
+    b = I.random_tensor(56, OC, 0.05, d)
+    r = I.random_tensor(57, (N, OC), 1.0, d)
+    x = dev(r, d)
+    G.matmul_residual_forward(x, dev(a, d), dev(w, d), dev(b, d), x)
+    ref = oracle.residual(r, oracle.matmul(a, w, b))
+    assert rel_err(host(x), ref) <= (1e-2 if d == I.BF16 else 1e-6)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N,C,splits", [(32, 768, 4), (32, 768, 8), (7, 64, 1), (1, 1024, 3), (32, 4096, 2)])
 def test_residual_layernorm(dt, N, C, splits):

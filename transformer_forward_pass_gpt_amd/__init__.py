@@ -34,6 +34,7 @@ EXPORTS = (
     "attention_decode_forward", "gpt2_decode_workspace_bytes", "gpt2_decode_step",
     "gpt2_status_string", "gpt2_last_hip_error", "matmul_kernel_config",
     "matmul_splitk_forward", "matmul_splitk_count", "matmul_gelu_forward", "residual_layernorm_forward",
+    "matmul_residual_forward",
 )
 
 
@@ -89,6 +90,7 @@ def load_library(path: str = LIB_PATH):
             "matmul_splitk_forward": (I, [P, P, P, I, I, I, I, I, P]),
             "matmul_splitk_count": (I, [I, I, I]),
             "matmul_gelu_forward": (I, [P, P, P, P, I, I, I, I, P]),
+            "matmul_residual_forward": (I, [P, P, P, P, P, I, I, I, I, P]),
             "residual_layernorm_forward": (I, [P, P, P, I, P, P, P, I, I, F, I, P]),
         }
         for name, (res, args) in sig.items():
@@ -204,6 +206,18 @@ def matmul_gelu_forward(out, inp, weight, bias=None, stream=None):
     OC = weight.shape[0]
     _check("matmul_gelu_forward", lib.matmul_gelu_forward(
         _dev(out, "out"), _dev(inp, "inp"), _dev(weight, "weight"), _dev(bias, "bias"),
+        N, C, OC, _dtype_code(inp), _stream(stream)))
+    return out
+
+
+def matmul_residual_forward(out, inp, weight, bias, res, stream=None):
+    """out [N,OC] = res + (inp [N,C] @ weight[OC,C]^T + bias); res may be out."""
+    lib = load_library()
+    C = inp.shape[-1]
+    N = inp.numel() // C if C else 0
+    OC = weight.shape[0]
+    _check("matmul_residual_forward", lib.matmul_residual_forward(
+        _dev(out, "out"), _dev(inp, "inp"), _dev(weight, "weight"), _dev(bias, "bias"), _dev(res, "res"),
         N, C, OC, _dtype_code(inp), _stream(stream)))
     return out
 

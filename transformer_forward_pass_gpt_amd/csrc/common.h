@@ -108,8 +108,11 @@ __device__ __forceinline__ float wave_max(float x) {
 // ------------------------------------------------------------------ host side
 namespace gpt2 {
 void set_last_hip_error(int e);
-// Epilogues of the skinny (decode) GEMM: bias, or bias then GELU.
-enum SkinnyEpilogue { SKINNY_BIAS = 0, SKINNY_BIAS_GELU = 1 };
+// GEMM epilogues: y = acc + bias, rounded to the output type; then either
+// nothing, GELU of the rounded y, or a residual r added to the rounded y
+// (each rounded again), i.e. exactly what a separate GELU or residual kernel
+// would compute from the stored product.
+enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2 };
 // Status after a launch: GPT2_OK, or GPT2_ERR_HIP with the code recorded.
 int launch_status();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

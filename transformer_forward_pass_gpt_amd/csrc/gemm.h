@@ -53,11 +53,12 @@ __device__ __forceinline__ int xcd_contiguous(int i, int n) {
 }
 
 // WM x WN wavefronts, each owning TM x TN 32x32 tiles; BK = k per LDS tile.
-template <typename T, int WM, int WN, int TM, int TN, int BK, bool ILV = true>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* __restrict__ out, const T* __restrict__ A,
+// EPI and res as for gemm_pipe_kernel.
+template <typename T, int WM, int WN, int TM, int TN, int BK, bool ILV = true, int EPI = EPI_BIAS>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __restrict__ A,
                                                            const T* __restrict__ W,
-                                                           const T* __restrict__ bias, int M, int N,
-                                                           int K, int group_m, int remap) {
+                                                           const T* __restrict__ bias, const T* res, int M,
+                                                           int N, int K, int group_m, int remap) {
     constexpr int NT = WM * WN * 64;
     constexpr int VE = Vec<T>::N;
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
@@ -173,7 +174,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* __restrict__ out, 
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (row < M) store_scalar(out + (int64_t)row * N + col, acc[i][j][v] + bv);
+                if (row < M) {
+                    float y = acc[i][j][v] + bv;
+                    if constexpr (EPI == EPI_BIAS_GELU) y = gelu_tanh(storage_round(out, y));
+                    if constexpr (EPI == EPI_BIAS_RESIDUAL)
+                        y = storage_round(out, y) + load_scalar(res + (int64_t)row * N + col);
+                    store_scalar(out + (int64_t)row * N + col, y);
+                }
             }
         }
     }
@@ -232,11 +239,15 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 // constraint); 2 workgroups of 8 wavefronts per CU need WPE = 4. DIRECT:
 // store the output straight from the accumulators (no LDS staging), which
 // keeps the LDS footprint at the stages alone.
-template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false>
-__global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* __restrict__ out, const T* __restrict__ A,
+// EPI: the epilogue (common.h); res [M,N] is the residual of
+// EPI_BIAS_RESIDUAL and may be `out` itself (each element is read and then
+// written by the same thread).
+template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false,
+          int EPI = EPI_BIAS>
+__global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, const T* __restrict__ A,
                                                                 const T* __restrict__ W,
-                                                                const T* __restrict__ bias, int M, int N,
-                                                                int K, int group_m, int remap) {
+                                                                const T* __restrict__ bias, const T* res, int M,
+                                                                int N, int K, int group_m, int remap) {
     // RB: bytes of k per tile row (64 or 128); S: LDS stages (S-1 tiles in flight)
     constexpr int NW = WM * WN;
     constexpr int VE = Vec<T>::N;
@@ -400,7 +411,9 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* __restri
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int rl = wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    store_scalar(&so[rl * LDO + cl], acc[i][j][v] + bv);
+                    float y = acc[i][j][v] + bv;
+                    if constexpr (EPI == EPI_BIAS_GELU) y = gelu_tanh(storage_round(so, y));
+                    store_scalar(&so[rl * LDO + cl], y);
                 }
         }
         __builtin_amdgcn_s_waitcnt((0xF) | (7 << 4) | (0x0 << 8) | (3 << 14));  // lgkmcnt(0)
@@ -410,9 +423,19 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* __restri
         for (int c = tid; c < BM * CPR; c += NW * 64) {
             const int rl = c / CPR, cv = c % CPR;
             const int row = m0 + rl, col = n0 + cv * VE;
-            if (row < M && col < N)
-                *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) =
-                    *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]);
+            if (row < M && col < N) {
+                const u32x4 y = *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]);
+                if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+                    float a[VE], r[VE];
+                    unpack_vec<T>(y, a);
+                    load_vec(res + (int64_t)row * N + col, r);
+#pragma unroll
+                    for (int e = 0; e < VE; e++) a[e] += r[e];
+                    store_vec(out + (int64_t)row * N + col, a);
+                } else {
+                    *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) = y;
+                }
+            }
         }
     } else {
 #pragma unroll
@@ -425,7 +448,13 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* __restri
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    if (row < M) store_scalar(out + (int64_t)row * N + col, acc[i][j][v] + bv);
+                    if (row < M) {
+                        float y = acc[i][j][v] + bv;
+                        if constexpr (EPI == EPI_BIAS_GELU) y = gelu_tanh(storage_round(out, y));
+                        if constexpr (EPI == EPI_BIAS_RESIDUAL)
+                            y = storage_round(out, y) + load_scalar(res + (int64_t)row * N + col);
+                        store_scalar(out + (int64_t)row * N + col, y);
+                    }
                 }
         }
     }
@@ -433,11 +462,16 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* __restri
 
 template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false>
 static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
-                             int group_m, int remap, hipStream_t s) {
+                             int group_m, int remap, hipStream_t s, int epi = EPI_BIAS, const T* res = nullptr) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT><<<nwg, WM * WN * 64, 0, s>>>(
-        out, A, W, bias, M, N, K, group_m, remap);
+#define GEMM_PIPE_LAUNCH(E)                                                                              \
+    gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, E><<<nwg, WM * WN * 64, 0, s>>>( \
+        out, A, W, bias, res, M, N, K, group_m, remap)
+    if (epi == EPI_BIAS_GELU) GEMM_PIPE_LAUNCH(EPI_BIAS_GELU);
+    else if (epi == EPI_BIAS_RESIDUAL) GEMM_PIPE_LAUNCH(EPI_BIAS_RESIDUAL);
+    else GEMM_PIPE_LAUNCH(EPI_BIAS);
+#undef GEMM_PIPE_LAUNCH
 }
 
 template <typename T, int WM, int WN, int TM, int TN, int SCHED = 4>
@@ -448,11 +482,15 @@ static void launch_gemm_lds3(T* out, const T* A, const T* W, const T* bias, int 
 
 template <typename T, int WM, int WN, int TM, int TN, int BK, bool ILV = true>
 static void launch_gemm_cfg(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
-                            int group_m, int remap, hipStream_t s) {
+                            int group_m, int remap, hipStream_t s, int epi = EPI_BIAS, const T* res = nullptr) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_kernel<T, WM, WN, TM, TN, BK, ILV><<<nwg, WM * WN * 64, 0, s>>>(out, A, W, bias, M, N, K,
-                                                                          group_m, remap);
+#define GEMM_CFG_LAUNCH(E) \
+    gemm_kernel<T, WM, WN, TM, TN, BK, ILV, E><<<nwg, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap)
+    if (epi == EPI_BIAS_GELU) GEMM_CFG_LAUNCH(EPI_BIAS_GELU);
+    else if (epi == EPI_BIAS_RESIDUAL) GEMM_CFG_LAUNCH(EPI_BIAS_RESIDUAL);
+    else GEMM_CFG_LAUNCH(EPI_BIAS);
+#undef GEMM_CFG_LAUNCH
 }
 
 // 16x16 MFMA step: bf16 16x16x32 (one 16-byte piece per lane) or fp32
@@ -490,14 +528,15 @@ template <> struct Mfma16<bf16> {
 // wavefronts takes a contiguous run, PF chunks per batch, in its own LDS
 // stages (PF x 8 KiB per wave); the NW partial tiles are summed through LDS
 // in wave order. With part == nullptr (then splits == 1) it writes
-// out = EPI(bias + sum); otherwise it writes the fp32 partial sums
-// part[y][M][N] (no bias), which the consumer adds in split order.
+// out = EPI(bias + sum) (res: the residual of EPI_BIAS_RESIDUAL, may be out);
+// otherwise it writes the fp32 partial sums part[y][M][N] (no bias), which
+// the consumer adds in split order.
 template <typename T, int NW, int PF, int EPI>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_lds_kernel(T* __restrict__ out, float* __restrict__ part,
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_lds_kernel(T* out, float* __restrict__ part,
                                                                   const T* __restrict__ A,
                                                                   const T* __restrict__ W,
-                                                                  const T* __restrict__ bias, int M, int N,
-                                                                  int K) {
+                                                                  const T* __restrict__ bias, const T* res, int M,
+                                                                  int N, int K) {
     constexpr int VE = Vec<T>::N;
     constexpr int CK = 128 / (int)sizeof(T);  // k per chunk: one 128-byte line per row
     constexpr int TILE = 32 * 128;            // bytes of one 32-row chunk tile
@@ -604,7 +643,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_lds_kernel(T* __restrict_
                 part[((int64_t)blockIdx.y * M + row) * N + col] = x;
             } else {
                 x += bcol[j];
-                if (EPI == SKINNY_BIAS_GELU) x = gelu_tanh(x);
+                if constexpr (EPI == EPI_BIAS_GELU) x = gelu_tanh(storage_round(out, x));
+                if constexpr (EPI == EPI_BIAS_RESIDUAL)
+                    x = storage_round(out, x) + load_scalar(res + (int64_t)row * N + col);
                 store_scalar(out + (int64_t)row * N + col, x);
             }
         }

@@ -11,13 +11,14 @@ static constexpr int kMaxSplits = 8;  // split-k ranges of the decode projection
 // Skinny (M <= 32) problems: the LDS-staged kernel, 8 wavefronts, one chunk
 // per load batch (the fastest variant on every decode shape swept on MI355X).
 template <typename T>
-static void launch_skinny(T* out, float* part, const T* A, const T* W, const T* bias, int M, int N, int K,
-                          int splits, int epi, hipStream_t s) {
+static void launch_skinny(T* out, float* part, const T* A, const T* W, const T* bias, const T* res, int M, int N,
+                          int K, int splits, int epi, hipStream_t s) {
     const dim3 grid((N + 31) / 32, splits);
-    if (epi == SKINNY_BIAS_GELU)
-        gemm_skinny_lds_kernel<T, 8, 1, SKINNY_BIAS_GELU><<<grid, 512, 0, s>>>(out, part, A, W, bias, M, N, K);
-    else
-        gemm_skinny_lds_kernel<T, 8, 1, SKINNY_BIAS><<<grid, 512, 0, s>>>(out, part, A, W, bias, M, N, K);
+#define SKINNY_LAUNCH(E) gemm_skinny_lds_kernel<T, 8, 1, E><<<grid, 512, 0, s>>>(out, part, A, W, bias, res, M, N, K)
+    if (epi == EPI_BIAS_GELU) SKINNY_LAUNCH(EPI_BIAS_GELU);
+    else if (epi == EPI_BIAS_RESIDUAL) SKINNY_LAUNCH(EPI_BIAS_RESIDUAL);
+    else SKINNY_LAUNCH(EPI_BIAS);
+#undef SKINNY_LAUNCH
 }
 
 // Tile shapes, chosen per problem from on-box sweeps (MI355X) over the GPT-2
@@ -74,28 +75,32 @@ static GemmCfg choose_cfg(int M, int N, int K, int dtype) {
 }
 
 template <typename T>
-static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
-                          int dtype, hipStream_t s) {
+static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T* res, int M, int N, int K,
+                          int dtype, int epi, hipStream_t s) {
     constexpr int BK = Vec<T>::N * 8;  // 128 bytes of k per row per LDS tile
     switch (choose_cfg(M, N, K, dtype)) {
-        case S32: launch_skinny<T>(out, nullptr, A, W, bias, M, N, K, 1, SKINNY_BIAS, s); break;
-        case R64x64: launch_gemm_cfg<T, 2, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 4, 1, s); break;
-        case R64x128: launch_gemm_cfg<T, 2, 2, 1, 2, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case R128x96: launch_gemm_cfg<T, 4, 1, 1, 3, BK>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        // launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SCHED, WPE>(..., group_m, remap, s)
-        case P128x96_S4: launch_gemm_pipe<T, 4, 1, 1, 3, 128, 4, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P128x96_S5: launch_gemm_pipe<T, 4, 1, 1, 3, 128, 5, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P256x128_S3A: launch_gemm_pipe<T, 4, 2, 2, 2, 128, 3, 2>(out, A, W, bias, M, N, K, 1, 0, s); break;
-        case P128x128_O3: launch_gemm_pipe<T, 2, 2, 2, 2, 64, 3, 2, 3>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P128x128_O2: launch_gemm_pipe<T, 2, 2, 2, 2, 64, 4, 2, 2>(out, A, W, bias, M, N, K, 4, 1, s); break;
-        case P128x256_O4: launch_gemm_pipe<T, 2, 4, 2, 2, 64, 3, 2, 4>(out, A, W, bias, M, N, K, 8, 1, s); break;
-        case P256x128_S3G: launch_gemm_pipe<T, 4, 2, 2, 2, 128, 3, 2>(out, A, W, bias, M, N, K, 8, 1, s); break;
+        case S32: launch_skinny<T>(out, nullptr, A, W, bias, res, M, N, K, 1, epi, s); break;
+        // launch_gemm_cfg<T, WM, WN, TM, TN, BK>(..., group_m, remap, s, epi, res)
+        case R64x64: launch_gemm_cfg<T, 2, 2, 1, 1, BK>(out, A, W, bias, M, N, K, 4, 1, s, epi, res); break;
+        case R64x128: launch_gemm_cfg<T, 2, 2, 1, 2, BK>(out, A, W, bias, M, N, K, 8, 1, s, epi, res); break;
+        case R128x96: launch_gemm_cfg<T, 4, 1, 1, 3, BK>(out, A, W, bias, M, N, K, 8, 1, s, epi, res); break;
+        // launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SCHED, WPE>(..., group_m, remap, s, epi, res)
+#define PIPE(WM, WN, TM, TN, RB, S, SC, WPE, G, R) \
+    launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SC, WPE>(out, A, W, bias, M, N, K, G, R, s, epi, res)
+        case P128x96_S4: PIPE(4, 1, 1, 3, 128, 4, 4, 0, 8, 1); break;
+        case P128x96_S5: PIPE(4, 1, 1, 3, 128, 5, 4, 0, 8, 1); break;
+        case P256x128_S3A: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 1, 0); break;
+        case P128x128_O2: PIPE(2, 2, 2, 2, 64, 4, 2, 2, 4, 1); break;
+        case P128x128_O3: PIPE(2, 2, 2, 2, 64, 3, 2, 3, 8, 1); break;
+        case P128x256_O4: PIPE(2, 4, 2, 2, 64, 3, 2, 4, 8, 1); break;
+        case P256x128_S3G: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 8, 1); break;
         default:
             if (N >= 16384)  // vocabulary: column sweep within each row band
-                launch_gemm_pipe<T, 4, 4, 2, 2, 64, 3, 2>(out, A, W, bias, M, N, K, 1, 0, s);
+                PIPE(4, 4, 2, 2, 64, 3, 2, 0, 1, 0);
             else
-                launch_gemm_pipe<T, 4, 4, 2, 2, 64, 3, 2>(out, A, W, bias, M, N, K, 4, 1, s);
+                PIPE(4, 4, 2, 2, 64, 3, 2, 0, 4, 1);
             break;
+#undef PIPE
     }
 }
 
@@ -107,15 +112,21 @@ const char* matmul_config_name(int N, int C, int OC, int dtype) {
     return g_cfg_name;
 }
 
+// out = epi(inp W^T + bias [, res]); res may alias out (EPI_BIAS_RESIDUAL).
+int launch_matmul_epi(void* out, const void* inp, const void* weight, const void* bias, const void* res, int N,
+                      int C, int OC, int epi, int dtype, hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_gemm_t<bf16>((bf16*)out, (const bf16*)inp, (const bf16*)weight, (const bf16*)bias,
+                            (const bf16*)res, N, OC, C, dtype, epi, s);
+    else
+        launch_gemm_t<float>((float*)out, (const float*)inp, (const float*)weight, (const float*)bias,
+                             (const float*)res, N, OC, C, dtype, epi, s);
+    return launch_status();
+}
+
 int launch_matmul(void* out, const void* inp, const void* weight, const void* bias, int N, int C,
                   int OC, int dtype, hipStream_t s) {
-    if (dtype == GPT2_BF16)
-        launch_gemm_t<bf16>((bf16*)out, (const bf16*)inp, (const bf16*)weight, (const bf16*)bias, N,
-                            OC, C, dtype, s);
-    else
-        launch_gemm_t<float>((float*)out, (const float*)inp, (const float*)weight,
-                             (const float*)bias, N, OC, C, dtype, s);
-    return launch_status();
+    return launch_matmul_epi(out, inp, weight, bias, nullptr, N, C, OC, EPI_BIAS, dtype, s);
 }
 
 // Decode-step GEMM on at most 32 rows (K % 8 == 0). part == nullptr:
@@ -128,11 +139,11 @@ int launch_skinny_gemm(void* out, float* part, const void* inp, const void* weig
     if (M < 1 || M > 32 || K % 8 || splits < 1 || (part ? out != nullptr : (out == nullptr || splits != 1)))
         return GPT2_ERR_INVALID_ARGUMENT;
     if (dtype == GPT2_BF16)
-        launch_skinny<bf16>((bf16*)out, part, (const bf16*)inp, (const bf16*)weight, (const bf16*)bias, M, N, K,
-                            splits, epi, s);
+        launch_skinny<bf16>((bf16*)out, part, (const bf16*)inp, (const bf16*)weight, (const bf16*)bias, nullptr,
+                            M, N, K, splits, epi, s);
     else
-        launch_skinny<float>((float*)out, part, (const float*)inp, (const float*)weight, (const float*)bias, M,
-                             N, K, splits, epi, s);
+        launch_skinny<float>((float*)out, part, (const float*)inp, (const float*)weight, (const float*)bias,
+                             nullptr, M, N, K, splits, epi, s);
     return launch_status();
 }
 
@@ -146,8 +157,6 @@ int skinny_split_count(int K, int N, int es) {
     while (s < kMaxSplits && tiles * s * 2 <= 256 && chunks >= 4 * s) s *= 2;
     return s;
 }
-
-int launch_gelu(void*, const void*, int64_t, int, hipStream_t);
 
 }  // namespace gpt2
 
@@ -169,7 +178,7 @@ extern "C" int matmul_splitk_forward(float* part, const void* inp, const void* w
     const int rc = check_linear(part, inp, weight, N, C, OC, dtype);
     if (rc <= 0) return rc;
     if (N > 32) return GPT2_ERR_UNSUPPORTED;
-    return launch_skinny_gemm(nullptr, part, inp, weight, nullptr, N, C, OC, splits, SKINNY_BIAS, dtype,
+    return launch_skinny_gemm(nullptr, part, inp, weight, nullptr, N, C, OC, splits, EPI_BIAS, dtype,
                               (hipStream_t)stream);
 }
 
@@ -182,11 +191,17 @@ extern "C" int matmul_gelu_forward(void* out, const void* inp, const void* weigh
                                    int C, int OC, int dtype, void* stream) {
     const int rc = check_linear(out, inp, weight, N, C, OC, dtype);
     if (rc <= 0) return rc;
-    const hipStream_t s = (hipStream_t)stream;
-    if (N <= 32)
-        return launch_skinny_gemm(out, nullptr, inp, weight, bias, N, C, OC, 1, SKINNY_BIAS_GELU, dtype, s);
-    const int r = launch_matmul(out, inp, weight, bias, N, C, OC, dtype, s);
-    return r != GPT2_OK ? r : launch_gelu(out, out, (int64_t)N * OC, dtype, s);
+    return launch_matmul_epi(out, inp, weight, bias, nullptr, N, C, OC, EPI_BIAS_GELU, dtype, (hipStream_t)stream);
+}
+
+extern "C" int matmul_residual_forward(void* out, const void* inp, const void* weight, const void* bias,
+                                       const void* res, int N, int C, int OC, int dtype, void* stream) {
+    const int rc = check_linear(out, inp, weight, N, C, OC, dtype);
+    if (rc <= 0) return rc;
+    if (!res) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!aligned16(res)) return GPT2_ERR_UNSUPPORTED;
+    return launch_matmul_epi(out, inp, weight, bias, res, N, C, OC, EPI_BIAS_RESIDUAL, dtype,
+                             (hipStream_t)stream);
 }
 
 extern "C" int matmul_forward(void* out, const void* inp, const void* weight, const void* bias,

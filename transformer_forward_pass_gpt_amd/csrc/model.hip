@@ -7,7 +7,10 @@
 // then lnf, logits against the tied token embedding, vocabulary softmax.
 // The steps are those of ECE408 Final Project - GPT-2, Milestone 1 (kernel
 // table); llm.c "State of the Union [April 22, 2024]" (step breakdown) splits
-// the same pass into encoder, forward blocks and classifier.
+// the same pass into encoder, forward blocks and classifier. GELU and the two
+// residual adds run in the epilogues of the fc, attproj and fcproj GEMMs
+// (the kernel-fusion item of the llm.c "big stones" list), bit-identical to
+// the separate kernels: 7L + 4 launches.
 #include "common.h"
 
 namespace gpt2 {
@@ -24,12 +27,12 @@ int launch_status() {
 }
 
 int launch_encoder(void*, const int32_t*, const void*, const void*, int, int, int, int, hipStream_t);
-int launch_residual(void*, const void*, const void*, int64_t, int, hipStream_t);
-int launch_gelu(void*, const void*, int64_t, int, hipStream_t);
 int launch_layernorm(void*, float*, float*, const void*, const void*, const void*, int, int, float,
                      int, hipStream_t);
 int launch_softmax(void*, const void*, int, int, int, int, hipStream_t);
 int launch_matmul(void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
+int launch_matmul_epi(void*, const void*, const void*, const void*, const void*, int, int, int, int, int,
+                      hipStream_t);
 int launch_attention(void*, const void*, int, int, int, int, int, hipStream_t);
 int launch_attention_decode(void*, const void*, void*, void*, int, int, int, int, int, int, float*,
                             hipStream_t);
@@ -98,7 +101,7 @@ static inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 // Workspace: residual stream x [N,C], LayerNorm output [N,C], qkv [N,3C],
 // attention output [N,C], projection output [N,C], MLP hidden [N,4C].
 struct Workspace {
-    char *x, *ln, *qkv, *att, *tmp, *fc;
+    char *x, *ln, *qkv, *att, *fc;
     float* part;
     int64_t bytes;
 };
@@ -110,7 +113,6 @@ static Workspace carve(char* base, int64_t N, int64_t C, int es, int64_t part_by
     w.ln = take(N * C * es);
     w.qkv = take(N * 3 * C * es);
     w.att = take(N * C * es);
-    w.tmp = take(N * C * es);
     w.fc = take(N * 4 * C * es);
     w.part = (float*)take(part_bytes);
     w.bytes = o;
@@ -179,17 +181,17 @@ extern "C" int gpt2_forward(void* logits, void* probs, const int32_t* tokens, co
         CHECK(launch_matmul(w.qkv, w.ln, at(po.qkv_w + l * 3 * C64 * C64), at(po.qkv_b + l * 3 * C64),
                             n, C, 3 * C, dt, s));
         CHECK(launch_attention(w.att, w.qkv, B, T, C, cfg->NH, dt, s));
-        CHECK(launch_matmul(w.tmp, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), n, C, C,
-                            dt, s));
-        CHECK(launch_residual(w.x, w.x, w.tmp, N * C64, dt, s));
+        // x += attproj(att), the residual add in the GEMM epilogue
+        CHECK(launch_matmul_epi(w.x, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), w.x, n, C, C,
+                                EPI_BIAS_RESIDUAL, dt, s));
         CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln2_g + l * C64),
                                at(po.ln2_b + l * C64), n, C, cfg->ln_eps, dt, s));
-        CHECK(launch_matmul(w.fc, w.ln, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), n,
-                            C, 4 * C, dt, s));
-        CHECK(launch_gelu(w.fc, w.fc, N * 4 * C64, dt, s));
-        CHECK(launch_matmul(w.tmp, w.fc, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), n,
-                            4 * C, C, dt, s));
-        CHECK(launch_residual(w.x, w.x, w.tmp, N * C64, dt, s));
+        // fc = gelu(fc(ln)), GELU in the GEMM epilogue
+        CHECK(launch_matmul_epi(w.fc, w.ln, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), nullptr,
+                                n, C, 4 * C, EPI_BIAS_GELU, dt, s));
+        // x += fcproj(fc)
+        CHECK(launch_matmul_epi(w.x, w.fc, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), w.x, n,
+                                4 * C, C, EPI_BIAS_RESIDUAL, dt, s));
     }
     CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.lnf_g), at(po.lnf_b), n, C,
                            cfg->ln_eps, dt, s));
@@ -236,19 +238,19 @@ extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens
                                dt, s));
         for (int l = 0; l < L; l++) {
             CHECK(launch_skinny_gemm(w.qkv, nullptr, w.ln, at(po.qkv_w + l * 3 * C64 * C64),
-                                     at(po.qkv_b + l * 3 * C64), B, C, 3 * C, 1, SKINNY_BIAS, dt, s));
+                                     at(po.qkv_b + l * 3 * C64), B, C, 3 * C, 1, EPI_BIAS, dt, s));
             CHECK(launch_attention_decode(w.att, w.qkv, (char*)kcache + l * layer_elems * es,
                                           (char*)vcache + l * layer_elems * es, B, pos, cfg->maxT, C, NH,
                                           dt, w.part, s));
             CHECK(launch_skinny_gemm(nullptr, w.part, w.att, at(po.ap_w + l * C64 * C64), nullptr, B, C, C,
-                                     s_ap, SKINNY_BIAS, dt, s));
+                                     s_ap, EPI_BIAS, dt, s));
             CHECK(launch_residual_layernorm(w.ln, w.x, w.part, s_ap, at(po.ap_b + l * C64),
                                             at(po.ln2_g + l * C64), at(po.ln2_b + l * C64), B, C,
                                             cfg->ln_eps, dt, s));
             CHECK(launch_skinny_gemm(w.fc, nullptr, w.ln, at(po.fc_w + l * 4 * C64 * C64),
-                                     at(po.fc_b + l * 4 * C64), B, C, 4 * C, 1, SKINNY_BIAS_GELU, dt, s));
+                                     at(po.fc_b + l * 4 * C64), B, C, 4 * C, 1, EPI_BIAS_GELU, dt, s));
             CHECK(launch_skinny_gemm(nullptr, w.part, w.fc, at(po.fp_w + l * 4 * C64 * C64), nullptr, B,
-                                     4 * C, C, s_fp, SKINNY_BIAS, dt, s));
+                                     4 * C, C, s_fp, EPI_BIAS, dt, s));
             const bool last = l == L - 1;
             CHECK(launch_residual_layernorm(w.ln, w.x, w.part, s_fp, at(po.fp_b + l * C64),
                                             at(last ? po.lnf_g : po.ln1_g + (l + 1) * C64),
@@ -267,17 +269,14 @@ extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens
         CHECK(launch_attention_decode(w.att, w.qkv, (char*)kcache + l * layer_elems * es,
                                       (char*)vcache + l * layer_elems * es, B, pos, cfg->maxT, C, NH,
                                       dt, w.part, s));
-        CHECK(launch_matmul(w.tmp, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), B, C, C,
-                            dt, s));
-        CHECK(launch_residual(w.x, w.x, w.tmp, B * C64, dt, s));
+        CHECK(launch_matmul_epi(w.x, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), w.x, B, C, C,
+                                EPI_BIAS_RESIDUAL, dt, s));
         CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln2_g + l * C64),
                                at(po.ln2_b + l * C64), B, C, cfg->ln_eps, dt, s));
-        CHECK(launch_matmul(w.fc, w.ln, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), B,
-                            C, 4 * C, dt, s));
-        CHECK(launch_gelu(w.fc, w.fc, B * 4 * C64, dt, s));
-        CHECK(launch_matmul(w.tmp, w.fc, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), B,
-                            4 * C, C, dt, s));
-        CHECK(launch_residual(w.x, w.x, w.tmp, B * C64, dt, s));
+        CHECK(launch_matmul_epi(w.fc, w.ln, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), nullptr,
+                                B, C, 4 * C, EPI_BIAS_GELU, dt, s));
+        CHECK(launch_matmul_epi(w.x, w.fc, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), w.x, B,
+                                4 * C, C, EPI_BIAS_RESIDUAL, dt, s));
     }
     CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.lnf_g), at(po.lnf_b), B, C,
                            cfg->ln_eps, dt, s));
