@@ -12,9 +12,10 @@ for each of 32 sequences against a prefilled key/value cache.
 
 Besides the end-to-end rate it times every kernel of one forward with HIP
 events (the same launches gpt2_forward makes, issued one entry at a time on
-the same stream, queued behind a GPU spin so that they run back to back) to
-report the dominant kernel against its roofline, and it times the CPU oracle
-on a bounded sample of the same workload.
+the same stream, one event between consecutive launches; for the decode step,
+whose kernels are shorter than a host launch, queued behind a GPU spin so they
+run back to back) to report the dominant kernel against its roofline, and it
+times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -166,12 +167,12 @@ class Bench:
                 fn = lambda: G.matmul_forward(out, inp, wt, bias)  # noqa: E731
             name = G.matmul_kernel_config(M, K, Nc, w.dtype) + ("+" + epi if epi else "")
             timed("gemm", name, fn, 2.0 * M * Nalg * K, 0.0, "gemm_" + tag + ("+" + epi if epi else ""))
+        # Forward kernels run for tens of microseconds or more, longer than a
+        # host launch, so the launches queue up by themselves; no GPU spin
+        # (it costs the following kernels a few percent of clock).
         all_runs = []
-        host_ms = 50.0
-        for _ in range(reps + 1):  # the first pass measures the host enqueue time
+        for _ in range(reps + 1):  # the first pass warms up and is dropped
             recs.clear()
-            self.gpu_hold(1.2 * host_ms)
-            t0 = time.perf_counter()
             timed("hbm", "encoder", lambda: G.encoder_forward(x.view(B, T, C), self.tokens, P("wte"), P("wpe")),
                   0.0, 4 * N + 2 * N * C * es + T * C * es)
             for l in range(L):
@@ -190,7 +191,6 @@ class Bench:
             gemm(logits, ln, P("wte"), None, N, C, w.Vp, w.V, "logits")
             timed("hbm", "softmax", lambda: G.softmax_forward(probs, logits, w.V), 0.0,
                   N * w.V * es + N * w.Vp * es)
-            host_ms = (time.perf_counter() - t0) * 1e3
             torch.cuda.synchronize()
             all_runs.append([r[:4] + [r[4].elapsed_time(r[5]), r[6]] for r in recs])
         all_runs = all_runs[1:]

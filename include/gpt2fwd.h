@@ -207,6 +207,34 @@ int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens, int pos,
                      const gpt2_config* cfg /* host */, int B, void* workspace,
                      int64_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ generation */
+/* Greedy choice (the next-token step of autoregressive prediction, optdl2025
+ * NanoGPT project): tokens[n] = argmax over v < V of logits[n, v], the lowest
+ * index among equal maxima; logits [N,Vp]. */
+int argmax_forward(int32_t* tokens, const void* logits, int N, int V, int Vp, int dtype, void* stream);
+
+/* Prefill for KV-cached generation: the blocks of gpt2_forward over the prompt
+ * tokens int32 [B,T] (1 <= T <= maxT), storing every layer's keys and values
+ * at positions 0..T-1 of kcache, vcache [L,B,NH,maxT,hs]; then logits [B,Vp]
+ * (and probs [B,Vp] or NULL) of the LAST position of each sequence. The
+ * workspace is gpt2_workspace_bytes(cfg, B, T). */
+int gpt2_prefill(void* logits, void* probs, const int32_t* tokens, void* kcache, void* vcache,
+                 const void* params, const gpt2_config* cfg /* host */, int B, int T,
+                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gpt2_generate needs (host call); -1 if invalid. */
+int64_t gpt2_generate_workspace_bytes(const gpt2_config* cfg /* host */, int B, int T);
+
+/* Greedy generation of n_new tokens per sequence: gpt2_prefill of the prompt
+ * [B,T], argmax_forward of its last logits -> token 0, then for i = 1..n_new-1
+ * one gpt2_decode_step at position T+i-1 on token i-1 and argmax -> token i.
+ * Everything is enqueued on the stream at once (no host round trip per
+ * token). out_tokens int32 [B,n_new]; caches as gpt2_prefill, positions
+ * 0..T+n_new-2 are written. Requires T + n_new - 1 <= maxT. */
+int gpt2_generate(int32_t* out_tokens, const int32_t* prompt, int n_new, void* kcache, void* vcache,
+                  const void* params, const gpt2_config* cfg /* host */, int B, int T,
+                  void* workspace, int64_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- status */
 const char* gpt2_status_string(int status);  /* static string, never NULL */
 int gpt2_last_hip_error(void);               /* hipError_t of this thread's last failure */

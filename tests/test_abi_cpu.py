@@ -166,3 +166,12 @@ def test_model_validation():
     assert lib.gpt2_decode_step(a, None, b, 32, c, c, c, ctypes.byref(cfg), 2, d, 1 << 30, None) \
         == G.ERR_INVALID_ARGUMENT  # pos == maxT
     assert lib.gpt2_forward(a, None, b, c, ctypes.byref(cfg), 0, 32, d, 0, None) == G.OK
+    # generation: T + n_new - 1 > maxT, T = 0, T > maxT, workspace too small, zero tokens
+    assert lib.gpt2_generate(a, b, 10, c, c, c, ctypes.byref(cfg), 2, 24, d, 1 << 30, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.gpt2_generate(a, b, 9, c, c, c, ctypes.byref(cfg), 2, 0, d, 1 << 30, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.gpt2_prefill(a, None, b, c, c, c, ctypes.byref(cfg), 2, 33, d, 1 << 30, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.gpt2_generate(a, b, 9, c, c, c, ctypes.byref(cfg), 2, 24, d, 100, None) == G.ERR_WORKSPACE_TOO_SMALL
+    assert lib.gpt2_generate(a, b, 0, c, c, c, ctypes.byref(cfg), 2, 24, d, 0, None) == G.OK
+    assert lib.argmax_forward(a, b, 4, 300, 256, 0, None) == G.ERR_INVALID_ARGUMENT  # V > Vp
+    assert G.generate_workspace_bytes(cfg, 2, 24) >= G.workspace_bytes(cfg, 2, 24)
+    assert G.generate_workspace_bytes(cfg, 2, 24) >= G.decode_workspace_bytes(cfg, 2)

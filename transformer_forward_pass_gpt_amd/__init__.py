@@ -34,7 +34,8 @@ EXPORTS = (
     "attention_decode_forward", "gpt2_decode_workspace_bytes", "gpt2_decode_step",
     "gpt2_status_string", "gpt2_last_hip_error", "matmul_kernel_config",
     "matmul_splitk_forward", "matmul_splitk_count", "matmul_gelu_forward", "residual_layernorm_forward",
-    "matmul_residual_forward",
+    "matmul_residual_forward", "argmax_forward", "gpt2_prefill", "gpt2_generate_workspace_bytes",
+    "gpt2_generate",
 )
 
 
@@ -91,6 +92,10 @@ def load_library(path: str = LIB_PATH):
             "matmul_splitk_count": (I, [I, I, I]),
             "matmul_gelu_forward": (I, [P, P, P, P, I, I, I, I, P]),
             "matmul_residual_forward": (I, [P, P, P, P, P, I, I, I, I, P]),
+            "argmax_forward": (I, [P, P, I, I, I, I, P]),
+            "gpt2_prefill": (I, [P, P, P, P, P, P, CP, I, I, P, I64, P]),
+            "gpt2_generate_workspace_bytes": (I64, [CP, I, I]),
+            "gpt2_generate": (I, [P, P, I, P, P, P, CP, I, I, P, I64, P]),
             "residual_layernorm_forward": (I, [P, P, P, I, P, P, P, I, I, F, I, P]),
         }
         for name, (res, args) in sig.items():
@@ -317,3 +322,41 @@ def gpt2_decode_step(logits, probs, tokens, pos, kcache, vcache, params, cfg: Co
         _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(params, "params"), ctypes.byref(cfg), B,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
     return logits
+
+
+# ------------------------------------------------------------------ generation
+def argmax_forward(tokens, logits, V, stream=None):
+    """tokens int32 [N] = argmax over v < V of logits [N,Vp] (lowest index on ties)."""
+    lib = load_library()
+    N, Vp = logits.shape
+    _check("argmax_forward", lib.argmax_forward(_dev(tokens, "tokens"), _dev(logits, "logits"), N, V, Vp,
+                                                _dtype_code(logits), _stream(stream)))
+    return tokens
+
+
+def gpt2_prefill(logits, probs, tokens, kcache, vcache, params, cfg: Config, workspace, stream=None):
+    """Blocks over tokens int32 [B,T], caches [L,B,NH,maxT,hs] filled at 0..T-1; logits/probs [B,Vp]
+    of the last position."""
+    lib = load_library()
+    B, T = tokens.shape
+    _check("gpt2_prefill", lib.gpt2_prefill(
+        _dev(logits, "logits"), _dev(probs, "probs"), _dev(tokens, "tokens"), _dev(kcache, "kcache"),
+        _dev(vcache, "vcache"), _dev(params, "params"), ctypes.byref(cfg), B, T, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return logits
+
+
+def generate_workspace_bytes(cfg: Config, B: int, T: int) -> int:
+    return int(load_library().gpt2_generate_workspace_bytes(ctypes.byref(cfg), B, T))
+
+
+def gpt2_generate(out_tokens, prompt, kcache, vcache, params, cfg: Config, workspace, stream=None):
+    """Greedy generation: out_tokens int32 [B,n_new] after prompt int32 [B,T]."""
+    lib = load_library()
+    B, T = prompt.shape
+    n_new = out_tokens.shape[1]
+    _check("gpt2_generate", lib.gpt2_generate(
+        _dev(out_tokens, "out_tokens"), _dev(prompt, "prompt"), n_new, _dev(kcache, "kcache"),
+        _dev(vcache, "vcache"), _dev(params, "params"), ctypes.byref(cfg), B, T, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out_tokens

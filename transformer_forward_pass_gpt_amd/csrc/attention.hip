@@ -25,6 +25,8 @@
 
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace gpt2 {
@@ -380,6 +382,38 @@ int launch_attention(void* out, const void* qkv, int B, int T, int C, int NH, in
 }
 
 bool attention_head_size_ok(int hs) { return hs == 16 || hs == 32 || hs == 64 || hs == 128; }
+
+// ------------------------------------------------------------- cache store
+// Prefill: the keys and values of positions 0..T-1 (the k and v thirds of
+// qkv [B,T,3C]) into one layer's caches [B,NH,maxT,hs], the layout the decode
+// step reads. One 16-byte vector per thread, grid-stride.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_store_kernel(T* __restrict__ kc, T* __restrict__ vc,
+                                                       const T* __restrict__ qkv, int B, int Tn, int C, int NH,
+                                                       int maxT, int64_t nvec) {
+    constexpr int VE = Vec<T>::N;
+    const int hs = C / NH, cv = C / VE;
+    for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256) {
+        const int64_t row = i / (2 * cv);  // b*T + t
+        const int rem = (int)(i - row * 2 * cv), which = rem / cv, c = (rem % cv) * VE;
+        const int b = (int)(row / Tn), t = (int)(row % Tn), h = c / hs, d = c % hs;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qkv + row * 3 * C + (1 + which) * C + c);
+        T* dst = (which ? vc : kc) + (((int64_t)b * NH + h) * maxT + t) * hs + d;
+        *reinterpret_cast<u32x4*>(dst) = v;
+    }
+}
+
+int launch_kv_store(void* kc, void* vc, const void* qkv, int B, int Tn, int C, int NH, int maxT, int dtype,
+                    hipStream_t s) {
+    const int64_t nvec = (int64_t)B * Tn * 2 * C / (dtype == GPT2_BF16 ? 8 : 4);
+    const unsigned grid = (unsigned)std::min<int64_t>((nvec + 255) / 256, 2048);
+    if (dtype == GPT2_BF16)
+        kv_store_kernel<bf16><<<grid, 256, 0, s>>>((bf16*)kc, (bf16*)vc, (const bf16*)qkv, B, Tn, C, NH, maxT, nvec);
+    else
+        kv_store_kernel<float><<<grid, 256, 0, s>>>((float*)kc, (float*)vc, (const float*)qkv, B, Tn, C, NH, maxT,
+                                                    nvec);
+    return launch_status();
+}
 
 // ------------------------------------------------------------------ decode
 // One new query per sequence against a KV cache (optdl2025 NanoGPT project:

@@ -2,6 +2,8 @@
 // MFMA GEMM of gemm.h with a tile shape chosen per problem size.
 #include <stdio.h>
 
+#include <type_traits>
+
 #include "gemm.h"
 
 namespace gpt2 {
@@ -91,14 +93,20 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
         case P128x96_S5: PIPE(4, 1, 1, 3, 128, 5, 4, 0, 8, 1); break;
         case P256x128_S3A: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 1, 0); break;
         case P128x128_O2: PIPE(2, 2, 2, 2, 64, 4, 2, 2, 4, 1); break;
-        case P128x128_O3: PIPE(2, 2, 2, 2, 64, 3, 2, 3, 8, 1); break;
-        case P128x256_O4: PIPE(2, 4, 2, 2, 64, 3, 2, 4, 8, 1); break;
-        case P256x128_S3G: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 8, 1); break;
         default:
-            if (N >= 16384)  // vocabulary: column sweep within each row band
-                PIPE(4, 4, 2, 2, 64, 3, 2, 0, 1, 0);
-            else
-                PIPE(4, 4, 2, 2, 64, 3, 2, 0, 4, 1);
+            if constexpr (std::is_same<T, bf16>::value) {  // the bf16-only shapes (choose_pipe)
+                switch (choose_cfg(M, N, K, dtype)) {
+                    case P128x128_O3: PIPE(2, 2, 2, 2, 64, 3, 2, 3, 8, 1); break;
+                    case P128x256_O4: PIPE(2, 4, 2, 2, 64, 3, 2, 4, 8, 1); break;
+                    case P256x128_S3G: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 8, 1); break;
+                    default:
+                        if (N >= 16384)  // vocabulary: column sweep within each row band
+                            PIPE(4, 4, 2, 2, 64, 3, 2, 0, 1, 0);
+                        else
+                            PIPE(4, 4, 2, 2, 64, 3, 2, 0, 4, 1);
+                        break;
+                }
+            }
             break;
 #undef PIPE
     }

@@ -40,6 +40,9 @@ int64_t decode_workspace_bytes(int B, int C, int NH, int maxT);
 bool attention_head_size_ok(int hs);
 int launch_skinny_gemm(void*, float*, const void*, const void*, const void*, int, int, int, int, int, int,
                        hipStream_t);
+int launch_kv_store(void*, void*, const void*, int, int, int, int, int, int, hipStream_t);
+int launch_argmax(int32_t*, int32_t*, int, const void*, int, int, int, int, hipStream_t);
+int launch_layernorm_rows(void*, const void*, int64_t, const void*, const void*, int, int, float, int, hipStream_t);
 int launch_residual_layernorm(void*, void*, const float*, int, const void*, const void*, const void*, int, int,
                               float, int, hipStream_t);
 
@@ -152,6 +155,42 @@ extern "C" int64_t gpt2_workspace_bytes(const gpt2_config* cfg, int B, int T) {
     return carve(nullptr, (int64_t)B * T, cfg->C, elem_size(cfg->dtype), 0).bytes;
 }
 
+// Embedding and the L blocks over B x T tokens; the residual stream ends in
+// w.x. With kcache/vcache ([L,B,NH,kv_maxT,hs]) the keys and values of every
+// layer are also stored at positions 0..T-1 (prefill).
+static int run_blocks(const Workspace& w, const int32_t* tokens, const char* P, const ParamOffsets& po,
+                      const gpt2_config& cf, int B, int T, void* kcache, void* vcache, int kv_maxT, hipStream_t s) {
+    const gpt2_config* cfg = &cf;
+    const int C = cfg->C, L = cfg->L, dt = cfg->dtype, es = elem_size(dt);
+    auto at = [&](int64_t off) { return (const void*)(P + off * es); };
+    const int n = B * T;
+    const int64_t C64 = C;
+    const int64_t layer_elems = (int64_t)B * cfg->NH * kv_maxT * (C / cfg->NH);
+    CHECK(launch_encoder(w.x, tokens, at(po.wte), at(po.wpe), B, T, C, dt, s));
+    for (int l = 0; l < L; l++) {
+        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln1_g + l * C64),
+                               at(po.ln1_b + l * C64), n, C, cfg->ln_eps, dt, s));
+        CHECK(launch_matmul(w.qkv, w.ln, at(po.qkv_w + l * 3 * C64 * C64), at(po.qkv_b + l * 3 * C64),
+                            n, C, 3 * C, dt, s));
+        if (kcache)
+            CHECK(launch_kv_store((char*)kcache + l * layer_elems * es, (char*)vcache + l * layer_elems * es, w.qkv,
+                                  B, T, C, cfg->NH, kv_maxT, dt, s));
+        CHECK(launch_attention(w.att, w.qkv, B, T, C, cfg->NH, dt, s));
+        // x += attproj(att), the residual add in the GEMM epilogue
+        CHECK(launch_matmul_epi(w.x, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), w.x, n, C, C,
+                                EPI_BIAS_RESIDUAL, dt, s));
+        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln2_g + l * C64),
+                               at(po.ln2_b + l * C64), n, C, cfg->ln_eps, dt, s));
+        // fc = gelu(fc(ln)), GELU in the GEMM epilogue
+        CHECK(launch_matmul_epi(w.fc, w.ln, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), nullptr,
+                                n, C, 4 * C, EPI_BIAS_GELU, dt, s));
+        // x += fcproj(fc)
+        CHECK(launch_matmul_epi(w.x, w.fc, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), w.x, n,
+                                4 * C, C, EPI_BIAS_RESIDUAL, dt, s));
+    }
+    return GPT2_OK;
+}
+
 extern "C" int gpt2_forward(void* logits, void* probs, const int32_t* tokens, const void* params,
                             const gpt2_config* cfg, int B, int T, void* workspace,
                             int64_t workspace_bytes, void* stream) {
@@ -172,27 +211,8 @@ extern "C" int gpt2_forward(void* logits, void* probs, const int32_t* tokens, co
     auto at = [&](int64_t off) { return (const void*)(P + off * es); };
     hipStream_t s = (hipStream_t)stream;
     const int n = (int)N;
-    const int64_t C64 = C;
 
-    CHECK(launch_encoder(w.x, tokens, at(po.wte), at(po.wpe), B, T, C, dt, s));
-    for (int l = 0; l < L; l++) {
-        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln1_g + l * C64),
-                               at(po.ln1_b + l * C64), n, C, cfg->ln_eps, dt, s));
-        CHECK(launch_matmul(w.qkv, w.ln, at(po.qkv_w + l * 3 * C64 * C64), at(po.qkv_b + l * 3 * C64),
-                            n, C, 3 * C, dt, s));
-        CHECK(launch_attention(w.att, w.qkv, B, T, C, cfg->NH, dt, s));
-        // x += attproj(att), the residual add in the GEMM epilogue
-        CHECK(launch_matmul_epi(w.x, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), w.x, n, C, C,
-                                EPI_BIAS_RESIDUAL, dt, s));
-        CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln2_g + l * C64),
-                               at(po.ln2_b + l * C64), n, C, cfg->ln_eps, dt, s));
-        // fc = gelu(fc(ln)), GELU in the GEMM epilogue
-        CHECK(launch_matmul_epi(w.fc, w.ln, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), nullptr,
-                                n, C, 4 * C, EPI_BIAS_GELU, dt, s));
-        // x += fcproj(fc)
-        CHECK(launch_matmul_epi(w.x, w.fc, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), w.x, n,
-                                4 * C, C, EPI_BIAS_RESIDUAL, dt, s));
-    }
+    CHECK(run_blocks(w, tokens, P, po, *cfg, B, T, nullptr, nullptr, 0, s));
     CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.lnf_g), at(po.lnf_b), n, C,
                            cfg->ln_eps, dt, s));
     CHECK(launch_matmul(logits, w.ln, at(po.wte), nullptr, n, C, cfg->Vp, dt, s));
@@ -206,26 +226,13 @@ extern "C" int64_t gpt2_decode_workspace_bytes(const gpt2_config* cfg, int B) {
         .bytes;
 }
 
-extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens, int pos,
-                                void* kcache, void* vcache, const void* params,
-                                const gpt2_config* cfg, int B, void* workspace,
-                                int64_t workspace_bytes, void* stream) {
-    if (!config_ok(cfg) || B < 0) return GPT2_ERR_INVALID_ARGUMENT;
-    if (B == 0) return GPT2_OK;
-    if (!logits || !tokens || !params || !kcache || !vcache || !workspace || pos < 0 ||
-        pos >= cfg->maxT)
-        return GPT2_ERR_INVALID_ARGUMENT;
-    if (!config_supported(cfg) || !aligned16(logits) || !aligned16(params) || !aligned16(kcache) ||
-        !aligned16(vcache) || !aligned16(workspace) || (probs && !aligned16(probs)))
-        return GPT2_ERR_UNSUPPORTED;
-    if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
+// One decode step for B sequences at position pos (arguments validated).
+static int decode_step_impl(void* logits, void* probs, const int32_t* tokens, int pos, void* kcache, void* vcache,
+                            const void* params, const gpt2_config* cfg, int B, const Workspace& w, hipStream_t s) {
     const int C = cfg->C, L = cfg->L, NH = cfg->NH, dt = cfg->dtype, es = elem_size(dt);
-    Workspace w = carve((char*)workspace, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT));
-    if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     const ParamOffsets po = param_offsets(*cfg);
     const char* P = (const char*)params;
     auto at = [&](int64_t off) { return (const void*)(P + off * es); };
-    hipStream_t s = (hipStream_t)stream;
     const int64_t C64 = C;
     const int64_t layer_elems = (int64_t)B * NH * cfg->maxT * (C / NH);
 
@@ -282,5 +289,111 @@ extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens
                            cfg->ln_eps, dt, s));
     CHECK(launch_matmul(logits, w.ln, at(po.wte), nullptr, B, C, cfg->Vp, dt, s));
     if (probs) CHECK(launch_softmax(probs, logits, B, cfg->V, cfg->Vp, dt, s));
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens, int pos,
+                                void* kcache, void* vcache, const void* params,
+                                const gpt2_config* cfg, int B, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+    if (!config_ok(cfg) || B < 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (B == 0) return GPT2_OK;
+    if (!logits || !tokens || !params || !kcache || !vcache || !workspace || pos < 0 ||
+        pos >= cfg->maxT)
+        return GPT2_ERR_INVALID_ARGUMENT;
+    if (!config_supported(cfg) || !aligned16(logits) || !aligned16(params) || !aligned16(kcache) ||
+        !aligned16(vcache) || !aligned16(workspace) || (probs && !aligned16(probs)))
+        return GPT2_ERR_UNSUPPORTED;
+    if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
+    const int C = cfg->C, NH = cfg->NH, es = elem_size(cfg->dtype);
+    Workspace w = carve((char*)workspace, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT));
+    if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    return decode_step_impl(logits, probs, tokens, pos, kcache, vcache, params, cfg, B, w, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------ generation
+// Prefill: the blocks over the prompt, storing every layer's keys and values
+// in the caches, then the logits (and probabilities) of the last position of
+// each sequence only.
+static int prefill_impl(void* logits, void* probs, const int32_t* tokens, void* kcache, void* vcache,
+                        const char* P, const gpt2_config* cfg, int B, int T, const Workspace& w, hipStream_t s) {
+    const int C = cfg->C, dt = cfg->dtype, es = elem_size(dt);
+    const ParamOffsets po = param_offsets(*cfg);
+    auto at = [&](int64_t off) { return (const void*)(P + off * es); };
+    CHECK(run_blocks(w, tokens, P, po, *cfg, B, T, kcache, vcache, cfg->maxT, s));
+    CHECK(launch_layernorm_rows(w.ln, w.x + (int64_t)(T - 1) * C * es, (int64_t)T * C, at(po.lnf_g), at(po.lnf_b),
+                                B, C, cfg->ln_eps, dt, s));
+    CHECK(launch_matmul(logits, w.ln, at(po.wte), nullptr, B, C, cfg->Vp, dt, s));
+    if (probs) CHECK(launch_softmax(probs, logits, B, cfg->V, cfg->Vp, dt, s));
+    return GPT2_OK;
+}
+
+static bool prefill_args_ok(const gpt2_config* cfg, int B, int T) {
+    return config_ok(cfg) && B >= 0 && T >= 1 && T <= cfg->maxT && (int64_t)B * T <= INT32_MAX / 4;
+}
+
+extern "C" int gpt2_prefill(void* logits, void* probs, const int32_t* tokens, void* kcache, void* vcache,
+                            const void* params, const gpt2_config* cfg, int B, int T, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+    if (!prefill_args_ok(cfg, B, T)) return GPT2_ERR_INVALID_ARGUMENT;
+    if (B == 0) return GPT2_OK;
+    if (!logits || !tokens || !kcache || !vcache || !params || !workspace || probs == logits)
+        return GPT2_ERR_INVALID_ARGUMENT;
+    if (!config_supported(cfg) || !aligned16(logits) || !aligned16(params) || !aligned16(kcache) ||
+        !aligned16(vcache) || !aligned16(workspace) || (probs && !aligned16(probs)))
+        return GPT2_ERR_UNSUPPORTED;
+    const Workspace w = carve((char*)workspace, (int64_t)B * T, cfg->C, elem_size(cfg->dtype), 0);
+    if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    return prefill_impl(logits, probs, tokens, kcache, vcache, (const char*)params, cfg, B, T, w,
+                        (hipStream_t)stream);
+}
+
+// Generation workspace: the larger of the prefill and decode carves (they are
+// used one after the other), then the last logits [B,Vp] and the token ids [B].
+struct GenLayout {
+    int64_t logits_off, tok_off, bytes;
+};
+static GenLayout gen_layout(const gpt2_config* cfg, int B, int T) {
+    const int C = cfg->C, es = elem_size(cfg->dtype);
+    const int64_t pre = carve(nullptr, (int64_t)B * T, C, es, 0).bytes;
+    const int64_t dec = carve(nullptr, B, C, es, decode_part_bytes(B, C, cfg->NH, cfg->maxT)).bytes;
+    GenLayout g;
+    g.logits_off = align256(pre > dec ? pre : dec);
+    g.tok_off = g.logits_off + align256((int64_t)B * cfg->Vp * es);
+    g.bytes = g.tok_off + align256((int64_t)B * 4);
+    return g;
+}
+
+extern "C" int64_t gpt2_generate_workspace_bytes(const gpt2_config* cfg, int B, int T) {
+    if (!prefill_args_ok(cfg, B, T)) return -1;
+    return gen_layout(cfg, B, T).bytes;
+}
+
+extern "C" int gpt2_generate(int32_t* out_tokens, const int32_t* prompt, int n_new, void* kcache, void* vcache,
+                             const void* params, const gpt2_config* cfg, int B, int T, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+    if (!prefill_args_ok(cfg, B, T) || n_new < 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (B == 0 || n_new == 0) return GPT2_OK;
+    // token i > 0 comes from the decode step at position T + i - 1 < maxT
+    if ((int64_t)T + n_new - 1 > cfg->maxT) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!out_tokens || !prompt || !kcache || !vcache || !params || !workspace) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!config_supported(cfg) || !aligned16(params) || !aligned16(kcache) || !aligned16(vcache) ||
+        !aligned16(workspace))
+        return GPT2_ERR_UNSUPPORTED;
+    const GenLayout g = gen_layout(cfg, B, T);
+    if (workspace_bytes < g.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    char* base = (char*)workspace;
+    const int C = cfg->C, es = elem_size(cfg->dtype);
+    const Workspace wp = carve(base, (int64_t)B * T, C, es, 0);
+    const Workspace wd = carve(base, B, C, es, decode_part_bytes(B, C, cfg->NH, cfg->maxT));
+    void* logits = base + g.logits_off;
+    int32_t* tok = (int32_t*)(base + g.tok_off);
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(prefill_impl(logits, nullptr, prompt, kcache, vcache, (const char*)params, cfg, B, T, wp, s));
+    CHECK(launch_argmax(tok, out_tokens, n_new, logits, B, cfg->V, cfg->Vp, cfg->dtype, s));
+    for (int i = 1; i < n_new; i++) {
+        CHECK(decode_step_impl(logits, nullptr, tok, T + i - 1, kcache, vcache, params, cfg, B, wd, s));
+        CHECK(launch_argmax(tok, out_tokens + i, n_new, logits, B, cfg->V, cfg->Vp, cfg->dtype, s));
+    }
     return GPT2_OK;
 }

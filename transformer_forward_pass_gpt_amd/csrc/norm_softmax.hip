@@ -28,12 +28,12 @@ __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, flo
                                                         const T* __restrict__ gamma,
                                                         const T* __restrict__ beta, int N, int C,
                                                         float eps, const float* __restrict__ part,
-                                                        int splits, const T* __restrict__ bias) {
+                                                        int splits, const T* __restrict__ bias, int64_t ldx) {
     constexpr int V = Vec<T>::N;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (row >= N) return;  // wave-uniform
-    T* x = inp + (int64_t)row * C;
+    T* x = inp + (int64_t)row * ldx;  // input rows ldx apart (C, or T*C to take one position per sequence)
     const int cv = C / V;
     float v[VPL][V];
     float s = 0.f;
@@ -121,13 +121,15 @@ __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, flo
 
 template <typename T, bool RES>
 static void launch_ln_t(T* out, float* mean, float* rstd, T* inp, const T* g, const T* b, int N, int C,
-                        float eps, const float* part, int splits, const T* bias, hipStream_t s) {
+                        float eps, const float* part, int splits, const T* bias, hipStream_t s, int64_t ldx = 0) {
+    if (ldx == 0) ldx = C;
     const int vpl = (C / Vec<T>::N + 63) / 64;
     // RES runs on decode-sized batches: one row per workgroup spreads them over CUs
     const int rows = RES ? 1 : 4;
     const dim3 grid((N + rows - 1) / rows), block(64 * rows);
 #define LN_LAUNCH(P) \
-    layernorm_kernel<T, P, RES><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps, part, splits, bias)
+    layernorm_kernel<T, P, RES><<<grid, block, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps, part, splits, bias, \
+                                                       ldx)
     if (vpl <= 1) LN_LAUNCH(1);
     else if (vpl <= 2) LN_LAUNCH(2);
     else if (vpl <= 3) LN_LAUNCH(3);
@@ -146,6 +148,18 @@ int launch_layernorm(void* out, float* mean, float* rstd, const void* inp, const
     else
         launch_ln_t<float, false>((float*)out, mean, rstd, (float*)inp, (const float*)gamma,
                                   (const float*)beta, N, C, eps, nullptr, 0, nullptr, s);
+    return launch_status();
+}
+
+// LayerNorm of N rows taken ldx elements apart (out rows are contiguous).
+int launch_layernorm_rows(void* out, const void* inp, int64_t ldx, const void* gamma, const void* beta, int N,
+                          int C, float eps, int dtype, hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_ln_t<bf16, false>((bf16*)out, nullptr, nullptr, (bf16*)inp, (const bf16*)gamma, (const bf16*)beta,
+                                 N, C, eps, nullptr, 0, nullptr, s, ldx);
+    else
+        launch_ln_t<float, false>((float*)out, nullptr, nullptr, (float*)inp, (const float*)gamma,
+                                  (const float*)beta, N, C, eps, nullptr, 0, nullptr, s, ldx);
     return launch_status();
 }
 
@@ -276,6 +290,56 @@ int launch_softmax(void* probs, const void* logits, int N, int V, int Vp, int dt
     return launch_status();
 }
 
+// --------------------------------------------------------------- argmax
+// Greedy next-token choice: tok[n] = argmax over v < V of logits[n, v], the
+// lowest index among equal maxima; also written to out[n * out_stride] when
+// out is given. One 256-thread workgroup per row; each thread keeps its best
+// (value, index) over a strided slice, then wavefront shuffles and LDS reduce
+// with the same tie rule, so the result does not depend on the order.
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+    if (v > bv || (v == bv && i < bi)) {
+        bv = v;
+        bi = i;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void argmax_kernel(int32_t* __restrict__ tok, int32_t* __restrict__ out,
+                                                     int out_stride, const T* __restrict__ logits, int V, int Vp) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const T* l = logits + (int64_t)row * Vp;
+    float bv = -INFINITY;
+    int bi = V;  // beats nothing: every real index is lower
+    for (int v = tid; v < V; v += 256) better(bv, bi, load_scalar(l + v), v);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        better(bv, bi, ov, oi);
+    }
+    if (lane == 0) {
+        sv[w] = bv;
+        si[w] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int i = 1; i < 4; i++) better(bv, bi, sv[i], si[i]);
+        tok[row] = bi;
+        if (out) out[(int64_t)row * out_stride] = bi;
+    }
+}
+
+int launch_argmax(int32_t* tok, int32_t* out, int out_stride, const void* logits, int N, int V, int Vp, int dtype,
+                  hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        argmax_kernel<bf16><<<N, 256, 0, s>>>(tok, out, out_stride, (const bf16*)logits, V, Vp);
+    else
+        argmax_kernel<float><<<N, 256, 0, s>>>(tok, out, out_stride, (const float*)logits, V, Vp);
+    return launch_status();
+}
+
 }  // namespace gpt2
 
 // ------------------------------------------------------------------ C ABI
@@ -308,6 +372,13 @@ extern "C" int residual_layernorm_forward(void* out, void* x, const float* part,
     if (out == x) return GPT2_ERR_INVALID_ARGUMENT;
     return launch_residual_layernorm(out, x, part, splits, bias, gamma, beta, N, C, eps, dtype,
                                      (hipStream_t)stream);
+}
+
+extern "C" int argmax_forward(int32_t* tokens, const void* logits, int N, int V, int Vp, int dtype, void* stream) {
+    if (!valid_dtype(dtype) || N < 0 || V < 0 || Vp < V) return GPT2_ERR_INVALID_ARGUMENT;
+    if (N == 0) return GPT2_OK;
+    if (!tokens || !logits || V == 0) return GPT2_ERR_INVALID_ARGUMENT;
+    return launch_argmax(tokens, nullptr, 0, logits, N, V, Vp, dtype, (hipStream_t)stream);
 }
 
 extern "C" int softmax_forward(void* probs, const void* logits, int N, int V, int Vp, int dtype,
