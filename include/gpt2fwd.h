@@ -108,6 +108,16 @@ int residual_forward(void* out, const void* a, const void* b, int64_t n, int dty
 int softmax_forward(void* probs, const void* logits, int N, int V, int Vp, int dtype,
                     void* stream);
 
+/* Softmax with cross-entropy, the whole forward of llm.c's
+ * fused_classifier_kernel3 in one pass over the logits:
+ *   losses[n] = log(sum_{v<V} exp(l[n,v] - m_n)) + m_n - l[n, targets[n]]  (fp32, [N])
+ *   probs [N,Vp] as softmax_forward, or NULL to skip writing them;
+ *   mean_loss (one fp32, nullable) = the mean of the N losses, summed in a
+ *   fixed order.
+ * targets int32 [N] must lie in [0, V) (not checked on the device). */
+int crossentropy_forward(float* losses, float* mean_loss, void* probs, const void* logits,
+                         const int32_t* targets, int N, int V, int Vp, int dtype, void* stream);
+
 /* ---------------------------------------------------------------- model */
 typedef struct {
     int L;        /* layers */

@@ -51,6 +51,7 @@ def _load():
             "oracle_gelu": (None, [P, P, I64]),
             "oracle_residual": (None, [P, P, P, I64]),
             "oracle_softmax": (None, [P, P, I, I, I]),
+            "oracle_crossentropy": (None, [P, P, P, I, I, I]),
             "oracle_param_count": (I64, [I, I, I, I]),
             "oracle_capture_count": (I64, [I, I, I, I]),
             "oracle_forward": (I, [P, P, P, P, I, I, I, I, I, I, D, I, I, P]),
@@ -144,6 +145,19 @@ def softmax(logits, V):
     N = logits.size // Vp
     out = np.empty_like(logits)
     lib.oracle_softmax(_ptr(out), _ptr(logits), N, V, Vp)
+    return out
+
+
+def crossentropy(logits, targets, V):
+    """Per-row losses [N] = log-sum-exp over v < V minus the target's logit."""
+    lib = _load()
+    logits = _f32(logits)
+    Vp = logits.shape[-1]
+    N = logits.size // Vp
+    targets = np.ascontiguousarray(targets, dtype=np.int32).reshape(N)
+    assert np.all((targets >= 0) & (targets < V))
+    out = np.empty(N, np.float32)
+    lib.oracle_crossentropy(_ptr(out), _ptr(logits), _ptr(targets), N, V, Vp)
     return out
 
 

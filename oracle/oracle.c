@@ -174,6 +174,22 @@ void oracle_softmax(float* probs, const float* logits, int N, int V, int Vp) {
     }
 }
 
+/* Cross-entropy of each row against its target token t_n (0 <= t_n < V):
+ *   loss_n = -log softmax(l_n)[t_n] = log(sum_{v<V} exp(l_v - m)) + m - l_{t_n},
+ * the log-sum-exp form (no probability is rounded before the log). The loss
+ * half of the llm.c classifier (fused_classifier_kernel3). */
+void oracle_crossentropy(float* losses, const float* logits, const int32_t* targets, int N, int V, int Vp) {
+    for (int n = 0; n < N; n++) {
+        const float* l = logits + (int64_t)n * Vp;
+        double mx = -INFINITY;
+        for (int v = 0; v < V; v++)
+            if ((double)l[v] > mx) mx = (double)l[v];
+        double sum = 0.0;
+        for (int v = 0; v < V; v++) sum += exp((double)l[v] - mx);
+        losses[n] = (float)(log(sum) + mx - (double)l[targets[n]]);
+    }
+}
+
 int64_t oracle_param_count(int L, int C, int maxT, int Vp) {
     int64_t c = C;
     return (int64_t)Vp * c + (int64_t)maxT * c + (int64_t)L * (12 * c * c + 13 * c) + 2 * c;

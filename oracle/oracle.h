@@ -43,6 +43,7 @@ void oracle_attention(float* out, const float* qkv, int B, int T, int C, int NH)
 void oracle_gelu(float* out, const float* inp, int64_t n);
 void oracle_residual(float* out, const float* a, const float* b, int64_t n);
 void oracle_softmax(float* probs, const float* logits, int N, int V, int Vp);
+void oracle_crossentropy(float* losses, const float* logits, const int32_t* targets, int N, int V, int Vp);
 
 int64_t oracle_param_count(int L, int C, int maxT, int Vp);
 /* Floats in the capture buffer of oracle_forward: N*C*(2 + 18*L), N = B*T.

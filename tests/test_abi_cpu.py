@@ -173,5 +173,9 @@ def test_model_validation():
     assert lib.gpt2_generate(a, b, 9, c, c, c, ctypes.byref(cfg), 2, 24, d, 100, None) == G.ERR_WORKSPACE_TOO_SMALL
     assert lib.gpt2_generate(a, b, 0, c, c, c, ctypes.byref(cfg), 2, 24, d, 0, None) == G.OK
     assert lib.argmax_forward(a, b, 4, 300, 256, 0, None) == G.ERR_INVALID_ARGUMENT  # V > Vp
+    assert lib.crossentropy_forward(a, None, None, b, c, 4, 300, 256, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.crossentropy_forward(a, None, b, b, c, 4, 200, 256, 0, None) == G.ERR_INVALID_ARGUMENT  # probs=logits
+    assert lib.crossentropy_forward(a, None, None, b, c, 4, 200, 252, 0, None) == G.ERR_UNSUPPORTED  # Vp % 8
+    assert lib.crossentropy_forward(None, None, None, None, None, 0, 200, 256, 0, None) == G.OK
     assert G.generate_workspace_bytes(cfg, 2, 24) >= G.workspace_bytes(cfg, 2, 24)
     assert G.generate_workspace_bytes(cfg, 2, 24) >= G.decode_workspace_bytes(cfg, 2)

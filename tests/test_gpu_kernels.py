@@ -404,6 +404,36 @@ def test_softmax(dt, N, V, Vp):
         assert np.all(np.abs(got.astype(np.float64).sum(1) - 1) <= 1e-5)
 
 
+# ----------------------------------------------------------------- cross-entropy
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,V,Vp", [(5, 256, 256), (64, 50257, 50304), (3, 1000, 1008), (130, 64, 64)])
+def test_crossentropy(dt, N, V, Vp):
+    """Per-row losses against the oracle; the probabilities written in the same
+    pass equal softmax_forward's bit for bit; the mean against the losses."""
+    announce("crossentropy", dt, N, V, Vp)
+    import torch
+    d = DT[dt]
+    x = I.random_tensor(70, (N, Vp), 2.0, d)
+    x[:, V:] = 0.0
+    t = I.random_int_tensor(71, N, 0, V - 1).astype(np.int32)
+    tx = dev(x, d)
+    losses = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    mean = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    probs = empty((N, Vp), d, fill=float("nan"))
+    G.crossentropy_forward(losses, tx, dev_int(t), V, probs=probs, mean_loss=mean)
+    got = losses.cpu().numpy()
+    ref = oracle.crossentropy(x, t, V)
+    assert np.all(np.abs(got - ref) <= 2e-5 * np.maximum(1.0, np.abs(ref)))
+    p2 = empty((N, Vp), d)
+    G.softmax_forward(p2, tx, V)
+    assert np.array_equal(host_bits(probs), host_bits(p2))
+    assert abs(float(mean.cpu()[0]) - float(got.astype(np.float64).mean())) <= 1e-6 * max(1.0, abs(got).max())
+    # losses only (no probabilities written)
+    l2 = torch.zeros(N, dtype=torch.float32, device="cuda")
+    G.crossentropy_forward(l2, tx, dev_int(t), V)
+    assert np.array_equal(l2.cpu().numpy(), got)
+
+
 # ----------------------------------------------------------------- decode attention
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("B,C,NH,maxT,pos", [(2, 256, 4, 1024, 1023), (3, 256, 4, 1024, 0),

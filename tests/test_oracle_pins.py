@@ -192,6 +192,39 @@ def test_softmax_vs_library_and_padding(oracle):
     assert np.max(np.abs(ps - p)) <= 1e-7
 
 
+# ----------------------------------------------------------------- cross-entropy
+def test_crossentropy_closed_forms_and_library(oracle):
+    r = rng(12)
+    N, V, Vp = 6, 1000, 1024
+    logits = (r.standard_normal((N, Vp)) * 2).astype(np.float32)
+    t = r.integers(0, V, N).astype(np.int32)
+    loss = oracle.crossentropy(logits, t, V)
+    ls = scipy.special.log_softmax(logits[:, :V].astype(np.float64), axis=1)
+    exp = -ls[np.arange(N), t]
+    # one fp32 rounding of a double result
+    assert np.all(np.abs(loss - exp) <= 0.5 * np.spacing(exp.astype(np.float32)) * (1 + 1e-6))
+    # equal logits: every token has probability 1/V, loss log V (any offset)
+    flat = np.full((2, Vp), 3.25, np.float32)
+    assert np.allclose(oracle.crossentropy(flat, [0, V - 1], V), np.log(V), rtol=2.0 ** -23, atol=0)
+    # padding columns are ignored; a shift of every logit changes nothing
+    l2 = logits.copy()
+    l2[:, V:] = 100.0
+    assert np.array_equal(oracle.crossentropy(l2, t, V), loss)
+    assert np.max(np.abs(oracle.crossentropy(logits + np.float32(5.0), t, V) - loss)) <= 1e-5
+    # -log of the oracle's own probability of the target
+    p = oracle.softmax(logits, V)[np.arange(N), t].astype(np.float64)
+    assert np.allclose(loss, -np.log(p), rtol=1e-6, atol=1e-7)
+    # a dominant target: loss = log(1 + (V-1) e^{-50}) ~ 1.9e-19, below the
+    # double spacing at 1, so the sum rounds to 1 and the loss to 0
+    dom = np.zeros((1, Vp), np.float32)
+    dom[0, 17] = 50.0
+    assert 0.0 <= oracle.crossentropy(dom, [17], V)[0] <= (V - 1) * np.exp(-50.0)
+    # and a target 50 below the others: loss ~ 50 + log(V - 1)
+    low = np.zeros((1, Vp), np.float32)
+    low[0, 17] = -50.0
+    assert abs(oracle.crossentropy(low, [17], V)[0] - (50.0 + np.log(V - 1 + np.exp(-50.0)))) <= 4e-6
+
+
 # ----------------------------------------------------------------- attention
 def _qkv(seed, B, T, C, std=1.0):
     return (rng(seed).standard_normal((B, T, 3 * C)) * std).astype(np.float32)

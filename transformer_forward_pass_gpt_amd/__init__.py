@@ -35,7 +35,7 @@ EXPORTS = (
     "gpt2_status_string", "gpt2_last_hip_error", "matmul_kernel_config",
     "matmul_splitk_forward", "matmul_splitk_count", "matmul_gelu_forward", "residual_layernorm_forward",
     "matmul_residual_forward", "argmax_forward", "gpt2_prefill", "gpt2_generate_workspace_bytes",
-    "gpt2_generate",
+    "gpt2_generate", "crossentropy_forward",
 )
 
 
@@ -93,6 +93,7 @@ def load_library(path: str = LIB_PATH):
             "matmul_gelu_forward": (I, [P, P, P, P, I, I, I, I, P]),
             "matmul_residual_forward": (I, [P, P, P, P, P, I, I, I, I, P]),
             "argmax_forward": (I, [P, P, I, I, I, I, P]),
+            "crossentropy_forward": (I, [P, P, P, P, P, I, I, I, I, P]),
             "gpt2_prefill": (I, [P, P, P, P, P, P, CP, I, I, P, I64, P]),
             "gpt2_generate_workspace_bytes": (I64, [CP, I, I]),
             "gpt2_generate": (I, [P, P, I, P, P, P, CP, I, I, P, I64, P]),
@@ -260,6 +261,16 @@ def residual_forward(out, a, b, stream=None):
     _check("residual_forward", lib.residual_forward(_dev(out, "out"), _dev(a, "a"), _dev(b, "b"),
                                                     a.numel(), _dtype_code(a), _stream(stream)))
     return out
+
+
+def crossentropy_forward(losses, logits, targets, V, probs=None, mean_loss=None, stream=None):
+    """losses fp32 [N] (and probs [N,Vp], mean_loss fp32 [1] when given) from logits [N,Vp]."""
+    lib = load_library()
+    N, Vp = logits.shape
+    _check("crossentropy_forward", lib.crossentropy_forward(
+        _dev(losses, "losses"), _dev(mean_loss, "mean_loss"), _dev(probs, "probs"), _dev(logits, "logits"),
+        _dev(targets, "targets"), N, V, Vp, _dtype_code(logits), _stream(stream)))
+    return losses
 
 
 def softmax_forward(probs, logits, V, stream=None):

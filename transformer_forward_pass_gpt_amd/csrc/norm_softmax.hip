@@ -207,9 +207,14 @@ __device__ __forceinline__ float block_sum(float x, float* sh) {
     return x;
 }
 
+// With targets and losses (the loss half of fused_classifier_kernel3, llm.c
+// "State of the Union", kernel summaries) the same pass also writes the
+// cross-entropy of each row, loss = log(sum_{v<V} e^{l_v - m}) + m - l_target,
+// from the max and sum it already holds; probs may then be NULL.
 template <typename T, int PT, int NT>
 __global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, const T* __restrict__ logits,
-                                                     int V, int Vp) {
+                                                     int V, int Vp, const int32_t* __restrict__ targets,
+                                                     float* __restrict__ losses) {
     constexpr int VE = Vec<T>::N;
     constexpr int NW = NT / 64;
     __shared__ float sh[NW];
@@ -244,6 +249,8 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, cons
             s += v[i][j];
         }
     s = block_sum<NW>(s, sh);
+    if (losses && threadIdx.x == 0) losses[row] = logf(s) + m - load_scalar(x + targets[row]);
+    if (!probs) return;
     const float inv = 1.0f / s;
 #pragma unroll
     for (int i = 0; i < PT; i++) {
@@ -256,29 +263,45 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, cons
     }
 }
 
+// Mean of n fp32 values in one workgroup, in a fixed order (deterministic).
+__global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out, const float* __restrict__ x, int n) {
+    __shared__ float sh[16];
+    float a = 0.f;
+    for (int i = threadIdx.x; i < n; i += 1024) a += x[i];
+    a = block_sum<16>(a, sh);
+    if (threadIdx.x == 0) *out = a / (float)n;
+}
+
 template <typename T>
-static void launch_softmax_t(T* probs, const T* logits, int N, int V, int Vp, hipStream_t s) {
+static void launch_softmax_t(T* probs, const T* logits, int N, int V, int Vp, hipStream_t s,
+                             const int32_t* targets = nullptr, float* losses = nullptr) {
     const int cv = Vp / Vec<T>::N;
     dim3 grid(N);
+#define SM_LAUNCH(P, NT) softmax_kernel<T, P, NT><<<grid, NT, 0, s>>>(probs, logits, V, Vp, targets, losses)
     if (cv <= 256) {
-        softmax_kernel<T, 1, 256><<<grid, 256, 0, s>>>(probs, logits, V, Vp);
+        SM_LAUNCH(1, 256);
         return;
     }
     const int pt = (cv + 1023) / 1024;
-    if (pt <= 1)
-        softmax_kernel<T, 1, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
-    else if (pt <= 2)
-        softmax_kernel<T, 2, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
-    else if (pt <= 4)
-        softmax_kernel<T, 4, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
-    else if (pt <= 7)
-        softmax_kernel<T, 7, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
-    else if (pt <= 13)
-        softmax_kernel<T, 13, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
-    else if (pt <= 16)
-        softmax_kernel<T, 16, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+    if (pt <= 1) SM_LAUNCH(1, 1024);
+    else if (pt <= 2) SM_LAUNCH(2, 1024);
+    else if (pt <= 4) SM_LAUNCH(4, 1024);
+    else if (pt <= 7) SM_LAUNCH(7, 1024);
+    else if (pt <= 13) SM_LAUNCH(13, 1024);
+    else if (pt <= 16) SM_LAUNCH(16, 1024);
+    else SM_LAUNCH(32, 1024);
+#undef SM_LAUNCH
+}
+
+// Softmax (probs nullable) with per-row cross-entropy, and the mean loss.
+int launch_softmax_loss(void* probs, float* losses, float* mean, const void* logits, const int32_t* targets, int N,
+                        int V, int Vp, int dtype, hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_softmax_t<bf16>((bf16*)probs, (const bf16*)logits, N, V, Vp, s, targets, losses);
     else
-        softmax_kernel<T, 32, 1024><<<grid, 1024, 0, s>>>(probs, logits, V, Vp);
+        launch_softmax_t<float>((float*)probs, (const float*)logits, N, V, Vp, s, targets, losses);
+    if (mean) mean_kernel<<<1, 1024, 0, s>>>(mean, losses, N);
+    return launch_status();
 }
 
 int launch_softmax(void* probs, const void* logits, int N, int V, int Vp, int dtype,
@@ -379,6 +402,15 @@ extern "C" int argmax_forward(int32_t* tokens, const void* logits, int N, int V,
     if (N == 0) return GPT2_OK;
     if (!tokens || !logits || V == 0) return GPT2_ERR_INVALID_ARGUMENT;
     return launch_argmax(tokens, nullptr, 0, logits, N, V, Vp, dtype, (hipStream_t)stream);
+}
+
+extern "C" int crossentropy_forward(float* losses, float* mean_loss, void* probs, const void* logits,
+                                    const int32_t* targets, int N, int V, int Vp, int dtype, void* stream) {
+    if (!valid_dtype(dtype) || N < 0 || V < 0 || Vp < V) return GPT2_ERR_INVALID_ARGUMENT;
+    if (N == 0) return GPT2_OK;
+    if (!losses || !logits || !targets || V == 0 || probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
+    if (Vp % 8 || Vp > 131072 || !aligned16(logits) || (probs && !aligned16(probs))) return GPT2_ERR_UNSUPPORTED;
+    return launch_softmax_loss(probs, losses, mean_loss, logits, targets, N, V, Vp, dtype, (hipStream_t)stream);
 }
 
 extern "C" int softmax_forward(void* probs, const void* logits, int N, int V, int Vp, int dtype,
