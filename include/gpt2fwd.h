@@ -220,7 +220,7 @@ int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens, int pos,
 /* ------------------------------------------------------------ generation */
 /* Greedy choice (the next-token step of autoregressive prediction, optdl2025
  * NanoGPT project): tokens[n] = argmax over v < V of logits[n, v], the lowest
- * index among equal maxima; logits [N,Vp]. */
+ * index among equal maxima; logits [N,Vp], Vp % 8 == 0. */
 int argmax_forward(int32_t* tokens, const void* logits, int N, int V, int Vp, int dtype, void* stream);
 
 /* Prefill for KV-cached generation: the blocks of gpt2_forward over the prompt

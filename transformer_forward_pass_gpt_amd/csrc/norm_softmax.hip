@@ -224,19 +224,18 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, cons
     const int cv = Vp / VE;
     float v[PT][VE];
     float m = -INFINITY;
+    // Every load of the row is issued before the first use: indices past the
+    // row are clamped to its last vector and masked, not branched around
+    // (a load inside a divergent branch would be waited for at the branch's end).
+#pragma unroll
+    for (int i = 0; i < PT; i++) load_vec(x + min((int)threadIdx.x + i * NT, cv - 1) * VE, v[i]);
 #pragma unroll
     for (int i = 0; i < PT; i++) {
-        int idx = threadIdx.x + i * NT;
-        if (idx < cv) {
-            load_vec(x + idx * VE, v[i]);
+        const int idx = threadIdx.x + i * NT;
 #pragma unroll
-            for (int j = 0; j < VE; j++) {
-                if (idx * VE + j >= V) v[i][j] = -INFINITY;
-                m = fmaxf(m, v[i][j]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < VE; j++) v[i][j] = -INFINITY;
+        for (int j = 0; j < VE; j++) {
+            if (idx >= cv || idx * VE + j >= V) v[i][j] = -INFINITY;
+            m = fmaxf(m, v[i][j]);
         }
     }
     m = block_max<NW>(m, sh);
@@ -317,8 +316,9 @@ int launch_softmax(void* probs, const void* logits, int N, int V, int Vp, int dt
 // Greedy next-token choice: tok[n] = argmax over v < V of logits[n, v], the
 // lowest index among equal maxima; also written to out[n * out_stride] when
 // out is given. One 256-thread workgroup per row; each thread keeps its best
-// (value, index) over a strided slice, then wavefront shuffles and LDS reduce
-// with the same tie rule, so the result does not depend on the order.
+// (value, index) over its 16-byte vectors of the row, then wavefront shuffles
+// and LDS reduce with the same tie rule, so the result does not depend on the
+// order. Vp % 8 == 0 (16-byte rows).
 __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
     if (v > bv || (v == bv && i < bi)) {
         bv = v;
@@ -332,10 +332,24 @@ __global__ __launch_bounds__(256) void argmax_kernel(int32_t* __restrict__ tok, 
     __shared__ float sv[4];
     __shared__ int si[4];
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int VE = Vec<T>::N, U = 8;
     const T* l = logits + (int64_t)row * Vp;
+    const int cv = Vp / VE;
     float bv = -INFINITY;
     int bi = V;  // beats nothing: every real index is lower
-    for (int v = tid; v < V; v += 256) better(bv, bi, load_scalar(l + v), v);
+    // U 16-byte vectors per thread in flight (indices clamped, values masked)
+    for (int base = 0; base < cv; base += 256 * U) {
+        float x[U][VE];
+#pragma unroll
+        for (int u = 0; u < U; u++) load_vec(l + min(base + u * 256 + tid, cv - 1) * VE, x[u]);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int vi = base + u * 256 + tid;
+#pragma unroll
+            for (int j = 0; j < VE; j++)
+                if (vi < cv && vi * VE + j < V) better(bv, bi, x[u][j], vi * VE + j);
+        }
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float ov = __shfl_xor(bv, o, 64);
@@ -401,6 +415,7 @@ extern "C" int argmax_forward(int32_t* tokens, const void* logits, int N, int V,
     if (!valid_dtype(dtype) || N < 0 || V < 0 || Vp < V) return GPT2_ERR_INVALID_ARGUMENT;
     if (N == 0) return GPT2_OK;
     if (!tokens || !logits || V == 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (Vp % 8 || !aligned16(logits)) return GPT2_ERR_UNSUPPORTED;
     return launch_argmax(tokens, nullptr, 0, logits, N, V, Vp, dtype, (hipStream_t)stream);
 }
 
