@@ -334,9 +334,21 @@ def summarize_kernels(recs, dtype_bf16, key=1):
     return table, roof
 
 
+# Source files that define each profiled kernel: a counter run stays valid
+# until one of them changes.
+KERNEL_SOURCES = {
+    "gemm": ("common.h", "gemm.h", "matmul.hip"),
+    "attention_decode": ("common.h", "attention.hip"),
+}
+
+
+def kernel_sources(kernel):
+    return KERNEL_SOURCES["gemm" if kernel.startswith("gemm_") else kernel]
+
+
 def load_traffic(kernel):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None if
-    there is none for this kernel or its source changed since."""
+    there is none for this kernel or its sources changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -345,17 +357,17 @@ def load_traffic(kernel):
         ent = data.get(kernel)
         if not ent:
             return None
-        if ent.get("source_sha1") != source_sha1():
+        if ent.get("source_sha1") != source_sha1(kernel_sources(kernel)):
             return None
         return ent.get("bytes_per_launch")
     except Exception:
         return None
 
 
-def source_sha1():
+def source_sha1(files):
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "transformer_forward_pass_gpt_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
