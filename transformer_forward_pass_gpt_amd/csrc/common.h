@@ -83,12 +83,14 @@ __device__ __forceinline__ void store_scalar(bf16* p, float v) { p->bits = (uint
 // GELU, tanh form: x/2 (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
 // Evaluated through the identity 1 + tanh(u) = 2 / (1 + e^{-2u}), so
 // g(x) = x / (1 + e^{-2u}): no cancellation for u << 0, and e^{-2u} = inf
-// gives the correct limit -0.
+// gives the correct limit -0. The exponential is the hardware base-2 one
+// (__expf) and the division a hardware reciprocal: a few ulp, a handful of
+// instructions (this runs in GEMM epilogues, after the matrix work).
 // (ECE408 Milestone 1, kernel table: GELU.)
 __device__ __forceinline__ float gelu_tanh(float x) {
     const float k2 = -2.0f * 0.7978845608028654f;  // -2 sqrt(2/pi)
     float u = x * (1.0f + 0.044715f * x * x);
-    return x / (1.0f + expf(k2 * u));
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(k2 * u));
 }
 
 // Reductions across the 64 lanes of a wavefront.

@@ -34,17 +34,19 @@ struct PipeCfg {
 };
 enum GemmCfg {
     S32 = 0, R64x64, R64x128, R128x96,
-    P128x96_S4, P128x96_S5, P256x128_S3A,                                 // fp32
-    P128x128_O2,                                                          // fp32 and bf16
-    P128x128_O3, P128x256_O4, P256x128_S3G, P256x256_W16,                 // bf16
+    P128x96_S4, P128x96_S5, P256x128_S3A, P128x128_O2,                    // fp32
+    P128x256_O4, P128x256_R3, P256x128_G, P128x128_R4, P128x128_O3, P256x256_W16,  // bf16
     G_NCFG
 };
 // "_p<S>" = S-stage pipeline; "_o<n>" = registers capped so n wavefronts fit per SIMD (2 or 3
-// workgroups per CU); "_w16" = 16 wavefronts per workgroup.
+// workgroups per CU); "_w16" = 16 wavefronts per workgroup; "_k128" = 128-byte k-rows per stage
+// (twice the default bf16 depth); "g" = grouped XCD-aware walk (the fp32 vocabulary tile walks
+// columns instead).
 static const PipeCfg kCfg[G_NCFG] = {
     {"skinny32", 0},          {"64x64_r", 0},          {"64x128_r", 0},         {"128x96_r", 0},
     {"128x96_p4", 128},       {"128x96_p5", 128},      {"256x128_p3", 128},     {"128x128_p4_o2", 64},
-    {"128x128_p3_o3", 64},    {"128x256_p3_o4", 64},   {"256x128_p3g", 128},    {"256x256_p3_w16", 64},
+    {"128x256_p3_o4", 64},    {"128x256_p3_k128", 128}, {"256x128_p3g", 128},
+    {"128x128_p4_k128", 128}, {"128x128_p3_o3", 64},   {"256x256_p3_w16", 64},
 };
 
 static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
@@ -54,14 +56,15 @@ static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
         if (N <= 1024) return P128x96_S4;                    // attproj
         return N >= 3072 ? P128x128_O2 : P128x96_S5;         // fc, qkv
     }
-    // bf16: K = 768 or 1024 gives each output tile only a few microseconds of
-    // MFMA work, so below the vocabulary projection the tiles are sized for
-    // two or three resident workgroups per CU (one's fill and epilogue
-    // overlap the others' math).
-    if (N >= 16384) return P256x256_W16;                       // vocabulary projection
-    if (K >= 2048) return M >= 8192 ? P256x128_S3G : P128x128_O2;  // fcproj
-    if (N <= 1024) return M >= 8192 ? P128x256_O4 : P128x128_O3;   // attproj
-    return M >= 8192 ? P128x256_O4 : P256x256_W16;             // qkv, fc
+    // bf16, chosen with operands cold in HBM, as in the forward (a pipeline
+    // tuned on cache-resident operands loses 10-30% there): wide projections
+    // use two resident 128x256 workgroups per CU or 256x256 tiles of 16
+    // wavefronts; the narrow (attproj) and deep (fcproj) ones need 128-byte
+    // k-rows per stage, twice the bytes in flight.
+    if (N >= 16384) return P256x256_W16;                        // vocabulary projection
+    if (K >= 2048) return M >= 8192 ? P256x128_G : P128x128_R4;    // fcproj
+    if (N <= 1024) return M >= 8192 ? P128x256_R3 : P128x128_O3;   // attproj
+    return M >= 8192 ? P128x256_O4 : P256x256_W16;              // qkv, fc
 }
 
 static GemmCfg choose_cfg(int M, int N, int K, int dtype) {
@@ -96,9 +99,11 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
         default:
             if constexpr (std::is_same<T, bf16>::value) {  // the bf16-only shapes (choose_pipe)
                 switch (choose_cfg(M, N, K, dtype)) {
+                    case P128x256_O4: PIPE(2, 4, 2, 2, 64, 3, 2, 4, 4, 1); break;
+                    case P128x256_R3: PIPE(2, 4, 2, 2, 128, 3, 2, 0, 4, 1); break;
+                    case P256x128_G: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 8, 1); break;
+                    case P128x128_R4: PIPE(2, 2, 2, 2, 128, 4, 2, 0, 8, 1); break;
                     case P128x128_O3: PIPE(2, 2, 2, 2, 64, 3, 2, 3, 8, 1); break;
-                    case P128x256_O4: PIPE(2, 4, 2, 2, 64, 3, 2, 4, 8, 1); break;
-                    case P256x128_S3G: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 8, 1); break;
                     default:
                         if (N >= 16384)  // vocabulary: column sweep within each row band
                             PIPE(4, 4, 2, 2, 64, 3, 2, 0, 1, 0);
