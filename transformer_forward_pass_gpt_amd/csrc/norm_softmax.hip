@@ -239,12 +239,16 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, cons
         }
     }
     m = block_max<NW>(m, sh);
+    // e^{l - m} = 2^{(l - m) log2 e} on the hardware base-2 exponential; the
+    // difference is formed first, so the argument's rounding error scales with
+    // |l - m| (tiny probabilities), not with |l|.
+    const float L2E = 1.4426950408889634f;
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < PT; i++)
 #pragma unroll
         for (int j = 0; j < VE; j++) {
-            v[i][j] = expf(v[i][j] - m);  // exp(-inf) = 0 for padding
+            v[i][j] = __builtin_amdgcn_exp2f((v[i][j] - m) * L2E);  // 2^-inf = 0 for padding
             s += v[i][j];
         }
     s = block_sum<NW>(s, sh);
