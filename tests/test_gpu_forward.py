@@ -286,3 +286,45 @@ def test_decode_batch_sizes(name, B):
         assert max_abs(host(probs), rp) <= 1e-6
     else:
         assert rel_err(host(probs), rp) <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["tiny_affine", "tiny_bf16"])
+@pytest.mark.parametrize("B,T", [(1, 1), (1, 17), (3, 5), (5, 32)])
+def test_forward_shapes(name, B, T):
+    """Degenerate and ragged shapes: a single token, one sequence, a length that
+    is not a multiple of any tile, the full context."""
+    announce("forward-shapes", name, B, T)
+    w = I.WORKLOADS[name]
+    m = Model(w)
+    rng = np.random.default_rng(800 + 10 * B + T)
+    tok = rng.integers(0, w.V, size=(B, T)).astype(np.int32)
+    logits, probs = m.forward(tok)
+    rl, rp, _ = oracle.forward(tok, m.params_np, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps)
+    check_logits(w, host(logits), rl)
+    if w.dtype == I.F32:
+        assert max_abs(host(probs), rp) <= 1e-6
+    else:
+        assert rel_err(host(probs), rp) <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["tiny_affine", "tiny_bf16"])
+def test_decode_first_position(name):
+    """Decode at position 0: attention over the step's own key only."""
+    announce("decode-pos0", name)
+    import torch
+    w = I.WORKLOADS[name]
+    params = I.make_params(w)
+    B = 3
+    tok = np.array([5, 77, 200], np.int32)
+    shape = (w.L, B, w.NH, w.maxT, w.hs)
+    kc, vc = np.zeros(shape, np.float32), np.zeros(shape, np.float32)
+    cfg = cfg_of(w)
+    tk, tv = dev(kc, w.dtype), dev(vc, w.dtype)
+    logits = empty((B, w.Vp), w.dtype, fill=float("nan"))
+    ws = torch.empty(G.decode_workspace_bytes(cfg, B), dtype=torch.uint8, device="cuda")
+    G.gpt2_decode_step(logits, None, dev_int(tok), 0, tk, tv, dev(params, w.dtype), cfg, ws)
+    rl, _ = oracle.decode_step(tok, 0, kc, vc, params, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps, probs=False)
+    check_logits(w, host(logits), rl)
+    # and the forward of the single token
+    rf, _, _ = oracle.forward(tok[:, None], params, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps, probs=False)
+    check_logits(w, host(logits), rf[:, 0])

@@ -138,3 +138,25 @@ def test_generate_greedy(name, B, T, n_new):
     tol = 2e-3 if w.dtype == I.F32 else 5e-2 * np.abs(ol).max()
     assert np.all(gap <= tol), gap.max()
     print("oracle argmax agreement %.3f" % np.mean(gap == 0))
+
+
+def test_generate_from_one_token():
+    """A one-token prompt: prefill at T = 1, then decode steps from position 1."""
+    announce("generate-T1")
+    import torch
+    w = I.WORKLOADS["tiny_affine"]
+    params = I.make_params(w)
+    B, n_new = 2, 12
+    prompt = np.array([[3], [250]], np.int32)
+    cfg = cfg_of(w)
+    shape = (w.L, B, w.NH, w.maxT, w.hs)
+    kc, vc = empty(shape, w.dtype, fill=0.0), empty(shape, w.dtype, fill=0.0)
+    out = torch.full((B, n_new), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(G.generate_workspace_bytes(cfg, B, 1), dtype=torch.uint8, device="cuda")
+    G.gpt2_generate(out, dev_int(prompt), kc, vc, dev(params, w.dtype), cfg, ws)
+    gen = out.cpu().numpy()
+    seq = np.concatenate([prompt, gen], axis=1)[:, :n_new]
+    rl, _, _ = oracle.forward(seq, params, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps, probs=False)
+    ol = rl[:, :, :w.V]
+    chosen = np.take_along_axis(ol, gen[:, :, None], axis=2)[:, :, 0]
+    assert np.all(ol.max(axis=2) - chosen <= 2e-3)
