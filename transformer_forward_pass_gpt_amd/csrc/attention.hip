@@ -66,9 +66,11 @@ __device__ __forceinline__ int vt_slot_bf16(int key) {
 // through LDS at the end, in a fixed order. Each iteration stages two key
 // blocks (the even and the odd one); when two iterations' worth fits in LDS
 // the next pair is loaded while the current one is computed.
-template <typename T, int HS>
-__global__ __launch_bounds__(512) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
-                                                        int Tn, int C, int NH, float sl2) {
+// WPE: minimum wavefronts per SIMD the registers must allow (0: none); SB:
+// single-buffered key/value staging (half the LDS).
+template <typename T, int HS, int WPE = 0, bool SB = false>
+__global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
+                                                             int Tn, int C, int NH, float sl2) {
     constexpr bool F32 = std::is_same<T, float>::value;
     constexpr int VE = Vec<T>::N;
     constexpr int DT = (HS + 31) / 32;  // 32-row tiles of O^T (head dim padded to 32)
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(512) void attention_kernel(T* __restrict__ out, con
     constexpr int LDV = kBKV + VE;  // V^T block [HSP][kBKV], 16-byte row pad
     constexpr int KSZ = kBKV * LDK, VSZ = HSP * LDV;  // elements per block
     constexpr int PAIR = 2 * (KSZ + VSZ);             // one iteration: even + odd block
-    constexpr bool DB = 2 * PAIR * (int)sizeof(T) <= 160 * 1024;  // double-buffered
+    constexpr bool DB = !SB && 2 * PAIR * (int)sizeof(T) <= 160 * 1024;  // double-buffered
     constexpr int NBUF = DB ? 2 : 1;
     constexpr int RV = HS / VE;                                  // 16-byte vectors per key row
     constexpr int NKV = (2 * kBKV * RV + 511) / 512;             // K vectors per thread
@@ -355,11 +357,20 @@ __global__ __launch_bounds__(512) void attention_kernel(T* __restrict__ out, con
     }
 }
 
+// Launch shape from on-box sweeps at the GPT-2 sizes: fp32 asks the register
+// allocator for 3 wavefronts per SIMD; bf16 grids of 768+ workgroups run
+// (head size 64) single-buffered with 3 per SIMD (two workgroups per CU hide
+// each other's staging), the rest double-buffered with one workgroup per CU.
 template <typename T, int HS>
 static void launch_attn_hs(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)HS);  // log2(e)/sqrt(hs)
     dim3 grid(B * NH, (Tn + kBQ - 1) / kBQ);
-    attention_kernel<T, HS><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2);
+    if constexpr (std::is_same<T, float>::value)
+        attention_kernel<T, HS, 3><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2);
+    else if (HS == 64 && (int64_t)grid.x * grid.y >= 768)
+        attention_kernel<T, HS, 3, HS == 64><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2);
+    else
+        attention_kernel<T, HS><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2);
 }
 
 template <typename T>
