@@ -174,11 +174,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __re
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                // residual read with the row clamped, outside the bounds branch
+                const float r = EPI == EPI_BIAS_RESIDUAL ? load_scalar(res + (int64_t)min(row, M - 1) * N + col) : 0.f;
                 if (row < M) {
                     float y = acc[i][j][v] + bv;
                     if constexpr (EPI == EPI_BIAS_GELU) y = gelu_tanh(storage_round(out, y));
-                    if constexpr (EPI == EPI_BIAS_RESIDUAL)
-                        y = storage_round(out, y) + load_scalar(res + (int64_t)row * N + col);
+                    if constexpr (EPI == EPI_BIAS_RESIDUAL) y = storage_round(out, y) + r;
                     store_scalar(out + (int64_t)row * N + col, y);
                 }
             }
@@ -419,22 +420,40 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
         __builtin_amdgcn_s_waitcnt((0xF) | (7 << 4) | (0x0 << 8) | (3 << 14));  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         constexpr int CPR = BN / VE;  // 16-byte chunks per tile row
-#pragma unroll 4
-        for (int c = tid; c < BM * CPR; c += NW * 64) {
-            const int rl = c / CPR, cv = c % CPR;
-            const int row = m0 + rl, col = n0 + cv * VE;
-            if (row < M && col < N) {
-                const u32x4 y = *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]);
-                if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+        if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+            // every residual chunk of this thread is loaded before the first
+            // add (rows and columns clamped into the matrix; out-of-range
+            // chunks are then not stored), so the loads overlap
+            constexpr int NCH = (BM * CPR + NW * 64 - 1) / (NW * 64);
+            u32x4 rv[NCH];
+#pragma unroll
+            for (int j = 0; j < NCH; j++) {
+                const int c = min(tid + j * NW * 64, BM * CPR - 1);
+                const int row = min(m0 + c / CPR, M - 1), col = min(n0 + (c % CPR) * VE, N - VE);
+                rv[j] = *reinterpret_cast<const u32x4*>(res + (int64_t)row * N + col);
+            }
+#pragma unroll
+            for (int j = 0; j < NCH; j++) {
+                const int c = tid + j * NW * 64;
+                const int rl = c / CPR, cv = c % CPR;
+                const int row = m0 + rl, col = n0 + cv * VE;
+                if (c < BM * CPR && row < M && col < N) {
                     float a[VE], r[VE];
-                    unpack_vec<T>(y, a);
-                    load_vec(res + (int64_t)row * N + col, r);
+                    unpack_vec<T>(*reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]), a);
+                    unpack_vec<T>(rv[j], r);
 #pragma unroll
                     for (int e = 0; e < VE; e++) a[e] += r[e];
                     store_vec(out + (int64_t)row * N + col, a);
-                } else {
-                    *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) = y;
                 }
+            }
+        } else {
+#pragma unroll 4
+            for (int c = tid; c < BM * CPR; c += NW * 64) {
+                const int rl = c / CPR, cv = c % CPR;
+                const int row = m0 + rl, col = n0 + cv * VE;
+                if (row < M && col < N)
+                    *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) =
+                        *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]);
             }
         }
     } else {
@@ -448,11 +467,12 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    const float r =
+                        EPI == EPI_BIAS_RESIDUAL ? load_scalar(res + (int64_t)min(row, M - 1) * N + col) : 0.f;
                     if (row < M) {
                         float y = acc[i][j][v] + bv;
                         if constexpr (EPI == EPI_BIAS_GELU) y = gelu_tanh(storage_round(out, y));
-                        if constexpr (EPI == EPI_BIAS_RESIDUAL)
-                            y = storage_round(out, y) + load_scalar(res + (int64_t)row * N + col);
+                        if constexpr (EPI == EPI_BIAS_RESIDUAL) y = storage_round(out, y) + r;
                         store_scalar(out + (int64_t)row * N + col, y);
                     }
                 }
