@@ -56,6 +56,14 @@ def _load():
             "oracle_capture_count": (I64, [I, I, I, I]),
             "oracle_forward": (I, [P, P, P, P, I, I, I, I, I, I, D, I, I, P]),
             "oracle_decode_step": (I, [P, P, P, I, P, P, P, I, I, I, I, I, I, D, I]),
+            "oracle_crossentropy_backward": (None, [P, P, P, D, I, I, I]),
+            "oracle_matmul_backward": (None, [P, P, P, P, P, P, I, I, I]),
+            "oracle_layernorm_backward": (None, [P, P, P, P, P, P, I, I, D]),
+            "oracle_gelu_backward": (None, [P, P, P, I64]),
+            "oracle_attention_lse": (None, [P, P, I, I, I, I]),
+            "oracle_attention_backward": (None, [P, P, P, I, I, I, I]),
+            "oracle_encoder_backward": (None, [P, P, P, P, I, I, I]),
+            "oracle_backward": (I, [P, P, P, P, P, I, I, I, I, I, I, D, I, I]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -216,3 +224,107 @@ def decode_step(tokens, pos, kcache, vcache, params, L, C, NH, V, Vp, maxT, eps=
     if rc != 0:
         raise RuntimeError("oracle_decode_step failed with code %d" % rc)
     return logits, pr
+
+
+# ------------------------------------------------------------------ backward
+
+
+def crossentropy_backward(logits, targets, V, dloss):
+    """dlogits [N,Vp] = dloss * (softmax - onehot(target)) on v < V, 0 in the padding."""
+    lib = _load()
+    logits = _f32(logits)
+    Vp = logits.shape[-1]
+    N = logits.size // Vp
+    targets = np.ascontiguousarray(targets, dtype=np.int32).reshape(N)
+    assert np.all((targets >= 0) & (targets < V))
+    out = np.empty_like(logits)
+    lib.oracle_crossentropy_backward(_ptr(out), _ptr(logits), _ptr(targets), float(dloss), N, V, Vp)
+    return out
+
+
+def matmul_backward(dout, x, weight):
+    """Returns (dinp [N,C], dweight [OC,C], dbias [OC]) for out = x W^T + b."""
+    lib = _load()
+    dout, x, weight = _f32(dout), _f32(x), _f32(weight)
+    OC, C = weight.shape
+    N = x.size // C
+    assert dout.size == N * OC
+    dinp = np.empty(x.shape, np.float32)
+    dw = np.empty((OC, C), np.float32)
+    db = np.empty(OC, np.float32)
+    lib.oracle_matmul_backward(_ptr(dinp), _ptr(dw), _ptr(db), _ptr(dout), _ptr(x), _ptr(weight), N, C, OC)
+    return dinp, dw, db
+
+
+def layernorm_backward(dout, x, gamma, eps=1e-5):
+    """Returns (dinp, dgamma, dbeta)."""
+    lib = _load()
+    dout, x, gamma = _f32(dout), _f32(x), _f32(gamma)
+    C = x.shape[-1]
+    N = x.size // C
+    dinp = np.empty_like(x)
+    dg = np.empty(C, np.float32)
+    db = np.empty(C, np.float32)
+    lib.oracle_layernorm_backward(_ptr(dinp), _ptr(dg), _ptr(db), _ptr(dout), _ptr(x), _ptr(gamma), N, C,
+                                  float(eps))
+    return dinp, dg, db
+
+
+def gelu_backward(x, dout):
+    lib = _load()
+    x, dout = _f32(x), _f32(dout)
+    out = np.empty_like(x)
+    lib.oracle_gelu_backward(_ptr(out), _ptr(x), _ptr(dout), x.size)
+    return out
+
+
+def attention_lse(qkv, NH):
+    """lse [B,NH,T] of the causal scaled scores."""
+    lib = _load()
+    qkv = _f32(qkv)
+    B, T, C3 = qkv.shape
+    out = np.empty((B, NH, T), np.float32)
+    lib.oracle_attention_lse(_ptr(out), _ptr(qkv), B, T, C3 // 3, NH)
+    return out
+
+
+def attention_backward(dout, qkv, NH):
+    """dqkv [B,T,3C] for y = attention(qkv) and the incoming dout [B,T,C]."""
+    lib = _load()
+    qkv, dout = _f32(qkv), _f32(dout)
+    B, T, C3 = qkv.shape
+    out = np.empty_like(qkv)
+    lib.oracle_attention_backward(_ptr(out), _ptr(dout), _ptr(qkv), B, T, C3 // 3, NH)
+    return out
+
+
+def encoder_backward(dout, tokens, Vp, maxT, dwte=None, dwpe=None):
+    """Accumulates into (copies of) dwte [Vp,C] and dwpe [maxT,C] (zeros if None)."""
+    lib = _load()
+    dout = _f32(dout)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    B, T = tokens.shape
+    C = dout.shape[-1]
+    dwte = np.zeros((Vp, C), np.float32) if dwte is None else _f32(dwte).copy()
+    dwpe = np.zeros((maxT, C), np.float32) if dwpe is None else _f32(dwpe).copy()
+    lib.oracle_encoder_backward(_ptr(dwte), _ptr(dwpe), _ptr(dout), _ptr(tokens), B, T, C)
+    return dwte, dwpe
+
+
+def backward(tokens, targets, params, L, C, NH, V, Vp, maxT, eps=1e-5):
+    """Gradient of the mean cross-entropy w.r.t. the flat parameters.
+    Returns (grads [P] float32, mean loss)."""
+    lib = _load()
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    targets = np.ascontiguousarray(targets, dtype=np.int32)
+    B, T = tokens.shape
+    assert targets.shape == (B, T) and np.all((targets >= 0) & (targets < V))
+    params = _f32(params)
+    assert params.size == param_count(L, C, maxT, Vp)
+    grads = np.empty_like(params)
+    loss = np.zeros(1, np.float32)
+    rc = lib.oracle_backward(_ptr(grads), _ptr(loss), _ptr(tokens), _ptr(targets), _ptr(params), L, C, NH, V,
+                             Vp, maxT, float(eps), B, T)
+    if rc != 0:
+        raise RuntimeError("oracle_backward failed with code %d" % rc)
+    return grads, float(loss[0])

@@ -391,3 +391,355 @@ int oracle_decode_step(float* logits, float* probs, const int32_t* tokens, int p
     free(x); free(a); free(qkv); free(y); free(f); free(g);
     return 0;
 }
+
+/* ===================================================================== backward
+ * Gradients of the same steps (the backward kernels of the llm.c training step,
+ * "State of the Union [April 22, 2024]", kernel summaries; attention after
+ * "Understand FlashAttention (II)", which asks for the backward of the standard
+ * algorithm). Each sum or dot product accumulates in double and every output
+ * is rounded to fp32 once. The derivations are the standard calculus of each
+ * forward definition above; the CPU test suite checks them against float64
+ * automatic differentiation of library operations and against central finite
+ * differences.
+ */
+
+/* Cross-entropy backward fused with the softmax (the backward half of the llm.c
+ * classifier): for the loss sum_n dloss * loss_n,
+ *   dlogits[n,v] = dloss * (p_v - [v == t_n])   for v < V,
+ * with p the softmax over the V real columns, and 0 in the padding columns. */
+void oracle_crossentropy_backward(float* dlogits, const float* logits, const int32_t* targets,
+                                  double dloss, int N, int V, int Vp) {
+    for (int n = 0; n < N; n++) {
+        const float* l = logits + (int64_t)n * Vp;
+        float* d = dlogits + (int64_t)n * Vp;
+        double mx = -INFINITY;
+        for (int v = 0; v < V; v++)
+            if ((double)l[v] > mx) mx = (double)l[v];
+        double sum = 0.0;
+        for (int v = 0; v < V; v++) sum += exp((double)l[v] - mx);
+        for (int v = 0; v < V; v++) {
+            double p = exp((double)l[v] - mx) / sum;
+            d[v] = (float)(dloss * (p - (v == targets[n] ? 1.0 : 0.0)));
+        }
+        for (int v = V; v < Vp; v++) d[v] = 0.0f;
+    }
+}
+
+/* Linear backward, for out = inp W^T + b and the incoming gradient dout [N,OC]:
+ *   dinp[n,c] = sum_o dout[n,o] W[o,c],   dW[o,c] = sum_n dout[n,o] inp[n,c],
+ *   db[o] = sum_n dout[n,o].
+ * Each output is optional (NULL) and overwritten. */
+void oracle_matmul_backward(float* dinp, float* dweight, float* dbias, const float* dout,
+                            const float* inp, const float* weight, int N, int C, int OC) {
+    if (dinp)
+        for (int n = 0; n < N; n++)
+            for (int c = 0; c < C; c++) {
+                double acc = 0.0;
+                for (int o = 0; o < OC; o++)
+                    acc += (double)dout[(int64_t)n * OC + o] * (double)weight[(int64_t)o * C + c];
+                dinp[(int64_t)n * C + c] = (float)acc;
+            }
+    if (dweight)
+        for (int o = 0; o < OC; o++)
+            for (int c = 0; c < C; c++) {
+                double acc = 0.0;
+                for (int n = 0; n < N; n++)
+                    acc += (double)dout[(int64_t)n * OC + o] * (double)inp[(int64_t)n * C + c];
+                dweight[(int64_t)o * C + c] = (float)acc;
+            }
+    if (dbias)
+        for (int o = 0; o < OC; o++) {
+            double acc = 0.0;
+            for (int n = 0; n < N; n++) acc += (double)dout[(int64_t)n * OC + o];
+            dbias[o] = (float)acc;
+        }
+}
+
+/* LayerNorm backward. With xh = (x - mu) rstd (mu, rstd recomputed from x in
+ * double exactly as oracle_layernorm defines them), y = xh gamma + beta, and
+ * g = dy gamma:
+ *   dx = rstd (g - mean_c(g) - xh mean_c(g xh)),
+ *   dgamma[c] = sum_n dy xh,   dbeta[c] = sum_n dy.
+ * (dx follows from d rstd / dx = -rstd^3 (x - mu) / C and d mu / dx = 1/C.)
+ * dinp is overwritten; dgamma and dbeta (optional) are overwritten. */
+void oracle_layernorm_backward(float* dinp, float* dgamma, float* dbeta, const float* dout,
+                               const float* inp, const float* gamma, int N, int C, double eps) {
+    double* xh = (double*)malloc(sizeof(double) * (size_t)N * (size_t)C);
+    if (!xh) return;
+    for (int n = 0; n < N; n++) {
+        const float* x = inp + (int64_t)n * C;
+        const float* dy = dout + (int64_t)n * C;
+        double s = 0.0;
+        for (int c = 0; c < C; c++) s += (double)x[c];
+        double mu = s / C, v = 0.0;
+        for (int c = 0; c < C; c++) v += ((double)x[c] - mu) * ((double)x[c] - mu);
+        double r = 1.0 / sqrt(v / C + eps);
+        double mg = 0.0, mgx = 0.0;
+        for (int c = 0; c < C; c++) {
+            double h = ((double)x[c] - mu) * r;
+            xh[(int64_t)n * C + c] = h;
+            double g = (double)dy[c] * (double)gamma[c];
+            mg += g;
+            mgx += g * h;
+        }
+        mg /= C;
+        mgx /= C;
+        for (int c = 0; c < C; c++) {
+            double h = xh[(int64_t)n * C + c];
+            double g = (double)dy[c] * (double)gamma[c];
+            dinp[(int64_t)n * C + c] = (float)(r * (g - mg - h * mgx));
+        }
+    }
+    for (int c = 0; c < C; c++) {
+        double sg = 0.0, sb = 0.0;
+        for (int n = 0; n < N; n++) {
+            double dy = (double)dout[(int64_t)n * C + c];
+            sg += dy * xh[(int64_t)n * C + c];
+            sb += dy;
+        }
+        if (dgamma) dgamma[c] = (float)sg;
+        if (dbeta) dbeta[c] = (float)sb;
+    }
+    free(xh);
+}
+
+/* GELU backward: with u = sqrt(2/pi) (x + 0.044715 x^3),
+ *   g'(x) = (1 + tanh u)/2 + (x/2)(1 - tanh^2 u) sqrt(2/pi)(1 + 3*0.044715 x^2),
+ *   dinp = dout g'(x). */
+void oracle_gelu_backward(float* dinp, const float* inp, const float* dout, int64_t n) {
+    const double k = sqrt(2.0 / M_PI);
+    for (int64_t i = 0; i < n; i++) {
+        double x = (double)inp[i];
+        double t = tanh(k * (x + 0.044715 * x * x * x));
+        double d = 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * k * (1.0 + 3.0 * 0.044715 * x * x);
+        dinp[i] = (float)((double)dout[i] * d);
+    }
+}
+
+/* The natural log-sum-exp of every causal score row, lse[b,h,t] =
+ * log sum_{j<=t} exp(S[t][j]) with S as in oracle_attention: what a tiled
+ * (FlashAttention) forward keeps per query row so its backward can rebuild P
+ * as exp(S - lse). */
+void oracle_attention_lse(float* lse, const float* qkv, int B, int T, int C, int NH) {
+    int hs = C / NH;
+    double scale = 1.0 / sqrt((double)hs);
+    double* s = (double*)malloc(sizeof(double) * (size_t)T);
+    if (!s) return;
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < NH; h++)
+            for (int t = 0; t < T; t++) {
+                const float* q = qkv + ((int64_t)b * T + t) * 3 * C + h * hs;
+                double mx = -INFINITY;
+                for (int j = 0; j <= t; j++) {
+                    const float* k = qkv + ((int64_t)b * T + j) * 3 * C + C + h * hs;
+                    double d = 0.0;
+                    for (int e = 0; e < hs; e++) d += (double)q[e] * (double)k[e];
+                    s[j] = d * scale;
+                    if (s[j] > mx) mx = s[j];
+                }
+                double sum = 0.0;
+                for (int j = 0; j <= t; j++) sum += exp(s[j] - mx);
+                lse[((int64_t)b * NH + h) * T + t] = (float)(mx + log(sum));
+            }
+    free(s);
+}
+
+/* Attention backward, the backward of the standard algorithm (materialised S
+ * and P, "Understand FlashAttention (II)"). Per batch b and head h, with
+ * S = Q K^T / sqrt(hs) over j <= t, P = row softmax of S, O = P V and the
+ * incoming dO:
+ *   dV = P^T dO,   dP = dO V^T,   dS[t][j] = P[t][j] (dP[t][j] - sum_j' P[t][j'] dP[t][j']),
+ *   dQ = dS K / sqrt(hs),   dK = dS^T Q / sqrt(hs).
+ * dqkv [B,T,3C] has the packed layout of qkv and is overwritten. */
+void oracle_attention_backward(float* dqkv, const float* dout, const float* qkv, int B, int T, int C,
+                               int NH) {
+    int hs = C / NH;
+    double scale = 1.0 / sqrt((double)hs);
+    double* P = (double*)malloc(sizeof(double) * (size_t)T * (size_t)T);
+    double* dS = (double*)malloc(sizeof(double) * (size_t)T * (size_t)T);
+    if (!P || !dS) {
+        free(P); free(dS);
+        return;
+    }
+#define Q_(t, e) ((double)qkv[((int64_t)b * T + (t)) * 3 * C + h * hs + (e)])
+#define K_(t, e) ((double)qkv[((int64_t)b * T + (t)) * 3 * C + C + h * hs + (e)])
+#define V_(t, e) ((double)qkv[((int64_t)b * T + (t)) * 3 * C + 2 * C + h * hs + (e)])
+#define DO_(t, e) ((double)dout[((int64_t)b * T + (t)) * C + h * hs + (e)])
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < NH; h++) {
+            for (int t = 0; t < T; t++) {
+                double* p = P + (int64_t)t * T;
+                double mx = -INFINITY;
+                for (int j = 0; j <= t; j++) {
+                    double d = 0.0;
+                    for (int e = 0; e < hs; e++) d += Q_(t, e) * K_(j, e);
+                    p[j] = d * scale;
+                    if (p[j] > mx) mx = p[j];
+                }
+                double sum = 0.0;
+                for (int j = 0; j <= t; j++) {
+                    p[j] = exp(p[j] - mx);
+                    sum += p[j];
+                }
+                for (int j = 0; j <= t; j++) p[j] /= sum;
+                /* dP row and dS row */
+                double* ds = dS + (int64_t)t * T;
+                double dot = 0.0;
+                for (int j = 0; j <= t; j++) {
+                    double d = 0.0;
+                    for (int e = 0; e < hs; e++) d += DO_(t, e) * V_(j, e);
+                    ds[j] = d; /* dP for now */
+                    dot += p[j] * d;
+                }
+                for (int j = 0; j <= t; j++) ds[j] = p[j] * (ds[j] - dot);
+            }
+            for (int t = 0; t < T; t++) {
+                float* dq = dqkv + ((int64_t)b * T + t) * 3 * C + h * hs;
+                float* dk = dq + C;
+                float* dv = dq + 2 * C;
+                for (int e = 0; e < hs; e++) {
+                    double aq = 0.0, ak = 0.0, av = 0.0;
+                    for (int j = 0; j <= t; j++) aq += dS[(int64_t)t * T + j] * K_(j, e);
+                    for (int i = t; i < T; i++) {
+                        ak += dS[(int64_t)i * T + t] * Q_(i, e);
+                        av += P[(int64_t)i * T + t] * DO_(i, e);
+                    }
+                    dq[e] = (float)(aq * scale);
+                    dk[e] = (float)(ak * scale);
+                    dv[e] = (float)av;
+                }
+            }
+        }
+#undef Q_
+#undef K_
+#undef V_
+#undef DO_
+    free(P);
+    free(dS);
+}
+
+/* Encoder backward, accumulating: for every vocabulary row v that occurs,
+ * dwte[v,:] += sum over positions (b,t) with tokens[b,t] == v of dout[b,t,:];
+ * dwpe[t,:] += sum_b dout[b,t,:]. Each sum is taken in double and added to the
+ * existing fp32 value once. (The token embedding is tied to the logits
+ * weight, so its gradient collects both uses.) */
+void oracle_encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tokens,
+                             int B, int T, int C) {
+    int N = B * T;
+    for (int n = 0; n < N; n++) {
+        int v = tokens[n];
+        int first = 1;
+        for (int m = 0; m < n; m++)
+            if (tokens[m] == v) { first = 0; break; }
+        if (!first) continue;
+        for (int c = 0; c < C; c++) {
+            double acc = 0.0;
+            for (int m = n; m < N; m++)
+                if (tokens[m] == v) acc += (double)dout[(int64_t)m * C + c];
+            dwte[(int64_t)v * C + c] = (float)((double)dwte[(int64_t)v * C + c] + acc);
+        }
+    }
+    if (dwpe)
+        for (int t = 0; t < T; t++)
+            for (int c = 0; c < C; c++) {
+                double acc = 0.0;
+                for (int b = 0; b < B; b++) acc += (double)dout[((int64_t)b * T + t) * C + c];
+                dwpe[(int64_t)t * C + c] = (float)((double)dwpe[(int64_t)t * C + c] + acc);
+            }
+}
+
+/* Gradient of the mean cross-entropy loss L = (1/N) sum_n loss_n (N = B*T,
+ * targets [B,T]) with respect to every parameter, in the flat parameter
+ * layout. Runs the steps of oracle_forward keeping every intermediate, then
+ * the backward steps above in reverse order; the residual stream's gradient
+ * is the sum of the gradient passed straight through and the branch's. *loss
+ * (optional) receives L. Returns 0 on success. */
+int oracle_backward(float* grads, float* loss, const int32_t* tokens, const int32_t* targets,
+                    const float* params, int L, int C, int NH, int V, int Vp, int maxT, double eps,
+                    int B, int T) {
+    if (!grads || !tokens || !targets || !params || L < 0 || C <= 0 || NH <= 0 || C % NH ||
+        V <= 0 || Vp < V || T <= 0 || T > maxT || B <= 0)
+        return 1;
+    int64_t N = (int64_t)B * T, c = C;
+    /* per layer: x_in, ln1, qkv, att, res1, ln2, fc, gelu  (= 1+1+3+1+1+1+4+4 = 16 C per row) */
+    int64_t per_layer = N * c * 16;
+    float* acts = (float*)malloc(sizeof(float) * (size_t)(per_layer * L + 3 * N * c));
+    float* logits = (float*)malloc(sizeof(float) * (size_t)(N * Vp));
+    float* d1 = (float*)malloc(sizeof(float) * (size_t)(N * 4 * c));
+    float* d2 = (float*)malloc(sizeof(float) * (size_t)(N * 4 * c));
+    float* dres = (float*)malloc(sizeof(float) * (size_t)(N * c));
+    float* tmp = (float*)malloc(sizeof(float) * (size_t)(N * c));
+    if (!acts || !logits || !d1 || !d2 || !dres || !tmp) {
+        free(acts); free(logits); free(d1); free(d2); free(dres); free(tmp);
+        return 2;
+    }
+    memset(grads, 0, sizeof(float) * (size_t)oracle_param_count(L, C, maxT, Vp));
+    /* forward, keeping everything */
+    layer_params p0 = params_at(params, L, C, maxT, Vp, 0);
+    float* x0 = acts + per_layer * L;      /* encoder output */
+    float* xf = x0 + N * c;                /* final residual stream */
+    float* lnf = xf + N * c;
+    oracle_encoder(x0, tokens, p0.wte, p0.wpe, B, T, C);
+    const float* xin = x0;
+    for (int l = 0; l < L; l++) {
+        layer_params p = params_at(params, L, C, maxT, Vp, l);
+        float* A = acts + per_layer * l;
+        float *x = A, *ln1 = x + N * c, *qkv = ln1 + N * c, *att = qkv + 3 * N * c;
+        float *res1 = att + N * c, *ln2 = res1 + N * c, *fc = ln2 + N * c, *ge = fc + 4 * N * c;
+        memcpy(x, xin, sizeof(float) * (size_t)(N * c));
+        oracle_layernorm(ln1, NULL, NULL, x, p.ln1_g, p.ln1_b, (int)N, C, eps);
+        oracle_matmul(qkv, ln1, p.qkv_w, p.qkv_b, (int)N, C, 3 * C);
+        oracle_attention(att, qkv, B, T, C, NH);
+        oracle_matmul(tmp, att, p.attproj_w, p.attproj_b, (int)N, C, C);
+        oracle_residual(res1, x, tmp, N * c);
+        oracle_layernorm(ln2, NULL, NULL, res1, p.ln2_g, p.ln2_b, (int)N, C, eps);
+        oracle_matmul(fc, ln2, p.fc_w, p.fc_b, (int)N, C, 4 * C);
+        oracle_gelu(ge, fc, N * 4 * c);
+        oracle_matmul(tmp, ge, p.fcproj_w, p.fcproj_b, (int)N, 4 * C, C);
+        float* xo = (l + 1 < L) ? acts + per_layer * (l + 1) : xf;
+        oracle_residual(xo, res1, tmp, N * c);
+        xin = xo;
+    }
+    if (L == 0) memcpy(xf, x0, sizeof(float) * (size_t)(N * c));
+    oracle_layernorm(lnf, NULL, NULL, xf, p0.lnf_g, p0.lnf_b, (int)N, C, eps);
+    oracle_matmul(logits, lnf, p0.wte, NULL, (int)N, C, Vp);
+    if (loss) {
+        float* ls = (float*)malloc(sizeof(float) * (size_t)N);
+        if (ls) {
+            oracle_crossentropy(ls, logits, targets, (int)N, V, Vp);
+            double s = 0.0;
+            for (int64_t n = 0; n < N; n++) s += (double)ls[n];
+            *loss = (float)(s / (double)N);
+            free(ls);
+        }
+    }
+    /* backward */
+    layer_params g0 = params_at(grads, L, C, maxT, Vp, 0);
+    float* dwte = (float*)g0.wte;
+    float* dwpe = (float*)g0.wpe;
+    oracle_crossentropy_backward(logits, logits, targets, 1.0 / (double)N, (int)N, V, Vp);
+    oracle_matmul_backward(tmp, dwte, NULL, logits, lnf, p0.wte, (int)N, C, Vp);
+    oracle_layernorm_backward(dres, (float*)g0.lnf_g, (float*)g0.lnf_b, tmp, xf, p0.lnf_g, (int)N, C, eps);
+    for (int l = L - 1; l >= 0; l--) {
+        layer_params p = params_at(params, L, C, maxT, Vp, l);
+        layer_params g = params_at(grads, L, C, maxT, Vp, l);
+        float* A = acts + per_layer * l;
+        float *x = A, *ln1 = x + N * c, *qkv = ln1 + N * c, *att = qkv + 3 * N * c;
+        float *res1 = att + N * c, *ln2 = res1 + N * c, *fc = ln2 + N * c, *ge = fc + 4 * N * c;
+        /* x_out = res1 + fcproj(gelu(fc(ln2(res1)))) */
+        oracle_matmul_backward(d1, (float*)g.fcproj_w, (float*)g.fcproj_b, dres, ge, p.fcproj_w, (int)N, 4 * C, C);
+        oracle_gelu_backward(d1, fc, d1, N * 4 * c);
+        oracle_matmul_backward(tmp, (float*)g.fc_w, (float*)g.fc_b, d1, ln2, p.fc_w, (int)N, C, 4 * C);
+        oracle_layernorm_backward(d2, (float*)g.ln2_g, (float*)g.ln2_b, tmp, res1, p.ln2_g, (int)N, C, eps);
+        oracle_residual(dres, dres, d2, N * c);
+        /* res1 = x + attproj(attention(qkv(ln1(x)))) */
+        oracle_matmul_backward(tmp, (float*)g.attproj_w, (float*)g.attproj_b, dres, att, p.attproj_w, (int)N, C, C);
+        oracle_attention_backward(d1, tmp, qkv, B, T, C, NH);
+        oracle_matmul_backward(tmp, (float*)g.qkv_w, (float*)g.qkv_b, d1, ln1, p.qkv_w, (int)N, C, 3 * C);
+        oracle_layernorm_backward(d2, (float*)g.ln1_g, (float*)g.ln1_b, tmp, x, p.ln1_g, (int)N, C, eps);
+        oracle_residual(dres, dres, d2, N * c);
+    }
+    oracle_encoder_backward(dwte, dwpe, dres, tokens, B, T, C);
+    free(acts); free(logits); free(d1); free(d2); free(dres); free(tmp);
+    return 0;
+}

@@ -21,7 +21,7 @@
  *           fc_b[L,4C] fcproj_w[L,C,4C] fcproj_b[L,C] lnf_g[C] lnf_b[C]
  *   kv cache [L,B,NH,maxT,hs]
  *
- * Parity status: every function below is pinned by the CPU test suite
+ * Parity status: every function below (forward and backward) is pinned by the CPU test suite
  * (closed forms, identities, brute force, a library GPT-2) except the full-size
  * logits of the 124M/350M workloads, which the pages print no values for.
  */
@@ -64,6 +64,27 @@ int oracle_forward(float* logits, float* probs, const int32_t* tokens, const flo
 int oracle_decode_step(float* logits, float* probs, const int32_t* tokens, int pos,
                        float* kcache, float* vcache, const float* params,
                        int L, int C, int NH, int V, int Vp, int maxT, double eps, int B);
+
+/* ------------------------------------------------------------------ backward
+ * Outputs are overwritten unless stated; optional outputs may be NULL. */
+void oracle_crossentropy_backward(float* dlogits, const float* logits, const int32_t* targets,
+                                  double dloss, int N, int V, int Vp);
+void oracle_matmul_backward(float* dinp, float* dweight, float* dbias, const float* dout,
+                            const float* inp, const float* weight, int N, int C, int OC);
+void oracle_layernorm_backward(float* dinp, float* dgamma, float* dbeta, const float* dout,
+                               const float* inp, const float* gamma, int N, int C, double eps);
+void oracle_gelu_backward(float* dinp, const float* inp, const float* dout, int64_t n);
+/* lse [B,NH,T] */
+void oracle_attention_lse(float* lse, const float* qkv, int B, int T, int C, int NH);
+void oracle_attention_backward(float* dqkv, const float* dout, const float* qkv, int B, int T, int C,
+                               int NH);
+/* accumulates into dwte [Vp,C] and dwpe [maxT,C] (dwpe may be NULL) */
+void oracle_encoder_backward(float* dwte, float* dwpe, const float* dout, const int32_t* tokens,
+                             int B, int T, int C);
+/* grads: flat buffer in the parameter layout (overwritten); loss may be NULL. */
+int oracle_backward(float* grads, float* loss, const int32_t* tokens, const int32_t* targets,
+                    const float* params, int L, int C, int NH, int V, int Vp, int maxT, double eps,
+                    int B, int T);
 
 #ifdef __cplusplus
 }
