@@ -245,6 +245,96 @@ int gpt2_generate(int32_t* out_tokens, const int32_t* prompt, int n_new, void* k
                   const void* params, const gpt2_config* cfg /* host */, int B, int T,
                   void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ============================================================== backward
+ * The training step's backward, one entry per forward step (the backward
+ * kernels of llm.c's training step, "State of the Union [April 22, 2024]",
+ * kernel summaries; the attention backward is the one asked for in the
+ * optdl2025 project "Understand FlashAttention (II)"). Gradients have the
+ * dtype and layout of the tensors they belong to; every reduction is done in
+ * fp32 in a fixed order (bitwise reproducible). Scratch comes from the
+ * caller's workspace, sized by the matching *_workspace_size call (host;
+ * negative on invalid arguments). */
+
+/* Fused classifier, backward half (llm.c fused_classifier_kernel3): for the
+ * loss sum_n dloss * loss_n,
+ *   dlogits[n,v] = dloss * (softmax(l_n)[v] - [v == targets[n]])  for v < V,
+ *   dlogits[n,v] = 0                                             for V <= v < Vp,
+ * and, from the same pass, losses [N] and mean_loss as crossentropy_forward
+ * (both nullable; mean_loss needs losses). dlogits may be logits (in place).
+ * For the mean loss pass dloss = 1/N. */
+int crossentropy_backward(void* dlogits, float* losses, float* mean_loss, const void* logits,
+                          const int32_t* targets, float dloss, int N, int V, int Vp, int dtype,
+                          void* stream);
+
+/* GELU backward: dinp = dout * g'(inp) with g the tanh-form GELU of
+ * gelu_forward; n elements; dinp may be dout, not inp. */
+int gelu_backward(void* dinp, const void* inp, const void* dout, int64_t n, int dtype, void* stream);
+
+/* LayerNorm backward for y = (x - mean) * rstd * gamma + beta over rows of C,
+ * with mean, rstd the fp32 statistics layernorm_forward saved:
+ *   dinp  = [dres +] rstd * (g - mean_c(g) - xh * mean_c(g * xh)),  g = dout * gamma,
+ *           xh = (x - mean) * rstd;
+ *   dgamma = sum_n dout * xh,  dbeta = sum_n dout   (each [C], nullable, overwritten).
+ * dres (nullable) is added: the residual stream's gradient flowing past the
+ * LayerNorm; it may be dinp. dinp must not alias dout or inp. C % 8 == 0,
+ * C <= 2048 (fp32) / 4096 (bf16). */
+int64_t layernorm_backward_workspace_size(int N, int C);
+int layernorm_backward(void* dinp, void* dgamma, void* dbeta, const void* dres, const void* dout,
+                       const void* inp, const void* gamma, const float* mean, const float* rstd, int N, int C,
+                       int dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Linear backward for out = inp [N,C] . weight[OC,C]^T + bias, given dout [N,OC]:
+ *   dinp [N,C] = dout . weight,  dweight [OC,C] = dout^T . inp,  dbias [OC] = sum_n dout
+ * each nullable (skipped) and overwritten; inp is needed for dweight, weight
+ * for dinp. C % 8 == 0, OC % 8 == 0. */
+int64_t matmul_backward_workspace_size(int N, int C, int OC, int dtype);
+int matmul_backward(void* dinp, void* dweight, void* dbias, const void* dout, const void* inp,
+                    const void* weight, int N, int C, int OC, int dtype, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
+/* attention_forward that also writes lse [B,NH,T] (fp32): the natural
+ * log-sum-exp of each query's causal scaled scores, ln sum_{j<=t} exp(S_tj),
+ * which attention_backward uses to rebuild the probabilities. */
+int attention_forward_lse(void* out, float* lse, const void* qkv, int B, int T, int C, int NH, int dtype,
+                          void* stream);
+
+/* Attention backward: dqkv [B,T,3C] (packed like qkv, overwritten) of the
+ * causal attention given dout [B,T,C] and the forward's qkv, out and lse:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - rowsum(dO o O)),
+ *   dQ = dS K / sqrt(hs),  dK = dS^T Q / sqrt(hs),   P = exp(S - lse).
+ * hs = C/NH in {16, 32, 64}. dqkv must not alias an input. */
+int64_t attention_backward_workspace_size(int B, int T, int C, int NH);
+int attention_backward(void* dqkv, const void* dout, const void* qkv, const void* out, const float* lse,
+                       int B, int T, int C, int NH, int dtype, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
+/* Embedding backward, accumulating:
+ *   dwte[tokens[b,t], :] += dout[b,t,:]   (each row summed over its positions in ascending order)
+ *   dwpe[t, :] += sum_b dout[b,t,:]
+ * either output may be NULL. tokens int32 [B,T] in [0, Vp) (not checked on
+ * the device). C % 8 == 0, C <= 4096 (fp32) / 8192 (bf16). */
+int encoder_backward(void* dwte, void* dwpe, const void* dout, const int32_t* tokens, int B, int T, int C,
+                     int dtype, void* stream);
+
+/* ------------------------------------------------------- training step
+ * gpt2_train_forward runs the forward (encoder, blocks, lnf, logits) keeping
+ * every activation the backward needs in acts (gpt2_train_acts_bytes), then
+ * the fused classifier: per-row losses against targets int32 [B,T] (losses
+ * fp32 [B*T], nullable), their mean (mean_loss fp32 [1], nullable) and, over
+ * the logits inside acts, the gradient of the mean loss with respect to them.
+ * gpt2_backward then writes the gradient of that mean loss with respect to
+ * every parameter into grads (the flat parameter layout, overwritten), using
+ * acts and the workspace (gpt2_train_workspace_bytes). Head size 16, 32 or 64.
+ * The optimizer is not part of this library. */
+int64_t gpt2_train_acts_bytes(const gpt2_config* cfg /* host */, int B, int T);
+int64_t gpt2_train_workspace_bytes(const gpt2_config* cfg /* host */, int B, int T);
+int gpt2_train_forward(float* losses, float* mean_loss, const int32_t* tokens, const int32_t* targets,
+                       const void* params, const gpt2_config* cfg /* host */, int B, int T, void* acts,
+                       int64_t acts_bytes, void* stream);
+int gpt2_backward(void* grads, const int32_t* tokens, const void* params, const gpt2_config* cfg /* host */,
+                  int B, int T, void* acts, int64_t acts_bytes, void* workspace, int64_t workspace_bytes,
+                  void* stream);
+
 /* ---------------------------------------------------------------- status */
 const char* gpt2_status_string(int status);  /* static string, never NULL */
 int gpt2_last_hip_error(void);               /* hipError_t of this thread's last failure */

@@ -36,6 +36,10 @@ EXPORTS = (
     "matmul_splitk_forward", "matmul_splitk_count", "matmul_gelu_forward", "residual_layernorm_forward",
     "matmul_residual_forward", "argmax_forward", "gpt2_prefill", "gpt2_generate_workspace_bytes",
     "gpt2_generate", "crossentropy_forward",
+    "crossentropy_backward", "gelu_backward", "layernorm_backward_workspace_size", "layernorm_backward",
+    "matmul_backward_workspace_size", "matmul_backward", "attention_forward_lse",
+    "attention_backward_workspace_size", "attention_backward", "encoder_backward", "gpt2_train_acts_bytes",
+    "gpt2_train_workspace_bytes", "gpt2_train_forward", "gpt2_backward",
 )
 
 
@@ -98,6 +102,20 @@ def load_library(path: str = LIB_PATH):
             "gpt2_generate_workspace_bytes": (I64, [CP, I, I]),
             "gpt2_generate": (I, [P, P, I, P, P, P, CP, I, I, P, I64, P]),
             "residual_layernorm_forward": (I, [P, P, P, I, P, P, P, I, I, F, I, P]),
+            "crossentropy_backward": (I, [P, P, P, P, P, F, I, I, I, I, P]),
+            "gelu_backward": (I, [P, P, P, I64, I, P]),
+            "layernorm_backward_workspace_size": (I64, [I, I]),
+            "layernorm_backward": (I, [P, P, P, P, P, P, P, P, P, I, I, I, P, I64, P]),
+            "matmul_backward_workspace_size": (I64, [I, I, I, I]),
+            "matmul_backward": (I, [P, P, P, P, P, P, I, I, I, I, P, I64, P]),
+            "attention_forward_lse": (I, [P, P, P, I, I, I, I, I, P]),
+            "attention_backward_workspace_size": (I64, [I, I, I, I]),
+            "attention_backward": (I, [P, P, P, P, P, I, I, I, I, I, P, I64, P]),
+            "encoder_backward": (I, [P, P, P, P, I, I, I, I, P]),
+            "gpt2_train_acts_bytes": (I64, [CP, I, I]),
+            "gpt2_train_workspace_bytes": (I64, [CP, I, I]),
+            "gpt2_train_forward": (I, [P, P, P, P, P, CP, I, I, P, I64, P]),
+            "gpt2_backward": (I, [P, P, P, CP, I, I, P, I64, P, I64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -371,3 +389,120 @@ def gpt2_generate(out_tokens, prompt, kcache, vcache, params, cfg: Config, works
         _dev(vcache, "vcache"), _dev(params, "params"), ctypes.byref(cfg), B, T, _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out_tokens
+
+
+# ------------------------------------------------------------------ backward
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def crossentropy_backward(dlogits, logits, targets, V, dloss, losses=None, mean_loss=None, stream=None):
+    """dlogits [N,Vp] = dloss * (softmax(logits) - onehot(targets)) on v < V, 0 in the padding
+    (dlogits may be logits); optional fp32 losses [N] and their mean [1]."""
+    lib = load_library()
+    N, Vp = logits.shape
+    _check("crossentropy_backward", lib.crossentropy_backward(
+        _dev(dlogits, "dlogits"), _dev(losses, "losses"), _dev(mean_loss, "mean_loss"), _dev(logits, "logits"),
+        _dev(targets, "targets"), float(dloss), N, V, Vp, _dtype_code(logits), _stream(stream)))
+    return dlogits
+
+
+def gelu_backward(dinp, inp, dout, stream=None):
+    """dinp = dout * gelu'(inp) (dinp may be dout)."""
+    lib = load_library()
+    _check("gelu_backward", lib.gelu_backward(_dev(dinp, "dinp"), _dev(inp, "inp"), _dev(dout, "dout"),
+                                              inp.numel(), _dtype_code(inp), _stream(stream)))
+    return dinp
+
+
+def layernorm_backward_workspace_size(N, C) -> int:
+    return int(load_library().layernorm_backward_workspace_size(N, C))
+
+
+def layernorm_backward(dinp, dgamma, dbeta, dout, inp, gamma, mean, rstd, workspace, dres=None, stream=None):
+    """dinp = [dres +] LayerNorm backward; dgamma, dbeta (nullable) overwritten; dres may be dinp."""
+    lib = load_library()
+    C = inp.shape[-1]
+    N = inp.numel() // C
+    _check("layernorm_backward", lib.layernorm_backward(
+        _dev(dinp, "dinp"), _dev(dgamma, "dgamma"), _dev(dbeta, "dbeta"), _dev(dres, "dres"), _dev(dout, "dout"),
+        _dev(inp, "inp"), _dev(gamma, "gamma"), _dev(mean, "mean"), _dev(rstd, "rstd"), N, C, _dtype_code(inp),
+        _dev(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
+    return dinp
+
+
+def matmul_backward_workspace_size(N, C, OC, dtype) -> int:
+    return int(load_library().matmul_backward_workspace_size(N, C, OC, dtype))
+
+
+def matmul_backward(dinp, dweight, dbias, dout, inp, weight, workspace, stream=None):
+    """For out = inp [N,C] @ weight[OC,C]^T + b: dinp [N,C], dweight [OC,C], dbias [OC] (each nullable)."""
+    lib = load_library()
+    OC, C = weight.shape
+    N = dout.numel() // OC
+    _check("matmul_backward", lib.matmul_backward(
+        _dev(dinp, "dinp"), _dev(dweight, "dweight"), _dev(dbias, "dbias"), _dev(dout, "dout"), _dev(inp, "inp"),
+        _dev(weight, "weight"), N, C, OC, _dtype_code(dout), _dev(workspace, "workspace"), _nbytes(workspace),
+        _stream(stream)))
+    return dinp
+
+
+def attention_forward_lse(out, lse, qkv, NH, stream=None):
+    """out [B,T,C] and lse fp32 [B,NH,T] (log-sum-exp of each causal score row) from qkv [B,T,3C]."""
+    lib = load_library()
+    B, T, C3 = qkv.shape
+    _check("attention_forward_lse", lib.attention_forward_lse(
+        _dev(out, "out"), _dev(lse, "lse"), _dev(qkv, "qkv"), B, T, C3 // 3, NH, _dtype_code(qkv), _stream(stream)))
+    return out
+
+
+def attention_backward_workspace_size(B, T, C, NH) -> int:
+    return int(load_library().attention_backward_workspace_size(B, T, C, NH))
+
+
+def attention_backward(dqkv, dout, qkv, out, lse, NH, workspace, stream=None):
+    """dqkv [B,T,3C] from dout [B,T,C] and the forward's qkv, out and lse."""
+    lib = load_library()
+    B, T, C3 = qkv.shape
+    _check("attention_backward", lib.attention_backward(
+        _dev(dqkv, "dqkv"), _dev(dout, "dout"), _dev(qkv, "qkv"), _dev(out, "out"), _dev(lse, "lse"), B, T, C3 // 3,
+        NH, _dtype_code(qkv), _dev(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
+    return dqkv
+
+
+def encoder_backward(dwte, dwpe, dout, tokens, stream=None):
+    """dwte[tokens[b,t]] += dout[b,t]; dwpe[t] += sum_b dout[b,t] (either may be None)."""
+    lib = load_library()
+    B, T = tokens.shape
+    C = dout.shape[-1]
+    _check("encoder_backward", lib.encoder_backward(
+        _dev(dwte, "dwte"), _dev(dwpe, "dwpe"), _dev(dout, "dout"), _dev(tokens, "tokens"), B, T, C,
+        _dtype_code(dout), _stream(stream)))
+
+
+def train_acts_bytes(cfg: Config, B: int, T: int) -> int:
+    return int(load_library().gpt2_train_acts_bytes(ctypes.byref(cfg), B, T))
+
+
+def train_workspace_bytes(cfg: Config, B: int, T: int) -> int:
+    return int(load_library().gpt2_train_workspace_bytes(ctypes.byref(cfg), B, T))
+
+
+def gpt2_train_forward(tokens, targets, params, cfg: Config, acts, losses=None, mean_loss=None, stream=None):
+    """Forward keeping its activations in acts, then the losses (fp32 [B*T], optional), their mean
+    (fp32 [1], optional) and the gradient of the mean loss w.r.t. the logits (kept in acts)."""
+    lib = load_library()
+    B, T = tokens.shape
+    _check("gpt2_train_forward", lib.gpt2_train_forward(
+        _dev(losses, "losses"), _dev(mean_loss, "mean_loss"), _dev(tokens, "tokens"), _dev(targets, "targets"),
+        _dev(params, "params"), ctypes.byref(cfg), B, T, _dev(acts, "acts"), _nbytes(acts), _stream(stream)))
+
+
+def gpt2_backward(grads, tokens, params, cfg: Config, acts, workspace, stream=None):
+    """grads (flat, parameter layout) of the mean loss of the preceding gpt2_train_forward."""
+    lib = load_library()
+    B, T = tokens.shape
+    _check("gpt2_backward", lib.gpt2_backward(
+        _dev(grads, "grads"), _dev(tokens, "tokens"), _dev(params, "params"), ctypes.byref(cfg), B, T,
+        _dev(acts, "acts"), _nbytes(acts), _dev(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
+    return grads

@@ -70,7 +70,8 @@ __device__ __forceinline__ int vt_slot_bf16(int key) {
 // single-buffered key/value staging (half the LDS).
 template <typename T, int HS, int WPE = 0, bool SB = false>
 __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
-                                                             int Tn, int C, int NH, float sl2) {
+                                                             int Tn, int C, int NH, float sl2,
+                                                             float* __restrict__ lse) {
     constexpr bool F32 = std::is_same<T, float>::value;
     constexpr int VE = Vec<T>::N;
     constexpr int DT = (HS + 31) / 32;  // 32-row tiles of O^T (head dim padded to 32)
@@ -329,11 +330,15 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
     const float m1 = mg[(DT * 16) * 64 + lane], l1 = mg[(DT * 16 + 1) * 64 + lane];
     const float m = fmaxf(m_run, m1);  // m_run is finite: the even half holds key block 0
     const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-    const float inv = 1.0f / (l_run * a0 + l1 * a1);
+    const float lsum = l_run * a0 + l1 * a1;
+    const float inv = 1.0f / lsum;
 
     // O^T register v of lane (h, r32): head dim dt*32 + 8*(v/4) + 4*h + v%4,
     // query qw + r32. Four consecutive head dims per store.
     const int q = qw + r32;
+    // lse (optional): the natural log-sum-exp of the query's scaled scores,
+    // ln sum_j e^{S_j} = (m + log2 l) ln 2 in the base-2 units used above.
+    if (lse && h == 0 && q < Tn) lse[(int64_t)bh * Tn + q] = (m + __log2f(lsum)) * 0.6931471805599453f;
     if (q < Tn) {
         T* orow = out + ((int64_t)b * Tn + q) * C + hd * HS;
 #pragma unroll
@@ -362,33 +367,34 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
 // (head size 64) single-buffered with 3 per SIMD (two workgroups per CU hide
 // each other's staging), the rest double-buffered with one workgroup per CU.
 template <typename T, int HS>
-static void launch_attn_hs(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s) {
+static void launch_attn_hs(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s, float* lse) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)HS);  // log2(e)/sqrt(hs)
     dim3 grid(B * NH, (Tn + kBQ - 1) / kBQ);
     if constexpr (std::is_same<T, float>::value)
-        attention_kernel<T, HS, 3><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2);
+        attention_kernel<T, HS, 3><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
     else if (HS == 64 && (int64_t)grid.x * grid.y >= 768)
-        attention_kernel<T, HS, 3, HS == 64><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2);
+        attention_kernel<T, HS, 3, HS == 64><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
     else
-        attention_kernel<T, HS><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2);
+        attention_kernel<T, HS><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
 }
 
 template <typename T>
-static void launch_attn_t(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s) {
+static void launch_attn_t(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s, float* lse) {
     switch (C / NH) {
-        case 16: launch_attn_hs<T, 16>(out, qkv, B, Tn, C, NH, s); break;
-        case 32: launch_attn_hs<T, 32>(out, qkv, B, Tn, C, NH, s); break;
-        case 64: launch_attn_hs<T, 64>(out, qkv, B, Tn, C, NH, s); break;
-        default: launch_attn_hs<T, 128>(out, qkv, B, Tn, C, NH, s); break;
+        case 16: launch_attn_hs<T, 16>(out, qkv, B, Tn, C, NH, s, lse); break;
+        case 32: launch_attn_hs<T, 32>(out, qkv, B, Tn, C, NH, s, lse); break;
+        case 64: launch_attn_hs<T, 64>(out, qkv, B, Tn, C, NH, s, lse); break;
+        default: launch_attn_hs<T, 128>(out, qkv, B, Tn, C, NH, s, lse); break;
     }
 }
 
+// lse (nullable): [B,NH,T] fp32, the log-sum-exp of every query row.
 int launch_attention(void* out, const void* qkv, int B, int T, int C, int NH, int dtype,
-                     hipStream_t s) {
+                     hipStream_t s, float* lse) {
     if (dtype == GPT2_BF16)
-        launch_attn_t<bf16>((bf16*)out, (const bf16*)qkv, B, T, C, NH, s);
+        launch_attn_t<bf16>((bf16*)out, (const bf16*)qkv, B, T, C, NH, s, lse);
     else
-        launch_attn_t<float>((float*)out, (const float*)qkv, B, T, C, NH, s);
+        launch_attn_t<float>((float*)out, (const float*)qkv, B, T, C, NH, s, lse);
     return launch_status();
 }
 
@@ -626,7 +632,17 @@ extern "C" int attention_forward(void* out, const void* qkv, int B, int T, int C
     if (!attention_head_size_ok(C / NH) || !aligned16(out) || !aligned16(qkv))
         return GPT2_ERR_UNSUPPORTED;
     if (out == qkv) return GPT2_ERR_INVALID_ARGUMENT;
-    return launch_attention(out, qkv, B, T, C, NH, dtype, (hipStream_t)stream);
+    return launch_attention(out, qkv, B, T, C, NH, dtype, (hipStream_t)stream, nullptr);
+}
+
+extern "C" int attention_forward_lse(void* out, float* lse, const void* qkv, int B, int T, int C, int NH,
+                                     int dtype, void* stream) {
+    if (!valid_dtype(dtype) || B < 0 || T < 0 || C < 0 || NH <= 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if ((int64_t)B * T == 0) return GPT2_OK;
+    if (!out || !lse || !qkv || C == 0 || C % NH) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!attention_head_size_ok(C / NH) || !aligned16(out) || !aligned16(qkv)) return GPT2_ERR_UNSUPPORTED;
+    if (out == qkv) return GPT2_ERR_INVALID_ARGUMENT;
+    return launch_attention(out, qkv, B, T, C, NH, dtype, (hipStream_t)stream, lse);
 }
 
 extern "C" int64_t attention_decode_workspace_bytes(int B, int C, int NH, int maxT) {

@@ -1,0 +1,472 @@
+// Backward of causal multi-head attention on the gfx950 matrix cores.
+//
+// Method: the backward of the tiled forward (derived in the optdl2025 project
+// "Understand FlashAttention (II)" from "Algorithm 1" of FlashAttention): the
+// probabilities are rebuilt from the scores and the saved per-row
+// log-sum-exp, P = exp(S - lse), so no T x T matrix ever reaches HBM. With
+// D_q = sum_d dO[q,d] O[q,d] (= sum_j P[q,j] dP[q,j]):
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dK = dS^T Q / sqrt(hs),
+//   dQ = dS K / sqrt(hs).
+// Two kernels, so every output has exactly one writer and a fixed summation
+// order (no atomics): one walks, per 64-key tile, the query tiles at or after
+// it and accumulates dK and dV; the other walks, per 64-query tile, the key
+// tiles up to it and accumulates dQ (recomputing S and dP). Key tiles above
+// the diagonal are never visited.
+//
+// Every product runs on v_mfma_f32_32x32x2_f32, whatever the storage type:
+// bf16 tiles are widened to fp32 when staged into LDS.
+//
+// Register layouts (32x32 MFMA: lane (h, r32) supplies A[r32][k-slot h] and
+// B[k-slot h][r32]; accumulator register v holds row 8*(v/4) + 4*h + v%4,
+// column r32):
+//  - head-dim contractions (S, dP) use k-slot h of step i <-> head dim
+//    (HS/2)*h + i, so a lane's operand is one contiguous run of its row;
+//  - the query (key) contractions of dV, dK (dQ) take the probabilities
+//    straight from the accumulator of S (S^T): step v pairs slot h with
+//    row 8*(v/4) + 4*h + v%4, and the other operand is read from LDS at that
+//    row, column r32.
+#include <math.h>
+
+#include "common.h"
+
+namespace gpt2 {
+
+static constexpr int kAB = 64;  // queries / keys per tile
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Widen one 16-byte vector of T into VE consecutive floats of LDS.
+__device__ __forceinline__ void put_f32(float* dst, const u32x4& v, const float*) {
+    *reinterpret_cast<u32x4*>(dst) = v;
+}
+__device__ __forceinline__ void put_f32(float* dst, const u32x4& v, const bf16*) {
+    float f[8];
+    unpack_vec<bf16>(v, f);
+    *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// A lane's HS/2 contiguous elements of one head row, as fp32 registers
+// (zeros for rows past the sequence).
+template <typename T, int KH>
+__device__ __forceinline__ void load_half_row(float (&f)[KH], const T* p, bool ok) {
+    constexpr int VE = Vec<T>::N;
+#pragma unroll
+    for (int i = 0; i < KH / VE; i++) {
+        float t[VE];
+        if (ok) load_vec(p + i * VE, t);
+#pragma unroll
+        for (int j = 0; j < VE; j++) f[i * VE + j] = ok ? t[j] : 0.f;
+    }
+}
+
+// Four consecutive head dims of one row, scaled, stored to T.
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+    u32x2 pk = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+    *reinterpret_cast<u32x2*>(p) = pk;
+}
+
+// D[b,h,t] = sum_d dO[b,t,h*HS+d] O[b,t,h*HS+d]; one thread per (b,t,h).
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(float* __restrict__ D, const T* __restrict__ dout,
+                                                           const T* __restrict__ out, int B, int Tn, int C, int NH) {
+    constexpr int VE = Vec<T>::N;
+    const int64_t i = blockIdx.x * 256LL + threadIdx.x;
+    if (i >= (int64_t)B * Tn * NH) return;
+    const int hd = (int)(i % NH);
+    const int64_t bt = i / NH;
+    const int b = (int)(bt / Tn), t = (int)(bt % Tn);
+    const T* o = out + bt * C + hd * HS;
+    const T* d = dout + bt * C + hd * HS;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < HS; c += VE) {
+        float x[VE], y[VE];
+        load_vec(o + c, x);
+        load_vec(d + c, y);
+#pragma unroll
+        for (int j = 0; j < VE; j++) s += x[j] * y[j];
+    }
+    D[((int64_t)b * NH + hd) * Tn + t] = s;
+}
+
+// ------------------------------------------------------------------ dK, dV
+// Workgroup (b*NH + h, key tile kb), 4 wavefronts: wave (kc, par) owns keys
+// kb*64 + 32*kc .. +31 and, of every 64-query tile, the 32 queries 32*par..;
+// the two parities' dK, dV are added through LDS at the end (par 0 + par 1).
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv,
+                                                           const T* __restrict__ dout, const float* __restrict__ lse,
+                                                           const float* __restrict__ Dg, int Tn, int C, int NH,
+                                                           float sl2, float scale) {
+    constexpr int VE = Vec<T>::N;
+    constexpr int KH = HS / 2;             // head-dim contraction steps
+    constexpr int DT = (HS + 31) / 32;     // 32-row tiles of dK^T, dV^T
+    constexpr int LD = HS + 4;             // fp32 LDS row stride
+    constexpr int TILE = kAB * LD;
+    constexpr int BUF = 2 * TILE + 2 * kAB;  // Q, dO, lse2, D
+    constexpr int RV = HS / VE;              // 16-byte vectors per head row
+    constexpr int NV = (kAB * RV + 255) / 256;
+    static_assert(KH % VE == 0, "head size");
+    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int kc = wid & 1, par = wid >> 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
+    const int kb = blockIdx.y;  // dispatched in order: tile 0 (the longest walk) first
+    const int k0 = kb * kAB + kc * 32, key = k0 + r32;
+    const int64_t rs = 3 * (int64_t)C;
+    const T* base = qkv + (int64_t)b * Tn * rs;
+    const T* dbase = dout + (int64_t)b * Tn * C + hd * HS;
+    const float* lrow = lse + (int64_t)bh * Tn;
+    const float* drow = Dg + (int64_t)bh * Tn;
+    const float L2E = 1.4426950408889634f;
+
+    // this lane's key row as the B operand of S = Q K^T and dP = dO V^T
+    float kf[KH], vf[KH];
+    load_half_row<T, KH>(kf, base + (int64_t)min(key, Tn - 1) * rs + C + hd * HS + KH * h, key < Tn);
+    load_half_row<T, KH>(vf, base + (int64_t)min(key, Tn - 1) * rs + 2 * C + hd * HS + KH * h, key < Tn);
+
+    u32x4 rq[NV], rd[NV];
+    float rl = 0.f, rD = 0.f;
+    auto gload = [&](int qt) {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int li = tid + i * 256, r = li / RV, cv = li % RV, q = min(qt * kAB + r, Tn - 1);
+            rq[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)q * rs + hd * HS + cv * VE);
+            rd[i] = *reinterpret_cast<const u32x4*>(dbase + (int64_t)q * C + cv * VE);
+        }
+        const int q = min(qt * kAB + (tid & 63), Tn - 1);
+        rl = lrow[q];
+        rD = drow[q];
+    };
+    auto sstore = [&](int buf, int qt) {
+        float* sQ = smem + buf * BUF;
+        float* sO = sQ + TILE;
+        float* sL = sO + TILE;
+        float* sD = sL + kAB;
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int li = tid + i * 256, r = li / RV, cv = li % RV;
+            if (li < kAB * RV) {
+                const bool ok = qt * kAB + r < Tn;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                put_f32(sQ + r * LD + cv * VE, ok ? rq[i] : z, (const T*)nullptr);
+                put_f32(sO + r * LD + cv * VE, ok ? rd[i] : z, (const T*)nullptr);
+            }
+        }
+        if (tid < 64) {
+            const bool ok = qt * kAB + tid < Tn;
+            sL[tid] = ok ? rl * L2E : 0.f;
+            sD[tid] = ok ? rD : 0.f;
+        }
+    };
+
+    f32x16 dv[DT], dk[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) dv[dt] = dk[dt] = f32x16{};
+
+    auto compute = [&](int buf, int qt) {
+        const float* sQ = smem + buf * BUF;
+        const float* sO = sQ + TILE;
+        const float* sL = sO + TILE;
+        const float* sD = sL + kAB;
+        const int qb = qt * kAB + par * 32;  // this wave's queries qb .. qb+31
+        if (qb + 31 < k0) return;           // every query precedes every key: P = 0
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const float* qrow = sQ + (par * 32 + r32) * LD + KH * h;
+        const float* orow = sO + (par * 32 + r32) * LD + KH * h;
+#pragma unroll
+        for (int i = 0; i < KH; i += 4) {
+            const float4 qa = *reinterpret_cast<const float4*>(qrow + i);
+            const float4 oa = *reinterpret_cast<const float4*>(orow + i);
+            s = mfma_f32(qa.x, kf[i], s);
+            dp = mfma_f32(oa.x, vf[i], dp);
+            s = mfma_f32(qa.y, kf[i + 1], s);
+            dp = mfma_f32(oa.y, vf[i + 1], dp);
+            s = mfma_f32(qa.z, kf[i + 2], s);
+            dp = mfma_f32(oa.z, vf[i + 2], dp);
+            s = mfma_f32(qa.w, kf[i + 3], s);
+            dp = mfma_f32(oa.w, vf[i + 3], dp);
+        }
+        // P and dS; register v: query qb + m, m = 8*(v/4) + 4h + v%4; key k0 + r32
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = 8 * (v >> 2) + 4 * h + (v & 3), q = qb + m;
+            const bool on = key <= q && q < Tn;
+            const float p = on ? __builtin_amdgcn_exp2f(s[v] * sl2 - sL[par * 32 + m]) : 0.f;
+            s[v] = p;
+            dp[v] = p * (dp[v] - sD[par * 32 + m]);
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS: A = (dO | Q)[query m][head dim dt*32 + r32]
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = par * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const int d = dt * 32 + r32;
+                const float ao = d < HS ? sO[m * LD + min(d, HS - 1)] : 0.f;
+                const float aq = d < HS ? sQ[m * LD + min(d, HS - 1)] : 0.f;
+                dv[dt] = mfma_f32(ao, s[v], dv[dt]);
+                dk[dt] = mfma_f32(aq, dp[v], dk[dt]);
+            }
+        }
+    };
+
+    const int nqt = (Tn + kAB - 1) / kAB;
+    gload(kb);
+    sstore(0, kb);
+    __syncthreads();
+    for (int qt = kb; qt < nqt; qt++) {
+        const int cur = (qt - kb) & 1;
+        if (qt + 1 < nqt) gload(qt + 1);
+        compute(cur, qt);
+        if (qt + 1 < nqt) sstore(cur ^ 1, qt + 1);
+        __syncthreads();
+    }
+
+    // parity merge (par 1 -> LDS -> par 0), then dK (scaled) and dV
+    float* mg = smem + kc * (2 * DT * 16 * 64);
+    if (par == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                mg[((2 * dt) * 16 + v) * 64 + lane] = dv[dt][v];
+                mg[((2 * dt + 1) * 16 + v) * 64 + lane] = dk[dt][v];
+            }
+    }
+    __syncthreads();
+    if (par == 1 || key >= Tn) return;
+    T* drow_k = dqkv + ((int64_t)b * Tn + key) * rs + C + hd * HS;
+    T* drow_v = drow_k + C;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int d0 = dt * 32 + 8 * g + 4 * h;
+            if (d0 < HS) {
+                float x[4], y[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int v = 4 * g + e;
+                    x[e] = dv[dt][v] + mg[((2 * dt) * 16 + v) * 64 + lane];
+                    y[e] = (dk[dt][v] + mg[((2 * dt + 1) * 16 + v) * 64 + lane]) * scale;
+                }
+                store4(drow_v + d0, x[0], x[1], x[2], x[3]);
+                store4(drow_k + d0, y[0], y[1], y[2], y[3]);
+            }
+        }
+}
+
+// --------------------------------------------------------------------- dQ
+// Workgroup (b*NH + h, query tile), 4 wavefronts: wave (qc, par) owns queries
+// qt*64 + 32*qc .. +31 and, of every 64-key tile, the 32 keys 32*par..; the
+// parities' dQ are added through LDS at the end.
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv,
+                                                          const T* __restrict__ dout, const float* __restrict__ lse,
+                                                          const float* __restrict__ Dg, int Tn, int C, int NH,
+                                                          float sl2, float scale) {
+    constexpr int VE = Vec<T>::N;
+    constexpr int KH = HS / 2;
+    constexpr int DT = (HS + 31) / 32;
+    constexpr int LD = HS + 4;
+    constexpr int TILE = kAB * LD;
+    constexpr int BUF = 2 * TILE;  // K, V
+    constexpr int RV = HS / VE;
+    constexpr int NV = (kAB * RV + 255) / 256;
+    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int qc = wid & 1, par = wid >> 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
+    const int qt = gridDim.y - 1 - blockIdx.y;  // the last (longest) query tiles first
+    const int qw = qt * kAB + qc * 32, q = qw + r32;
+    const int64_t rs = 3 * (int64_t)C;
+    const T* base = qkv + (int64_t)b * Tn * rs;
+    const float L2E = 1.4426950408889634f;
+
+    float qf[KH], df[KH];
+    load_half_row<T, KH>(qf, base + (int64_t)min(q, Tn - 1) * rs + hd * HS + KH * h, q < Tn);
+    load_half_row<T, KH>(df, dout + ((int64_t)b * Tn + min(q, Tn - 1)) * C + hd * HS + KH * h, q < Tn);
+    const float l2 = q < Tn ? lse[(int64_t)bh * Tn + q] * L2E : 0.f;
+    const float Dq = q < Tn ? Dg[(int64_t)bh * Tn + q] : 0.f;
+
+    u32x4 rk[NV], rv[NV];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int li = tid + i * 256, r = li / RV, cv = li % RV, k = min(kt * kAB + r, Tn - 1);
+            rk[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)k * rs + C + hd * HS + cv * VE);
+            rv[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)k * rs + 2 * C + hd * HS + cv * VE);
+        }
+    };
+    auto sstore = [&](int buf, int kt) {
+        float* sK = smem + buf * BUF;
+        float* sV = sK + TILE;
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int li = tid + i * 256, r = li / RV, cv = li % RV;
+            if (li < kAB * RV) {
+                const bool ok = kt * kAB + r < Tn;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                put_f32(sK + r * LD + cv * VE, ok ? rk[i] : z, (const T*)nullptr);
+                put_f32(sV + r * LD + cv * VE, ok ? rv[i] : z, (const T*)nullptr);
+            }
+        }
+    };
+
+    f32x16 dq[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) dq[dt] = f32x16{};
+
+    auto compute = [&](int buf, int kt) {
+        const float* sK = smem + buf * BUF;
+        const float* sV = sK + TILE;
+        const int kbse = kt * kAB + par * 32;  // this wave's keys kbse .. kbse+31
+        if (kbse > qw + 31) return;            // every key follows every query
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const float* krow = sK + (par * 32 + r32) * LD + KH * h;
+        const float* vrow = sV + (par * 32 + r32) * LD + KH * h;
+#pragma unroll
+        for (int i = 0; i < KH; i += 4) {
+            const float4 ka = *reinterpret_cast<const float4*>(krow + i);
+            const float4 va = *reinterpret_cast<const float4*>(vrow + i);
+            s = mfma_f32(ka.x, qf[i], s);
+            dp = mfma_f32(va.x, df[i], dp);
+            s = mfma_f32(ka.y, qf[i + 1], s);
+            dp = mfma_f32(va.y, df[i + 1], dp);
+            s = mfma_f32(ka.z, qf[i + 2], s);
+            dp = mfma_f32(va.z, df[i + 2], dp);
+            s = mfma_f32(ka.w, qf[i + 3], s);
+            dp = mfma_f32(va.w, df[i + 3], dp);
+        }
+        // S^T register v: key kbse + m, m = 8*(v/4) + 4h + v%4; query q
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+            const bool on = kbse + m <= q && q < Tn;
+            const float p = on ? __builtin_amdgcn_exp2f(s[v] * sl2 - l2) : 0.f;
+            dp[v] = p * (dp[v] - Dq);
+        }
+        // dQ^T += K^T dS^T: A = K[key m][head dim dt*32 + r32]
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = par * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const int d = dt * 32 + r32;
+                const float a = d < HS ? sK[m * LD + min(d, HS - 1)] : 0.f;
+                dq[dt] = mfma_f32(a, dp[v], dq[dt]);
+            }
+        }
+    };
+
+    const int nkt = qt + 1;
+    gload(0);
+    sstore(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt++) {
+        const int cur = kt & 1;
+        if (kt + 1 < nkt) gload(kt + 1);
+        compute(cur, kt);
+        if (kt + 1 < nkt) sstore(cur ^ 1, kt + 1);
+        __syncthreads();
+    }
+
+    float* mg = smem + qc * (DT * 16 * 64);
+    if (par == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) mg[(dt * 16 + v) * 64 + lane] = dq[dt][v];
+    }
+    __syncthreads();
+    if (par == 1 || q >= Tn) return;
+    T* drow = dqkv + ((int64_t)b * Tn + q) * rs + hd * HS;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int d0 = dt * 32 + 8 * g + 4 * h;
+            if (d0 < HS) {
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int v = 4 * g + e;
+                    x[e] = (dq[dt][v] + mg[(dt * 16 + v) * 64 + lane]) * scale;
+                }
+                store4(drow + d0, x[0], x[1], x[2], x[3]);
+            }
+        }
+}
+
+int64_t attention_backward_workspace_bytes(int B, int T, int NH) { return ((int64_t)B * NH * T * 4 + 255) & ~255LL; }
+
+template <typename T, int HS>
+static void launch_attn_bwd_hs(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* D, int B,
+                               int Tn, int C, int NH, hipStream_t s) {
+    const float scale = 1.0f / sqrtf((float)HS);
+    const float sl2 = 1.4426950408889634f * scale;
+    const int64_t rows = (int64_t)B * Tn * NH;
+    attn_bwd_dot_kernel<T, HS><<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(D, dout, out, B, Tn, C, NH);
+    const dim3 grid(B * NH, (Tn + kAB - 1) / kAB);
+    attn_bwd_dkv_kernel<T, HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+    attn_bwd_dq_kernel<T, HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+}
+
+template <typename T>
+static void launch_attn_bwd_t(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* D, int B,
+                              int Tn, int C, int NH, hipStream_t s) {
+    switch (C / NH) {
+        case 16: launch_attn_bwd_hs<T, 16>(dqkv, dout, qkv, out, lse, D, B, Tn, C, NH, s); break;
+        case 32: launch_attn_bwd_hs<T, 32>(dqkv, dout, qkv, out, lse, D, B, Tn, C, NH, s); break;
+        default: launch_attn_bwd_hs<T, 64>(dqkv, dout, qkv, out, lse, D, B, Tn, C, NH, s); break;
+    }
+}
+
+bool attention_backward_head_size_ok(int hs) { return hs == 16 || hs == 32 || hs == 64; }
+
+// dqkv [B,T,3C] from dout [B,T,C], the forward's qkv, out and lse [B,NH,T];
+// ws: D [B,NH,T] fp32.
+int launch_attention_backward(void* dqkv, const void* dout, const void* qkv, const void* out, const float* lse,
+                              int B, int T, int C, int NH, int dtype, void* ws, hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_attn_bwd_t<bf16>((bf16*)dqkv, (const bf16*)dout, (const bf16*)qkv, (const bf16*)out, lse, (float*)ws,
+                                B, T, C, NH, s);
+    else
+        launch_attn_bwd_t<float>((float*)dqkv, (const float*)dout, (const float*)qkv, (const float*)out, lse,
+                                 (float*)ws, B, T, C, NH, s);
+    return launch_status();
+}
+
+}  // namespace gpt2
+
+using namespace gpt2;
+
+extern "C" int64_t attention_backward_workspace_size(int B, int T, int C, int NH) {
+    if (B < 0 || T < 0 || C <= 0 || NH <= 0 || C % NH) return GPT2_ERR_INVALID_ARGUMENT;
+    return attention_backward_workspace_bytes(B, T, NH);
+}
+
+extern "C" int attention_backward(void* dqkv, const void* dout, const void* qkv, const void* out, const float* lse,
+                                  int B, int T, int C, int NH, int dtype, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+    if (!valid_dtype(dtype) || B < 0 || T < 0 || C < 0 || NH <= 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if ((int64_t)B * T == 0) return GPT2_OK;
+    if (!dqkv || !dout || !qkv || !out || !lse || !workspace || C == 0 || C % NH) return GPT2_ERR_INVALID_ARGUMENT;
+    if (dqkv == qkv || dqkv == dout || dqkv == out) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!attention_backward_head_size_ok(C / NH) || !aligned16(dqkv) || !aligned16(dout) || !aligned16(qkv) ||
+        !aligned16(out))
+        return GPT2_ERR_UNSUPPORTED;
+    if (workspace_bytes < attention_backward_workspace_bytes(B, T, NH)) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    return launch_attention_backward(dqkv, dout, qkv, out, lse, B, T, C, NH, dtype, workspace, (hipStream_t)stream);
+}

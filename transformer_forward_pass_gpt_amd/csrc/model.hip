@@ -12,6 +12,7 @@
 // (the kernel-fusion item of the llm.c "big stones" list), bit-identical to
 // the separate kernels: 7L + 4 launches.
 #include "common.h"
+#include "model.h"
 
 namespace gpt2 {
 
@@ -33,7 +34,7 @@ int launch_softmax(void*, const void*, int, int, int, int, hipStream_t);
 int launch_matmul(void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
 int launch_matmul_epi(void*, const void*, const void*, const void*, const void*, int, int, int, int, int,
                       hipStream_t);
-int launch_attention(void*, const void*, int, int, int, int, int, hipStream_t);
+int launch_attention(void*, const void*, int, int, int, int, int, hipStream_t, float*);
 int launch_attention_decode(void*, const void*, void*, void*, int, int, int, int, int, int, float*,
                             hipStream_t);
 int64_t decode_workspace_bytes(int B, int C, int NH, int maxT);
@@ -60,46 +61,6 @@ static int64_t decode_part_bytes(int B, int C, int NH, int maxT) {
     return att > split ? att : split;
 }
 
-// Element offsets into the flat parameter buffer.
-struct ParamOffsets {
-    int64_t wte, wpe, ln1_g, ln1_b, qkv_w, qkv_b, ap_w, ap_b, ln2_g, ln2_b, fc_w, fc_b, fp_w, fp_b,
-        lnf_g, lnf_b, total;
-};
-
-static ParamOffsets param_offsets(const gpt2_config& c) {
-    const int64_t C = c.C, L = c.L;
-    ParamOffsets o;
-    int64_t p = 0;
-    o.wte = p;   p += (int64_t)c.Vp * C;
-    o.wpe = p;   p += (int64_t)c.maxT * C;
-    o.ln1_g = p; p += L * C;
-    o.ln1_b = p; p += L * C;
-    o.qkv_w = p; p += L * 3 * C * C;
-    o.qkv_b = p; p += L * 3 * C;
-    o.ap_w = p;  p += L * C * C;
-    o.ap_b = p;  p += L * C;
-    o.ln2_g = p; p += L * C;
-    o.ln2_b = p; p += L * C;
-    o.fc_w = p;  p += L * 4 * C * C;
-    o.fc_b = p;  p += L * 4 * C;
-    o.fp_w = p;  p += L * 4 * C * C;
-    o.fp_b = p;  p += L * C;
-    o.lnf_g = p; p += C;
-    o.lnf_b = p; p += C;
-    o.total = p;
-    return o;
-}
-
-static bool config_ok(const gpt2_config* c) {
-    return c && c->L >= 1 && c->C > 0 && c->NH > 0 && c->C % c->NH == 0 && c->V > 0 &&
-           c->Vp >= c->V && c->maxT > 0 && valid_dtype(c->dtype) && c->ln_eps >= 0.f;
-}
-static bool config_supported(const gpt2_config* c) {
-    return c->C % 8 == 0 && c->C <= 4096 && c->Vp % 8 == 0 && c->Vp <= 131072 &&
-           attention_head_size_ok(c->C / c->NH);
-}
-
-static inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 // Workspace: residual stream x [N,C], LayerNorm output [N,C], qkv [N,3C],
 // attention output [N,C], projection output [N,C], MLP hidden [N,4C].
@@ -175,7 +136,7 @@ static int run_blocks(const Workspace& w, const int32_t* tokens, const char* P, 
         if (kcache)
             CHECK(launch_kv_store((char*)kcache + l * layer_elems * es, (char*)vcache + l * layer_elems * es, w.qkv,
                                   B, T, C, cfg->NH, kv_maxT, dt, s));
-        CHECK(launch_attention(w.att, w.qkv, B, T, C, cfg->NH, dt, s));
+        CHECK(launch_attention(w.att, w.qkv, B, T, C, cfg->NH, dt, s, nullptr));
         // x += attproj(att), the residual add in the GEMM epilogue
         CHECK(launch_matmul_epi(w.x, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), w.x, n, C, C,
                                 EPI_BIAS_RESIDUAL, dt, s));

@@ -211,10 +211,15 @@ __device__ __forceinline__ float block_sum(float x, float* sh) {
 // "State of the Union", kernel summaries) the same pass also writes the
 // cross-entropy of each row, loss = log(sum_{v<V} e^{l_v - m}) + m - l_target,
 // from the max and sum it already holds; probs may then be NULL.
-template <typename T, int PT, int NT>
-__global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, const T* __restrict__ logits,
-                                                     int V, int Vp, const int32_t* __restrict__ targets,
-                                                     float* __restrict__ losses) {
+// BWD (the backward half of that classifier): probs receives instead the
+// gradient of sum_n dscale * loss_n with respect to the logits,
+// dscale * (p_v - [v == target]), 0 in the padding columns. It may overwrite
+// the logits in place: every element of the row (and the target's logit) is
+// read before the first barrier, and every write comes after it.
+template <typename T, int PT, int NT, bool BWD = false>
+__global__ __launch_bounds__(NT) void softmax_kernel(T* probs, const T* logits, int V, int Vp,
+                                                     const int32_t* __restrict__ targets,
+                                                     float* __restrict__ losses, float dscale) {
     constexpr int VE = Vec<T>::N;
     constexpr int NW = NT / 64;
     __shared__ float sh[NW];
@@ -222,6 +227,8 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, cons
     const T* x = logits + row * Vp;
     T* y = probs + row * Vp;
     const int cv = Vp / VE;
+    const int tg = targets ? targets[row] : 0;
+    const float lt = targets ? load_scalar(x + tg) : 0.f;
     float v[PT][VE];
     float m = -INFINITY;
     // Every load of the row is issued before the first use: indices past the
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, cons
             s += v[i][j];
         }
     s = block_sum<NW>(s, sh);
-    if (losses && threadIdx.x == 0) losses[row] = logf(s) + m - load_scalar(x + targets[row]);
+    if (losses && threadIdx.x == 0) losses[row] = logf(s) + m - lt;
     if (!probs) return;
     const float inv = 1.0f / s;
 #pragma unroll
@@ -260,7 +267,12 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* __restrict__ probs, cons
         int idx = threadIdx.x + i * NT;
         if (idx < cv) {
 #pragma unroll
-            for (int j = 0; j < VE; j++) v[i][j] *= inv;
+            for (int j = 0; j < VE; j++) {
+                if constexpr (BWD)
+                    v[i][j] = (v[i][j] * inv - (idx * VE + j == tg ? 1.f : 0.f)) * dscale;
+                else
+                    v[i][j] *= inv;
+            }
             store_vec(y + idx * VE, v[i]);
         }
     }
@@ -275,12 +287,13 @@ __global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out, con
     if (threadIdx.x == 0) *out = a / (float)n;
 }
 
-template <typename T>
+template <typename T, bool BWD = false>
 static void launch_softmax_t(T* probs, const T* logits, int N, int V, int Vp, hipStream_t s,
-                             const int32_t* targets = nullptr, float* losses = nullptr) {
+                             const int32_t* targets = nullptr, float* losses = nullptr, float dscale = 0.f) {
     const int cv = Vp / Vec<T>::N;
     dim3 grid(N);
-#define SM_LAUNCH(P, NT) softmax_kernel<T, P, NT><<<grid, NT, 0, s>>>(probs, logits, V, Vp, targets, losses)
+#define SM_LAUNCH(P, NT) \
+    softmax_kernel<T, P, NT, BWD><<<grid, NT, 0, s>>>(probs, logits, V, Vp, targets, losses, dscale)
     if (cv <= 256) {
         SM_LAUNCH(1, 256);
         return;
@@ -304,6 +317,20 @@ int launch_softmax_loss(void* probs, float* losses, float* mean, const void* log
     else
         launch_softmax_t<float>((float*)probs, (const float*)logits, N, V, Vp, s, targets, losses);
     if (mean) mean_kernel<<<1, 1024, 0, s>>>(mean, losses, N);
+    return launch_status();
+}
+
+// dlogits = dscale * (softmax - onehot(target)) (may overwrite logits), with
+// the per-row losses and their mean (both nullable).
+int launch_crossentropy_backward(void* dlogits, float* losses, float* mean, const void* logits,
+                                 const int32_t* targets, float dscale, int N, int V, int Vp, int dtype,
+                                 hipStream_t s) {
+    if (dtype == GPT2_BF16)
+        launch_softmax_t<bf16, true>((bf16*)dlogits, (const bf16*)logits, N, V, Vp, s, targets, losses, dscale);
+    else
+        launch_softmax_t<float, true>((float*)dlogits, (const float*)logits, N, V, Vp, s, targets, losses,
+                                      dscale);
+    if (mean && losses) mean_kernel<<<1, 1024, 0, s>>>(mean, losses, N);
     return launch_status();
 }
 
@@ -441,4 +468,15 @@ extern "C" int softmax_forward(void* probs, const void* logits, int N, int V, in
         return GPT2_ERR_UNSUPPORTED;
     if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
     return launch_softmax(probs, logits, N, V, Vp, dtype, (hipStream_t)stream);
+}
+
+extern "C" int crossentropy_backward(void* dlogits, float* losses, float* mean_loss, const void* logits,
+                                     const int32_t* targets, float dloss, int N, int V, int Vp, int dtype,
+                                     void* stream) {
+    if (!valid_dtype(dtype) || N < 0 || V < 0 || Vp < V) return GPT2_ERR_INVALID_ARGUMENT;
+    if (N == 0) return GPT2_OK;
+    if (!dlogits || !logits || !targets || V == 0 || (mean_loss && !losses)) return GPT2_ERR_INVALID_ARGUMENT;
+    if (Vp % 8 || Vp > 131072 || !aligned16(logits) || !aligned16(dlogits)) return GPT2_ERR_UNSUPPORTED;
+    return launch_crossentropy_backward(dlogits, losses, mean_loss, logits, targets, dloss, N, V, Vp, dtype,
+                                        (hipStream_t)stream);
 }

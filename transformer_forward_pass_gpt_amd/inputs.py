@@ -133,6 +133,17 @@ def make_tokens(w: Workload) -> np.ndarray:
     return rng.integers(0, w.V, size=shape, dtype=np.int64).astype(np.int32)
 
 
+def make_targets(w: Workload) -> np.ndarray:
+    """Next-token targets int32 [B,T]: position t's target is token t+1 of the
+    same sequence; the last position's is a seeded uniform draw."""
+    tok = make_tokens(w)
+    rng = np.random.default_rng(w.token_seed + 7)
+    tg = np.empty_like(tok)
+    tg[:, :-1] = tok[:, 1:]
+    tg[:, -1] = rng.integers(0, w.V, size=tok.shape[0], dtype=np.int64).astype(np.int32)
+    return tg
+
+
 def make_params(w: Workload) -> np.ndarray:
     """fp32 flat parameters. For bf16 workloads the values are already rounded
     to bf16, so the fp32 array holds exactly what the bf16 buffer holds."""
