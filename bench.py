@@ -8,7 +8,10 @@ adds fused into the GEMM epilogues, final LayerNorm, logits GEMM, vocabulary
 softmax) over one batch of synthetic tokens, with weights, tokens,
 workspace and outputs already resident in HBM. Prints ONE JSON line. With
 ``--workload decode`` a step is one gpt2_decode_step instead: one new token
-for each of 32 sequences against a prefilled key/value cache.
+for each of 32 sequences against a prefilled key/value cache. With ``--mode train`` a step is
+one training step without the optimizer: gpt2_train_forward (forward keeping
+activations, losses and the logit gradient) then gpt2_backward (every
+parameter gradient).
 
 Besides the end-to-end rate it times every kernel of one forward with HIP
 events (the same launches gpt2_forward makes, issued one entry at a time on
@@ -46,8 +49,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="small",
                     help="small (fp32 B4 T1024, default), small_bf16_b4, small_bf16_b8, medium, decode")
+    ap.add_argument("--mode", default="forward", choices=["forward", "train"],
+                    help="train: one step = gpt2_train_forward + gpt2_backward (losses, the logit gradient "
+                         "and every parameter gradient; no optimizer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--cpu-sample-train-tokens", type=int, default=16,
+                    help="train mode: positions of sequence 0 the CPU oracle's training step runs on")
     ap.add_argument("--cpu-sample-seqs", type=int, default=32,
                     help="decode workload: sequences the CPU oracle steps")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -58,7 +66,7 @@ def parse():
 
 
 class Bench:
-    def __init__(self, w, keep_host_cache=False):
+    def __init__(self, w, keep_host_cache=False, train=False):
         import torch
         import transformer_forward_pass_gpt_amd as G
         from transformer_forward_pass_gpt_amd import inputs as I
@@ -89,6 +97,15 @@ class Bench:
             ws = G.workspace_bytes(self.cfg, B, T)
         self.probs = torch.empty_like(self.logits)
         self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.train = train
+        if train:
+            self.targets_np = I.make_targets(w)
+            self.targets = torch.from_numpy(self.targets_np).cuda()
+            self.acts = torch.empty(G.train_acts_bytes(self.cfg, B, T), dtype=torch.uint8, device="cuda")
+            self.tws = torch.empty(G.train_workspace_bytes(self.cfg, B, T), dtype=torch.uint8, device="cuda")
+            self.grads = torch.empty_like(self.params)
+            self.mean_loss = torch.empty(1, dtype=torch.float32, device="cuda")
+            del self.probs, self.ws
 
     def to_dev(self, a):
         if self.w.dtype == self.I.BF16:
@@ -97,7 +114,11 @@ class Bench:
         return self.torch.from_numpy(a).cuda()
 
     def step(self):
-        if self.decode:
+        if self.train:
+            self.G.gpt2_train_forward(self.tokens, self.targets, self.params, self.cfg, self.acts, None,
+                                      self.mean_loss)
+            self.G.gpt2_backward(self.grads, self.tokens, self.params, self.cfg, self.acts, self.tws)
+        elif self.decode:
             self.G.gpt2_decode_step(self.logits, self.probs, self.tokens, self.w.decode_pos, self.kcache,
                                     self.vcache, self.params, self.cfg, self.ws)
         else:
@@ -200,6 +221,122 @@ class Bench:
             out.append(all_runs[0][i][:4] + [ms, all_runs[0][i][5]])
         return out
 
+
+    def train_kernel_timing(self, reps=2):
+        """The entries of one training step (gpt2_train_forward, then
+        gpt2_backward) issued one at a time with HIP events between them, with
+        per-layer activation buffers as in the library (so every layer's
+        operands are as cold as in the real step). A backward entry may run
+        several kernels (the linear backward: operand transposes, two GEMMs,
+        the bias reduction); its record is the whole entry, charged its
+        algorithmic work: 4MNK for the linear backward (dinp and dW), the four
+        products dV, dP, dQ, dK for attention (twice the forward's), bytes read
+        and written once for the rest."""
+        torch, G, I, w = self.torch, self.G, self.I, self.w
+        B, T, C, L, NH, Vp, V = w.B, w.T, w.C, w.L, w.NH, w.Vp, w.V
+        N = B * T
+        es = self.es
+        offs = I.param_offsets(L, C, w.maxT, Vp)
+
+        def view(flat, name, l=None):
+            o, shp = offs[name]
+            t = flat[o:o + int(np.prod(shp))].view(*shp)
+            return t if l is None else t[l]
+
+        P = lambda n, l=None: view(self.params, n, l)  # noqa: E731
+        D = lambda n, l=None: view(self.grads, n, l)  # noqa: E731
+        mk = lambda *s: torch.empty(s, dtype=self.tdtype, device="cuda")  # noqa: E731
+        f32 = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")  # noqa: E731
+        acts = [dict(x=mk(N, C), ln1=mk(N, C), m1=f32(N), r1=f32(N), qkv=mk(N, 3 * C), att=mk(N, C),
+                     lse=f32(B, NH, T), res1=mk(N, C), ln2=mk(N, C), m2=f32(N), r2=f32(N), fch=mk(N, 4 * C),
+                     fchg=mk(N, 4 * C)) for _ in range(L)]
+        xf, lnf, mf, rf = mk(N, C), mk(N, C), f32(N), f32(N)
+        logits = self.logits.view(N, Vp)
+        losses, mean = f32(N), f32(1)
+        dres, dC, d4, dqkv = mk(N, C), mk(N, C), mk(N, 4 * C), mk(N, 3 * C)
+        ws = torch.empty(G.train_workspace_bytes(self.cfg, B, T), dtype=torch.uint8, device="cuda")
+        s = torch.cuda.current_stream()
+        recs = []
+
+        def timed(kind, name, fn, flops=0.0, nbytes=0.0, site=None):
+            if not recs:
+                a = torch.cuda.Event(enable_timing=True)
+                a.record(s)
+            else:
+                a = recs[-1][5]
+            fn()
+            b = torch.cuda.Event(enable_timing=True)
+            b.record(s)
+            recs.append([kind, name, flops, nbytes, a, b, site or name])
+
+        def gemm(out, inp, wt, bias, K, Nc, tag, res=None, Nalg=None):
+            name = G.matmul_kernel_config(N, K, Nc, w.dtype) + ("+residual" if res is not None else "")
+            fn = ((lambda: G.matmul_residual_forward(out, inp, wt, bias, res)) if res is not None
+                  else (lambda: G.matmul_forward(out, inp, wt, bias)))
+            timed("gemm", name, fn, 2.0 * N * (Nalg or Nc) * K, 0.0, "gemm_" + tag)
+
+        def mmb(dinp, dw, db, dout, inp, wt, K, Nc, tag, Nalg=None):
+            timed("gemm", "matmul_backward", lambda: G.matmul_backward(dinp, dw, db, dout, inp, wt, ws),
+                  4.0 * N * (Nalg or Nc) * K, 0.0, "matmul_backward_" + tag)
+
+        ln_bytes = 2 * N * C * es + 2 * C * es + 8 * N
+        lnb_bytes = lambda res: (4 if res else 3) * N * C * es + C * es + 2 * C * es + 8 * N  # noqa: E731
+        attn_flops = 4.0 * B * NH * (C // NH) * T * (T + 1) / 2
+        all_runs = []
+        for _ in range(reps + 1):  # the first pass warms up and is dropped
+            recs.clear()
+            timed("hbm", "encoder", lambda: G.encoder_forward(acts[0]["x"].view(B, T, C), self.tokens, P("wte"),
+                                                               P("wpe")), 0.0, 4 * N + 2 * N * C * es + T * C * es)
+            for l in range(L):
+                a = acts[l]
+                xn = acts[l + 1]["x"] if l + 1 < L else xf
+                timed("hbm", "layernorm", lambda: G.layernorm_forward(a["ln1"], a["x"], P("ln1_g", l), P("ln1_b", l),
+                                                                       w.ln_eps, a["m1"], a["r1"]), 0.0, ln_bytes)
+                gemm(a["qkv"], a["ln1"], P("qkv_w", l), P("qkv_b", l), C, 3 * C, "qkv")
+                timed("mfma", "attention", lambda: G.attention_forward_lse(
+                    a["att"].view(B, T, C), a["lse"], a["qkv"].view(B, T, 3 * C), NH), attn_flops, 0.0)
+                gemm(a["res1"], a["att"], P("attproj_w", l), P("attproj_b", l), C, C, "attproj", res=a["x"])
+                timed("hbm", "layernorm", lambda: G.layernorm_forward(a["ln2"], a["res1"], P("ln2_g", l),
+                                                                       P("ln2_b", l), w.ln_eps, a["m2"], a["r2"]),
+                      0.0, ln_bytes)
+                gemm(a["fch"], a["ln2"], P("fc_w", l), P("fc_b", l), C, 4 * C, "fc")
+                timed("hbm", "gelu", lambda: G.gelu_forward(a["fchg"], a["fch"]), 0.0, 2 * N * 4 * C * es)
+                gemm(xn, a["fchg"], P("fcproj_w", l), P("fcproj_b", l), 4 * C, C, "fcproj", res=a["res1"])
+            timed("hbm", "layernorm", lambda: G.layernorm_forward(lnf, xf, P("lnf_g"), P("lnf_b"), w.ln_eps, mf, rf),
+                  0.0, ln_bytes)
+            gemm(logits, lnf, P("wte"), None, C, Vp, "logits", Nalg=V)
+            timed("hbm", "crossentropy_backward", lambda: G.crossentropy_backward(
+                logits, logits, self.targets.view(N), V, 1.0 / N, losses, mean), 0.0, N * V * es + N * Vp * es)
+            # backward
+            mmb(dC, D("wte"), None, logits, lnf, P("wte"), C, Vp, "logits", Nalg=V)
+            timed("hbm", "layernorm_backward", lambda: G.layernorm_backward(
+                dres, D("lnf_g"), D("lnf_b"), dC, xf, P("lnf_g"), mf, rf, ws), 0.0, lnb_bytes(False))
+            for l in reversed(range(L)):
+                a = acts[l]
+                mmb(d4, D("fcproj_w", l), D("fcproj_b", l), dres, a["fchg"], P("fcproj_w", l), 4 * C, C, "fcproj")
+                timed("hbm", "gelu_backward", lambda: G.gelu_backward(d4, a["fch"], d4), 0.0, 3 * N * 4 * C * es)
+                mmb(dC, D("fc_w", l), D("fc_b", l), d4, a["ln2"], P("fc_w", l), C, 4 * C, "fc")
+                timed("hbm", "layernorm_backward", lambda: G.layernorm_backward(
+                    dres, D("ln2_g", l), D("ln2_b", l), dC, a["res1"], P("ln2_g", l), a["m2"], a["r2"], ws, dres=dres),
+                    0.0, lnb_bytes(True))
+                mmb(dC, D("attproj_w", l), D("attproj_b", l), dres, a["att"], P("attproj_w", l), C, C, "attproj")
+                timed("mfma", "attention_backward", lambda: G.attention_backward(
+                    dqkv.view(B, T, 3 * C), dC.view(B, T, C), a["qkv"].view(B, T, 3 * C), a["att"].view(B, T, C),
+                    a["lse"], NH, ws), 2.0 * attn_flops, 0.0)
+                mmb(dC, D("qkv_w", l), D("qkv_b", l), dqkv, a["ln1"], P("qkv_w", l), C, 3 * C, "qkv")
+                timed("hbm", "layernorm_backward", lambda: G.layernorm_backward(
+                    dres, D("ln1_g", l), D("ln1_b", l), dC, a["x"], P("ln1_g", l), a["m1"], a["r1"], ws, dres=dres),
+                    0.0, lnb_bytes(True))
+            timed("hbm", "encoder_backward", lambda: G.encoder_backward(D("wte"), D("wpe"), dres.view(B, T, C),
+                                                                         self.tokens), 0.0, 3 * N * C * es)
+            torch.cuda.synchronize()
+            all_runs.append([r[:4] + [r[4].elapsed_time(r[5]), r[6]] for r in recs])
+        all_runs = all_runs[1:]
+        out = []
+        for i in range(len(all_runs[0])):
+            ms = float(np.median([run[i][4] for run in all_runs]))
+            out.append(all_runs[0][i][:4] + [ms, all_runs[0][i][5]])
+        return out
 
     def decode_kernel_timing(self, reps=3):
         """The launches of one gpt2_decode_step (batches of at most 32
@@ -418,6 +555,22 @@ def cpu_baseline(b, ntok):
                       "single-threaded C oracle)" % (ntok - 1, ntok, dt)}
 
 
+def cpu_baseline_train(b, ntok):
+    """The oracle's forward + backward, single-threaded, on the first ntok
+    positions of sequence 0 with their targets (a training step on that
+    sample; its gradient is that sample's, not a share of the full batch's)."""
+    import oracle
+    w = b.w
+    tok = b.tokens_np[:1, :ntok]
+    tg = b.targets_np[:1, :ntok]
+    t0 = time.perf_counter()
+    oracle.backward(tok, tg, b.params_np, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps)
+    dt = time.perf_counter() - t0
+    return {"value": round(ntok / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "training step on sequence 0, positions 0..%d with their targets (%d tokens, %.1f s, "
+                      "single-threaded C oracle)" % (ntok - 1, ntok, dt)}
+
+
 def cpu_baseline_decode(b, nseq):
     """The oracle's decode step, single-threaded, for the first nseq of the 32
     sequences (sequences are independent, so this is exactly their share of
@@ -447,7 +600,11 @@ def main():
     w = I.WORKLOADS[args.workload]
     decode = w.decode_pos >= 0
     torch.cuda.set_device(0)
-    b = Bench(w, keep_host_cache=decode and not args.no_cpu_baseline)
+    train = args.mode == "train"
+    if train and decode:
+        print("bench.py: --mode train needs a prefill workload", file=sys.stderr)
+        sys.exit(2)
+    b = Bench(w, keep_host_cache=decode and not args.no_cpu_baseline, train=train)
     if args.profile_kernel:
         profile_kernel(b)
         return
@@ -463,7 +620,13 @@ def main():
     tokens = w.B * (1 if decode else w.T)
     prec = "bf16" if w.dtype == I.BF16 else "fp32"
     size = "124M" if w.C == 768 else "350M"
-    if decode:
+    if train:
+        metric = "train tokens/s GPT-2 %s %s B%d T%d (forward + loss + backward, no optimizer)" % (
+            size, prec, w.B, w.T)
+        wl = "GPT-2 %s %s training step B%d T%d: forward keeping activations, cross-entropy, backward to " \
+             "every parameter gradient" % (size, prec, w.B, w.T)
+        data = "synthetic (seeded uniform tokens, next-token targets, N(0,0.02) weights)"
+    elif decode:
         metric = "decode tokens/s GPT-2 124M bf16, 32 sequences at position %d; HBM GB/s" % w.decode_pos
         wl = "GPT-2 %s %s decode step, %d sequences, KV cache of %d positions (logits + softmax)" % (
             size, prec, w.B, w.decode_pos)
@@ -490,15 +653,19 @@ def main():
     if decode:
         res["config"]["pos"] = w.decode_pos
     if not args.no_kernel_timing:
-        recs = b.decode_kernel_timing() if decode else b.kernel_timing()
+        recs = (b.train_kernel_timing() if train else b.decode_kernel_timing() if decode
+                else b.kernel_timing())
         table, roof = summarize_kernels(recs, w.dtype == I.BF16)
         sites, _ = summarize_kernels(recs, w.dtype == I.BF16, key=5)
         res["roofline"] = roof
         res["kernels"] = table
         res["sites"] = sites
         res["kernel_sum_ms"] = round(sum(r[4] for r in recs), 4)
+    if train:
+        res["mean_loss"] = round(float(b.mean_loss.item()), 6)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = (cpu_baseline_decode(b, args.cpu_sample_seqs) if decode
+        res["cpu_baseline"] = (cpu_baseline_train(b, args.cpu_sample_train_tokens) if train
+                               else cpu_baseline_decode(b, args.cpu_sample_seqs) if decode
                                else cpu_baseline(b, args.cpu_sample_tokens))
     print(json.dumps(res), flush=True)
 

@@ -9,11 +9,14 @@
 // bitwise reproducible (no floating-point atomics).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace gpt2 {
 
 int launch_matmul(void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
+int launch_matmul_splitk_part(float*, const float*, const float*, int, int, int, int, int, hipStream_t);
 
 static constexpr int kBwdThreads = 256;
 
@@ -61,36 +64,68 @@ __global__ __launch_bounds__(kBwdThreads) void gelu_backward_kernel(T* dinp, con
 }
 
 // ------------------------------------------------------- column reduction
-// out[c] = sum_{r < R} part[r * C + c], r ascending within each quarter of
-// the rows and the four quarters added in order: one thread per (column,
-// quarter), 64 columns per workgroup. With acc, out[c] += that sum.
+// out[c] = sum_{r < R} part[r * C + c]: 64 columns x 16 row slices per
+// workgroup (1024 threads); slice k sums rows k*q .. k*q+q-1 in ascending
+// order (q = ceil(R/16)), and the 16 slice sums are added in slice order, so
+// the result is a fixed function of the partials.
+static constexpr int kColSlices = 16;
+
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_kernel(T* out, const float* __restrict__ part, int R, int C) {
-    __shared__ float sh[4][64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__global__ __launch_bounds__(1024) void colsum_kernel(T* out, const float* __restrict__ part, int R, int C) {
+    __shared__ float sh[kColSlices][64];
+    const int lane = threadIdx.x & 63, k = threadIdx.x >> 6;
     const int c = blockIdx.x * 64 + lane;
-    const int q = (R + 3) / 4, r0 = w * q, r1 = min(R, r0 + q);
+    const int q = (R + kColSlices - 1) / kColSlices, r0 = k * q, r1 = min(R, r0 + q);
     float s = 0.f;
     if (c < C) {
         int r = r0;
-        for (; r + 4 <= r1; r += 4) {
-            const float a0 = part[(int64_t)r * C + c], a1 = part[(int64_t)(r + 1) * C + c];
-            const float a2 = part[(int64_t)(r + 2) * C + c], a3 = part[(int64_t)(r + 3) * C + c];
-            s += a0;
-            s += a1;
-            s += a2;
-            s += a3;
+        for (; r + 8 <= r1; r += 8) {
+            float a[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) a[u] = part[(int64_t)(r + u) * C + c];
+#pragma unroll
+            for (int u = 0; u < 8; u++) s += a[u];
         }
         for (; r < r1; r++) s += part[(int64_t)r * C + c];
     }
-    sh[w][lane] = s;
+    sh[k][lane] = s;
     __syncthreads();
-    if (w == 0 && c < C) store_scalar(out + c, ((sh[0][lane] + sh[1][lane]) + sh[2][lane]) + sh[3][lane]);
+    if (k == 0 && c < C) {
+        float t = sh[0][lane];
+#pragma unroll
+        for (int i = 1; i < kColSlices; i++) t += sh[i][lane];
+        store_scalar(out + c, t);
+    }
 }
 
 template <typename T>
 static void launch_colsum(T* out, const float* part, int R, int C, hipStream_t s) {
-    colsum_kernel<T><<<(C + 63) / 64, 256, 0, s>>>(out, part, R, C);
+    colsum_kernel<T><<<(C + 63) / 64, 1024, 0, s>>>(out, part, R, C);
+}
+
+// out[i] = sum_{s < S} part[s * n + i] (s ascending), n = M*N elements, 16
+// bytes of T per thread: the split-k partial products of a weight gradient.
+template <typename T>
+__global__ __launch_bounds__(256) void splitsum_kernel(T* out, const float* __restrict__ part, int S, int64_t n) {
+    constexpr int V = Vec<T>::N;
+    const int64_t nvec = n / V;
+    for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256) {
+        float a[V];
+#pragma unroll
+        for (int j = 0; j < V; j++) a[j] = 0.f;
+        for (int sp = 0; sp < S; sp++) {
+            float b[V];
+            const float* p = part + (int64_t)sp * n + i * V;
+#pragma unroll
+            for (int j = 0; j < V; j += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(p + j);
+                b[j] = x.x; b[j + 1] = x.y; b[j + 2] = x.z; b[j + 3] = x.w;
+            }
+#pragma unroll
+            for (int j = 0; j < V; j++) a[j] += b[j];
+        }
+        store_vec(out + i * V, a);
+    }
 }
 
 // ------------------------------------------------------ LayerNorm backward
@@ -100,11 +135,13 @@ static void launch_colsum(T* out, const float* part, int R, int C, hipStream_t s
 //   dgamma = sum_n dy * xh,   dbeta = sum_n dy.
 // One wavefront per row (the row in registers, loads clamped and masked),
 // rows strided over the grid; each workgroup sums its rows' dgamma and dbeta
-// terms in registers, combines its four wavefronts through LDS in order and
-// writes one row of partials (gpart, bpart: [gridDim.x][C]). dres may be
+// terms in registers, combines its kLnbWaves wavefronts through LDS in order
+// and writes one row of partials (gpart, bpart: [gridDim.x][C]). dres may be
 // dinp (read before written by the same lane).
+static constexpr int kLnbWaves = 8;
+
 template <typename T, int VPL>
-__global__ __launch_bounds__(256) void layernorm_backward_kernel(T* dinp, float* __restrict__ gpart,
+__global__ __launch_bounds__(64 * kLnbWaves) void layernorm_backward_kernel(T* dinp, float* __restrict__ gpart,
                                                                  float* __restrict__ bpart, const T* dres,
                                                                  const T* __restrict__ dout,
                                                                  const T* __restrict__ inp,
@@ -112,7 +149,7 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(T* dinp, float*
                                                                  const float* __restrict__ mean,
                                                                  const float* __restrict__ rstd, int N, int C) {
     constexpr int V = Vec<T>::N;
-    __shared__ float sh[4][64 * V];
+    __shared__ float sh[kLnbWaves][64 * V];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int cv = C / V;
     const float invC = 1.0f / (float)C;
@@ -123,7 +160,7 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(T* dinp, float*
 #pragma unroll
         for (int j = 0; j < V; j++) ag[i][j] = ab[i][j] = 0.f;
     }
-    for (int row = blockIdx.x * 4 + w; row < N; row += gridDim.x * 4) {  // wave-uniform
+    for (int row = blockIdx.x * kLnbWaves + w; row < N; row += gridDim.x * kLnbWaves) {  // wave-uniform
         const T* xr = inp + (int64_t)row * C;
         const T* dr = dout + (int64_t)row * C;
         float x[VPL][V], d[VPL][V], r0[VPL][V];
@@ -132,7 +169,8 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(T* dinp, float*
             const int idx = min(lane + i * 64, cv - 1);
             load_vec(xr + idx * V, x[i]);
             load_vec(dr + idx * V, d[i]);
-            if (dres) load_vec(dres + (int64_t)row * C + idx * V, r0[i]);
+            // unconditional (dout stands in when there is no dres), so no load waits at a branch
+            load_vec((dres ? dres : dout) + (int64_t)row * C + idx * V, r0[i]);
         }
         const float mu = mean[row], rs = rstd[row];
         float a = 0.f, b = 0.f;
@@ -161,14 +199,14 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(T* dinp, float*
 #pragma unroll
                 for (int j = 0; j < V; j++) {
                     float dx = rs * (d[i][j] - a - x[i][j] * b);
-                    if (dres) dx += r0[i][j];
+                    dx += dres ? r0[i][j] : 0.f;
                     x[i][j] = dx;
                 }
                 store_vec(dinp + (int64_t)row * C + idx * V, x[i]);
             }
         }
     }
-    // the workgroup's four partial rows, added in wavefront order
+    // the workgroup's partial rows, added in wavefront order
 #pragma unroll
     for (int p = 0; p < 2; p++) {
         float* dst = p == 0 ? gpart : bpart;
@@ -177,16 +215,21 @@ __global__ __launch_bounds__(256) void layernorm_backward_kernel(T* dinp, float*
 #pragma unroll
             for (int j = 0; j < V; j++) sh[w][lane * V + j] = p == 0 ? ag[i][j] : ab[i][j];
             __syncthreads();
-            for (int e = threadIdx.x; e < 64 * V; e += 256) {
+            for (int e = threadIdx.x; e < 64 * V; e += 64 * kLnbWaves) {
                 const int c = i * 64 * V + e;
-                if (c < C) dst[(int64_t)blockIdx.x * C + c] = ((sh[0][e] + sh[1][e]) + sh[2][e]) + sh[3][e];
+                if (c < C) {
+                    float t = sh[0][e];
+#pragma unroll
+                    for (int k = 1; k < kLnbWaves; k++) t += sh[k][e];
+                    dst[(int64_t)blockIdx.x * C + c] = t;
+                }
             }
             __syncthreads();
         }
     }
 }
 
-static int ln_bwd_grid(int N) { return max(1, min((N + 3) / 4, 512)); }
+static int ln_bwd_grid(int N) { return max(1, min((N + kLnbWaves - 1) / kLnbWaves, 512)); }
 
 int64_t layernorm_backward_workspace_bytes(int N, int C) {
     return 2 * align256((int64_t)ln_bwd_grid(N) * C * 4);
@@ -200,7 +243,8 @@ static void launch_ln_bwd_t(T* dinp, T* dgamma, T* dbeta, const T* dres, const T
     float* bpart = (float*)((char*)ws + align256((int64_t)grid * C * 4));
     const int vpl = (C / Vec<T>::N + 63) / 64;
 #define LNB(P)                                                                                                \
-    layernorm_backward_kernel<T, P><<<grid, 256, 0, s>>>(dinp, gpart, bpart, dres, dout, inp, gamma, mean, rstd, \
+    layernorm_backward_kernel<T, P><<<grid, 64 * kLnbWaves, 0, s>>>(dinp, gpart, bpart, dres, dout, inp, gamma, \
+                                                                    mean, rstd, \
                                                           N, C)
     if (vpl <= 1) LNB(1);
     else if (vpl <= 2) LNB(2);
@@ -275,10 +319,24 @@ static void launch_transpose(T* out, float* colpart, const T* in, int R, int Cc,
 // 64, so the K loop of the pipelined GEMM has no tail.
 static int64_t round64(int64_t n) { return (n + 63) / 64 * 64; }
 
+// Split-k count for the weight gradient (fp32): its OC x C output in 128x96
+// tiles is often far below the chip's 256 CUs while K = Np is deep, so the
+// token range is cut into up to 8 slices (each a whole number of 32-deep
+// k-tiles, at least 256 deep) until there are >= 512 workgroups. bf16 keeps
+// one slice (its partial products would be rounded to bf16).
+static int dw_splits(int N, int C, int OC, int dtype) {
+    if (dtype != GPT2_F32) return 1;
+    const int64_t Np = round64(N), tiles = (int64_t)((OC + 127) / 128) * ((C + 95) / 96);
+    int s = 1;
+    while (s < 8 && tiles * s < 512 && (Np / (2 * s)) % 32 == 0 && Np / (2 * s) >= 256 && Np % (2 * s) == 0) s *= 2;
+    return s;
+}
+
 int64_t matmul_backward_workspace_bytes(int N, int C, int OC, int dtype) {
     const int64_t es = elem_size(dtype), Np = round64(N);
+    const int S = dw_splits(N, C, OC, dtype);
     return align256((int64_t)C * OC * es) + align256((int64_t)OC * Np * es) + align256((int64_t)C * Np * es) +
-           align256(Np / 64 * OC * 4);
+           align256(Np / 64 * OC * 4) + (S > 1 ? align256((int64_t)S * OC * C * 4) : 0);
 }
 
 template <typename T>
@@ -293,6 +351,9 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
     T* inpT = (T*)p;
     p += align256((int64_t)C * Np * es);
     float* bpart = (float*)p;
+    p += align256(Np / 64 * OC * 4);
+    float* wpart = (float*)p;  // split-k partials of dweight (fp32 only)
+    const int S = dw_splits(N, C, OC, dtype);
     int rc = GPT2_OK;
     if (dinp) {
         launch_transpose<T>(wt, nullptr, weight, OC, C, OC, s);  // W^T [C, OC]
@@ -302,8 +363,18 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
     if (dweight || dbias) launch_transpose<T>(doutT, dbias ? bpart : nullptr, dout, N, OC, (int)Np, s);
     if (dweight) {
         launch_transpose<T>(inpT, nullptr, inp, N, C, (int)Np, s);
-        rc = launch_matmul(dweight, doutT, inpT, nullptr, OC, (int)Np, C, dtype, s);
-        if (rc) return rc;
+        if constexpr (std::is_same<T, float>::value) {
+            if (S > 1) {
+                rc = launch_matmul_splitk_part(wpart, doutT, inpT, OC, C, (int)(Np / S), (int)Np, S, s);
+                if (rc) return rc;
+                const int64_t n = (int64_t)OC * C;
+                splitsum_kernel<T><<<stream_grid_bwd(n / 4), 256, 0, s>>>(dweight, wpart, S, n);
+            }
+        }
+        if (S == 1) {
+            rc = launch_matmul(dweight, doutT, inpT, nullptr, OC, (int)Np, C, dtype, s);
+            if (rc) return rc;
+        }
     }
     if (dbias) launch_colsum<T>(dbias, bpart, (int)(Np / 64), OC, s);
     return launch_status();

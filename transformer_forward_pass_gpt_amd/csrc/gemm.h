@@ -243,12 +243,16 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 // EPI: the epilogue (common.h); res [M,N] is the residual of
 // EPI_BIAS_RESIDUAL and may be `out` itself (each element is read and then
 // written by the same thread).
+// SPLITK: workgroup row blockIdx.y multiplies the k-range [y*K, (y+1)*K) of
+// A and W rows lda elements long and writes its product to out + y*split_out
+// (without SPLITK, rows are K long and lda, split_out are unused).
 template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false,
-          int EPI = EPI_BIAS>
+          int EPI = EPI_BIAS, bool SPLITK = false>
 __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, const T* __restrict__ A,
                                                                 const T* __restrict__ W,
                                                                 const T* __restrict__ bias, const T* res, int M,
-                                                                int N, int K, int group_m, int remap) {
+                                                                int N, int K, int group_m, int remap, int lda,
+                                                                int64_t split_out) {
     // RB: bytes of k per tile row (64 or 128); S: LDS stages (S-1 tiles in flight)
     constexpr int NW = WM * WN;
     constexpr int VE = Vec<T>::N;
@@ -273,6 +277,12 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid / WN, wn = wid % WN;
     const int h = lane >> 5, r32 = lane & 31;
+    if constexpr (SPLITK) {
+        A += (int64_t)blockIdx.y * K;
+        W += (int64_t)blockIdx.y * K;
+        out += (int64_t)blockIdx.y * split_out;
+    }
+    const int ld = SPLITK ? lda : K;
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int nwg = tiles_m * tiles_n;
@@ -290,12 +300,12 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
 #pragma unroll
     for (int j = 0; j < LA; j++) {
         const int q = (wid * LA + j) * 64 + lane, row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
-        offA[j] = (int64_t)min(m0 + row, M - 1) * K + lc * VE;
+        offA[j] = (int64_t)min(m0 + row, M - 1) * ld + lc * VE;
     }
 #pragma unroll
     for (int j = 0; j < LB; j++) {
         const int q = (wid * LB + j) * 64 + lane, row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
-        offB[j] = (int64_t)min(n0 + row, N - 1) * K + lc * VE;
+        offB[j] = (int64_t)min(n0 + row, N - 1) * ld + lc * VE;
     }
     auto issue = [&](int stage, int k0) {
         T* sA = smem + stage * STAGE;
@@ -482,12 +492,20 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
 
 template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false>
 static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
-                             int group_m, int remap, hipStream_t s, int epi = EPI_BIAS, const T* res = nullptr) {
+                             int group_m, int remap, hipStream_t s, int epi = EPI_BIAS, const T* res = nullptr,
+                             int lda = 0, int splits = 1, int64_t split_out = 0) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const dim3 grid(nwg, splits);
+    if (lda == 0) lda = K;
 #define GEMM_PIPE_LAUNCH(E)                                                                              \
-    gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, E><<<nwg, WM * WN * 64, 0, s>>>( \
-        out, A, W, bias, res, M, N, K, group_m, remap)
+    gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, E><<<grid, WM * WN * 64, 0, s>>>( \
+        out, A, W, bias, res, M, N, K, group_m, remap, lda, split_out)
+    if (splits > 1 || lda != K) {
+        gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, EPI_BIAS, true>
+            <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap, lda, split_out);
+        return;
+    }
     if (epi == EPI_BIAS_GELU) GEMM_PIPE_LAUNCH(EPI_BIAS_GELU);
     else if (epi == EPI_BIAS_RESIDUAL) GEMM_PIPE_LAUNCH(EPI_BIAS_RESIDUAL);
     else GEMM_PIPE_LAUNCH(EPI_BIAS);

@@ -142,6 +142,19 @@ int launch_matmul(void* out, const void* inp, const void* weight, const void* bi
     return launch_matmul_epi(out, inp, weight, bias, nullptr, N, C, OC, EPI_BIAS, dtype, s);
 }
 
+// Split-k partial products (fp32): part[s] [M,N] = A_s W_s^T for s < splits,
+// where A_s, W_s are the columns s*Kc .. s*Kc+Kc-1 of A [M, lda] and
+// W [N, lda]; one launch, splits x tiles workgroups. For weight gradients,
+// whose M x N output has too few tiles for the chip while K (the tokens) is
+// deep. Kc % 32 == 0.
+int launch_matmul_splitk_part(float* part, const float* A, const float* W, int M, int N, int Kc, int lda,
+                              int splits, hipStream_t s) {
+    if (Kc % 32 || splits < 1 || (int64_t)Kc * splits > lda) return GPT2_ERR_INVALID_ARGUMENT;
+    launch_gemm_pipe<float, 4, 1, 1, 3, 128, 4, 4>(part, A, W, nullptr, M, N, Kc, 8, 1, s, EPI_BIAS, nullptr, lda,
+                                                   splits, (int64_t)M * N);
+    return launch_status();
+}
+
 // Decode-step GEMM on at most 32 rows (K % 8 == 0). part == nullptr:
 // out = epi(inp W^T + bias) in one split; otherwise fp32 partial sums over
 // `splits` k-ranges into part[splits][M][N], bias and epilogue left to the
