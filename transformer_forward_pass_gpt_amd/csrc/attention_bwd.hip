@@ -13,8 +13,8 @@
 // tiles up to it and accumulates dQ (recomputing S and dP). Key tiles above
 // the diagonal are never visited.
 //
-// Every product runs on v_mfma_f32_32x32x2_f32, whatever the storage type:
-// bf16 tiles are widened to fp32 when staged into LDS.
+// fp32 runs every product on v_mfma_f32_32x32x2_f32; bf16 on
+// v_mfma_f32_32x32x16_bf16 with its own operand layouts (below).
 //
 // Register layouts (32x32 MFMA: lane (h, r32) supplies A[r32][k-slot h] and
 // B[k-slot h][r32]; accumulator register v holds row 8*(v/4) + 4*h + v%4,
@@ -26,6 +26,8 @@
 //    row 8*(v/4) + 4*h + v%4, and the other operand is read from LDS at that
 //    row, column r32.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -409,6 +411,351 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(T* __restrict__ dqkv, 
         }
 }
 
+// ------------------------------------------------------------------ bf16
+// The same two walks on v_mfma_f32_32x32x16_bf16 (lane (h, r32) supplies
+// A[r32][8h..8h+7] and B[8h..8h+7][r32]). Operand tiles stay bf16 in LDS:
+//  - head-dim contractions (S, dP): step i covers head dims 16i..16i+15, a
+//    lane's 8 values are one 16-byte run of a row-major tile row;
+//  - the query (key) contractions take P and dS from the accumulator: step j
+//    covers accumulator registers 8j..8j+7, i.e. rows 16j + 8(u/4) + 4h + u%4
+//    for the lane's slots u = 0..7. The other operand is kept TRANSPOSED in
+//    LDS ([head dim][row]) with bits 2 and 3 of the row index swapped inside
+//    each 16, which puts exactly those 8 rows in slots 16j + 8h .. +7: one
+//    16-byte read. P and dS are rounded to bf16 for these products, as the
+//    forward rounds P before P.V.
+__device__ __forceinline__ int bwd_slot(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+// accumulator registers 8j..8j+7 of one lane, as 8 bf16 (the B operand above)
+__device__ __forceinline__ u32x4 pack8(const f32x16& x, int j) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; e++) r[e] = pack_bf16x2(x[8 * j + 2 * e], x[8 * j + 2 * e + 1]);
+    return r;
+}
+
+// Staging of one 64-row tile of a head (rows r0 .. r0+63 of a [rows, ld]
+// tensor, head columns col .. col+HS-1): thread item (quad kq, chunk cv)
+// holds rows 4kq..4kq+3 x 8 head dims; it writes them row-major (rows of
+// LDR) and, when tr is given, transposed with permuted slots (rows of LDT).
+template <int HS>
+struct QuadTile {
+    static constexpr int LDR = HS + 8, LDT = kAB + 8;
+    static constexpr int ITEMS = 16 * (HS / 8);  // quads x chunks
+    u32x4 v[4];
+    __device__ __forceinline__ void load(const bf16* base, int64_t ld, int r0, int Tn, int item) {
+        const int kq = item & 15, cv = item >> 4;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int r = r0 + 4 * kq + e;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(base + (int64_t)min(r, Tn - 1) * ld + cv * 8);
+            v[e] = r < Tn ? x : z;
+        }
+    }
+    __device__ __forceinline__ void store(bf16* row, bf16* tr, int item) const {
+        const int kq = item & 15, cv = item >> 4;
+#pragma unroll
+        for (int e = 0; e < 4; e++) *reinterpret_cast<u32x4*>(row + (4 * kq + e) * LDR + cv * 8) = v[e];
+        if (tr) {
+            const int slot = bwd_slot(4 * kq);
+#pragma unroll
+            for (int d = 0; d < 8; d++) {
+                const int w = d >> 1, sh = 16 * (d & 1);
+                const uint32_t a0 = (v[0][w] >> sh) & 0xffffu, a1 = (v[1][w] >> sh) & 0xffffu;
+                const uint32_t a2 = (v[2][w] >> sh) & 0xffffu, a3 = (v[3][w] >> sh) & 0xffffu;
+                const u32x2 col = {a0 | (a1 << 16), a2 | (a3 << 16)};
+                *reinterpret_cast<u32x2*>(tr + (cv * 8 + d) * LDT + slot) = col;
+            }
+        }
+    }
+};
+
+// dK, dV (bf16): workgroup and wave roles as attn_bwd_dkv_kernel.
+template <int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_bf16_kernel(bf16* __restrict__ dqkv, const bf16* __restrict__ qkv,
+                                                                const bf16* __restrict__ dout,
+                                                                const float* __restrict__ lse,
+                                                                const float* __restrict__ Dg, int Tn, int C, int NH,
+                                                                float sl2, float scale) {
+    using QT = QuadTile<HS>;
+    constexpr int LDR = QT::LDR, LDT = QT::LDT;
+    constexpr int KS = HS / 16;          // 16-deep head-dim steps
+    constexpr int DT = (HS + 31) / 32;   // 32-row tiles of dK^T, dV^T
+    constexpr int RT = kAB * LDR, TT = HS * LDT;
+    constexpr int BUF = 2 * RT + 2 * TT + 4 * kAB;  // Qr, Or, Qt, Ot (bf16) + lse2, D (fp32 = 2 bf16 each)
+    static_assert(HS % 16 == 0, "head size");
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int kc = wid & 1, par = wid >> 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
+    const int kb = blockIdx.y;
+    const int k0 = kb * kAB + kc * 32, key = k0 + r32;
+    const int64_t rs = 3 * (int64_t)C;
+    const bf16* base = qkv + (int64_t)b * Tn * rs;
+    const bf16* dbase = dout + (int64_t)b * Tn * C + hd * HS;
+    const float* lrow = lse + (int64_t)bh * Tn;
+    const float* drow = Dg + (int64_t)bh * Tn;
+    const float L2E = 1.4426950408889634f;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    // this lane's key and value row: B operands of S = Q K^T and dP = dO V^T
+    u32x4 kf[KS], vf[KS];
+#pragma unroll
+    for (int i = 0; i < KS; i++) {
+        const bf16* kr = base + (int64_t)min(key, Tn - 1) * rs + C + hd * HS + 16 * i + 8 * h;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kr);
+        const u32x4 c = *reinterpret_cast<const u32x4*>(kr + C);
+        kf[i] = key < Tn ? a : z4;
+        vf[i] = key < Tn ? c : z4;
+    }
+
+    // staging: threads 0..127 the Q tile, 128..255 the dO tile
+    const int which = tid >> 7, item = tid & 127;
+    const bool stager = item < QT::ITEMS;
+    QT st;
+    float rl = 0.f, rD = 0.f;
+    const bf16* src = which ? dbase : base + hd * HS;
+    const int64_t ld = which ? (int64_t)C : rs;
+    auto gload = [&](int qt) {
+        // unconditional (idle items reload item 0): no load behind a branch
+        st.load(src, ld, qt * kAB, Tn, stager ? item : 0);
+        const int q = min(qt * kAB + (tid & 63), Tn - 1);
+        rl = lrow[q];
+        rD = drow[q];
+    };
+    auto sstore = [&](int buf, int qt) {
+        bf16* b0 = smem + buf * BUF;
+        if (stager) st.store(b0 + which * RT, b0 + 2 * RT + which * TT, item);
+        float* sL = reinterpret_cast<float*>(b0 + 2 * RT + 2 * TT);
+        if (tid < 64) {
+            const bool ok = qt * kAB + tid < Tn;
+            sL[tid] = ok ? rl * L2E : 0.f;
+            sL[kAB + tid] = ok ? rD : 0.f;
+        }
+    };
+
+    f32x16 dv[DT], dk[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) dv[dt] = dk[dt] = f32x16{};
+
+    auto compute = [&](int buf, int qt) {
+        const bf16* sQr = smem + buf * BUF;
+        const bf16* sOr = sQr + RT;
+        const bf16* sQt = sQr + 2 * RT;
+        const bf16* sOt = sQt + TT;
+        const float* sL = reinterpret_cast<const float*>(sQr + 2 * RT + 2 * TT);
+        const float* sD = sL + kAB;
+        const int qb = qt * kAB + par * 32;
+        if (qb + 31 < k0) return;
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int i = 0; i < KS; i++) {
+            const u32x4 qa = *reinterpret_cast<const u32x4*>(sQr + (par * 32 + r32) * LDR + 16 * i + 8 * h);
+            const u32x4 oa = *reinterpret_cast<const u32x4*>(sOr + (par * 32 + r32) * LDR + 16 * i + 8 * h);
+            s = mfma_bf16(qa, kf[i], s);
+            dp = mfma_bf16(oa, vf[i], dp);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = 8 * (v >> 2) + 4 * h + (v & 3), q = qb + m;
+            const bool on = key <= q && q < Tn;
+            const float p = on ? __builtin_amdgcn_exp2f(s[v] * sl2 - sL[par * 32 + m]) : 0.f;
+            s[v] = p;
+            dp[v] = p * (dp[v] - sD[par * 32 + m]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const u32x4 pb = pack8(s, j), sb = pack8(dp, j);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const int d = dt * 32 + r32;
+                const int off = min(d, HS - 1) * LDT + par * 32 + 16 * j + 8 * h;
+                const u32x4 ao = *reinterpret_cast<const u32x4*>(sOt + off);
+                const u32x4 aq = *reinterpret_cast<const u32x4*>(sQt + off);
+                dv[dt] = mfma_bf16(d < HS ? ao : z4, pb, dv[dt]);
+                dk[dt] = mfma_bf16(d < HS ? aq : z4, sb, dk[dt]);
+            }
+        }
+    };
+
+    const int nqt = (Tn + kAB - 1) / kAB;
+    gload(kb);
+    sstore(0, kb);
+    __syncthreads();
+    for (int qt = kb; qt < nqt; qt++) {
+        const int cur = (qt - kb) & 1;
+        if (qt + 1 < nqt) gload(qt + 1);
+        compute(cur, qt);
+        if (qt + 1 < nqt) sstore(cur ^ 1, qt + 1);
+        __syncthreads();
+    }
+
+    float* mg = reinterpret_cast<float*>(smem) + kc * (2 * DT * 16 * 64);
+    if (par == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                mg[((2 * dt) * 16 + v) * 64 + lane] = dv[dt][v];
+                mg[((2 * dt + 1) * 16 + v) * 64 + lane] = dk[dt][v];
+            }
+    }
+    __syncthreads();
+    if (par == 1 || key >= Tn) return;
+    bf16* drow_k = dqkv + ((int64_t)b * Tn + key) * rs + C + hd * HS;
+    bf16* drow_v = drow_k + C;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int d0 = dt * 32 + 8 * g + 4 * h;
+            if (d0 < HS) {
+                float x[4], y[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int v = 4 * g + e;
+                    x[e] = dv[dt][v] + mg[((2 * dt) * 16 + v) * 64 + lane];
+                    y[e] = (dk[dt][v] + mg[((2 * dt + 1) * 16 + v) * 64 + lane]) * scale;
+                }
+                store4(drow_v + d0, x[0], x[1], x[2], x[3]);
+                store4(drow_k + d0, y[0], y[1], y[2], y[3]);
+            }
+        }
+}
+
+// dQ (bf16): workgroup and wave roles as attn_bwd_dq_kernel.
+template <int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(bf16* __restrict__ dqkv, const bf16* __restrict__ qkv,
+                                                               const bf16* __restrict__ dout,
+                                                               const float* __restrict__ lse,
+                                                               const float* __restrict__ Dg, int Tn, int C, int NH,
+                                                               float sl2, float scale) {
+    using QT = QuadTile<HS>;
+    constexpr int LDR = QT::LDR, LDT = QT::LDT;
+    constexpr int KS = HS / 16;
+    constexpr int DT = (HS + 31) / 32;
+    constexpr int RT = kAB * LDR, TT = HS * LDT;
+    constexpr int BUF = 2 * RT + TT;  // Kr, Vr, Kt
+    constexpr int MERGE = 2 * DT * 16 * 64 * 2;  // bf16 units of the fp32 parity merge
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF > MERGE ? 2 * BUF : MERGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int qc = wid & 1, par = wid >> 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
+    const int qt = gridDim.y - 1 - blockIdx.y;
+    const int qw = qt * kAB + qc * 32, q = qw + r32;
+    const int64_t rs = 3 * (int64_t)C;
+    const bf16* base = qkv + (int64_t)b * Tn * rs;
+    const float L2E = 1.4426950408889634f;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    u32x4 qf[KS], df[KS];
+#pragma unroll
+    for (int i = 0; i < KS; i++) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(base + (int64_t)min(q, Tn - 1) * rs + hd * HS + 16 * i + 8 * h);
+        const u32x4 c = *reinterpret_cast<const u32x4*>(dout + ((int64_t)b * Tn + min(q, Tn - 1)) * C + hd * HS +
+                                                        16 * i + 8 * h);
+        qf[i] = q < Tn ? a : z4;
+        df[i] = q < Tn ? c : z4;
+    }
+    const float l2 = q < Tn ? lse[(int64_t)bh * Tn + q] * L2E : 0.f;
+    const float Dq = q < Tn ? Dg[(int64_t)bh * Tn + q] : 0.f;
+
+    // staging: threads 0..127 the K tile (row-major and transposed), 128..255 the V tile
+    const int which = tid >> 7, item = tid & 127;
+    const bool stager = item < QT::ITEMS;
+    QT st;
+    auto gload = [&](int kt) { st.load(base + (1 + which) * C + hd * HS, rs, kt * kAB, Tn, stager ? item : 0); };
+    auto sstore = [&](int buf) {
+        bf16* b0 = smem + buf * BUF;
+        if (stager) st.store(b0 + which * RT, which == 0 ? b0 + 2 * RT : nullptr, item);
+    };
+
+    f32x16 dq[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) dq[dt] = f32x16{};
+
+    auto compute = [&](int buf, int kt) {
+        const bf16* sKr = smem + buf * BUF;
+        const bf16* sVr = sKr + RT;
+        const bf16* sKt = sKr + 2 * RT;
+        const int kbse = kt * kAB + par * 32;
+        if (kbse > qw + 31) return;
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int i = 0; i < KS; i++) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(sKr + (par * 32 + r32) * LDR + 16 * i + 8 * h);
+            const u32x4 va = *reinterpret_cast<const u32x4*>(sVr + (par * 32 + r32) * LDR + 16 * i + 8 * h);
+            s = mfma_bf16(ka, qf[i], s);
+            dp = mfma_bf16(va, df[i], dp);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+            const bool on = kbse + m <= q && q < Tn;
+            const float p = on ? __builtin_amdgcn_exp2f(s[v] * sl2 - l2) : 0.f;
+            dp[v] = p * (dp[v] - Dq);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const u32x4 sb = pack8(dp, j);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const int d = dt * 32 + r32;
+                const u32x4 a =
+                    *reinterpret_cast<const u32x4*>(sKt + min(d, HS - 1) * LDT + par * 32 + 16 * j + 8 * h);
+                dq[dt] = mfma_bf16(d < HS ? a : z4, sb, dq[dt]);
+            }
+        }
+    };
+
+    const int nkt = qt + 1;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt++) {
+        const int cur = kt & 1;
+        if (kt + 1 < nkt) gload(kt + 1);
+        compute(cur, kt);
+        if (kt + 1 < nkt) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    float* mg = reinterpret_cast<float*>(smem) + qc * (DT * 16 * 64);
+    if (par == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) mg[(dt * 16 + v) * 64 + lane] = dq[dt][v];
+    }
+    __syncthreads();
+    if (par == 1 || q >= Tn) return;
+    bf16* drow = dqkv + ((int64_t)b * Tn + q) * rs + hd * HS;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int d0 = dt * 32 + 8 * g + 4 * h;
+            if (d0 < HS) {
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int v = 4 * g + e;
+                    x[e] = (dq[dt][v] + mg[(dt * 16 + v) * 64 + lane]) * scale;
+                }
+                store4(drow + d0, x[0], x[1], x[2], x[3]);
+            }
+        }
+}
+
 int64_t attention_backward_workspace_bytes(int B, int T, int NH) { return ((int64_t)B * NH * T * 4 + 255) & ~255LL; }
 
 template <typename T, int HS>
@@ -419,8 +766,13 @@ static void launch_attn_bwd_hs(T* dqkv, const T* dout, const T* qkv, const T* ou
     const int64_t rows = (int64_t)B * Tn * NH;
     attn_bwd_dot_kernel<T, HS><<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(D, dout, out, B, Tn, C, NH);
     const dim3 grid(B * NH, (Tn + kAB - 1) / kAB);
-    attn_bwd_dkv_kernel<T, HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
-    attn_bwd_dq_kernel<T, HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+    if constexpr (std::is_same<T, bf16>::value) {
+        attn_bwd_dkv_bf16_kernel<HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+        attn_bwd_dq_bf16_kernel<HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+    } else {
+        attn_bwd_dkv_kernel<T, HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+        attn_bwd_dq_kernel<T, HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+    }
 }
 
 template <typename T>
