@@ -9,6 +9,7 @@
 // bitwise reproducible (no floating-point atomics).
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -17,6 +18,7 @@ namespace gpt2 {
 
 int launch_matmul(void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
 int launch_matmul_splitk_part(float*, const float*, const float*, int, int, int, int, int, hipStream_t);
+int launch_matmul_kmajor(float*, const float*, const float*, int, int, int, int, int, bool, bool, int, hipStream_t);
 
 static constexpr int kBwdThreads = 256;
 
@@ -101,6 +103,32 @@ __global__ __launch_bounds__(1024) void colsum_kernel(T* out, const float* __res
 template <typename T>
 static void launch_colsum(T* out, const float* part, int R, int C, hipStream_t s) {
     colsum_kernel<T><<<(C + 63) / 64, 1024, 0, s>>>(out, part, R, C);
+}
+
+// First stage of the column sums of x [R, C] (fp32): part[y][c] = sum of rows
+// 256y .. 256y+255 of column c, four 64-row quarters (one wavefront each, rows
+// ascending) added in order. Grid (ceil(C/64), ceil(R/256)).
+template <typename T>
+__global__ __launch_bounds__(256) void colpart_kernel(float* __restrict__ part, const T* __restrict__ x, int R, int C) {
+    __shared__ float sh[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
+    const int r0 = blockIdx.y * 256 + w * 64, r1 = min(R, r0 + 64);
+    float s = 0.f;
+    if (c < C) {
+        int r = r0;
+        for (; r + 8 <= r1; r += 8) {
+            float a[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) a[u] = load_scalar(x + (int64_t)(r + u) * C + c);
+#pragma unroll
+            for (int u = 0; u < 8; u++) s += a[u];
+        }
+        for (; r < r1; r++) s += load_scalar(x + (int64_t)r * C + c);
+    }
+    sh[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && c < C) part[(int64_t)blockIdx.y * C + c] = ((sh[0][lane] + sh[1][lane]) + sh[2][lane]) + sh[3][lane];
 }
 
 // out[i] = sum_{s < S} part[s * n + i] (s ascending), n = M*N elements, 16
@@ -332,9 +360,18 @@ static int dw_splits(int N, int C, int OC, int dtype) {
     return s;
 }
 
+// The same rule for the k-major fp32 path, whose k-range is the N tokens
+// themselves (N % 32 == 0): slices of N/S rows, each a multiple of 32.
+static int dw_splits_kmajor(int N, int C, int OC) {
+    const int64_t tiles = (int64_t)((OC + 127) / 128) * ((C + 95) / 96);
+    int s = 1;
+    while (s < 8 && tiles * s < 512 && N % (2 * s) == 0 && (N / (2 * s)) % 32 == 0 && N / (2 * s) >= 256) s *= 2;
+    return s;
+}
+
 int64_t matmul_backward_workspace_bytes(int N, int C, int OC, int dtype) {
     const int64_t es = elem_size(dtype), Np = round64(N);
-    const int S = dw_splits(N, C, OC, dtype);
+    const int S = std::max(dw_splits(N, C, OC, dtype), dtype == GPT2_F32 ? dw_splits_kmajor(N, C, OC) : 1);
     return align256((int64_t)C * OC * es) + align256((int64_t)OC * Np * es) + align256((int64_t)C * Np * es) +
            align256(Np / 64 * OC * 4) + (S > 1 ? align256((int64_t)S * OC * C * 4) : 0);
 }
@@ -353,8 +390,35 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
     float* bpart = (float*)p;
     p += align256(Np / 64 * OC * 4);
     float* wpart = (float*)p;  // split-k partials of dweight (fp32 only)
-    const int S = dw_splits(N, C, OC, dtype);
     int rc = GPT2_OK;
+    if constexpr (std::is_same<T, float>::value) {
+        // k-major operands read in place: dinp = dout . W with W as stored
+        // ([OC][C] is k-major for this product), dW = dout^T . inp with both as
+        // stored; the bias from a two-stage column sum of dout
+        const bool km_dinp = OC % 32 == 0, km_dw = N % 32 == 0;
+        if (dinp && km_dinp) {
+            rc = launch_matmul_kmajor(dinp, dout, weight, N, C, OC, OC, C, false, true, 1, s);
+            if (rc) return rc;
+        }
+        if (dweight && km_dw) {
+            const int Sk = dw_splits_kmajor(N, C, OC);
+            rc = launch_matmul_kmajor(Sk > 1 ? wpart : dweight, dout, inp, OC, C, N / Sk, OC, C, true, true, Sk, s);
+            if (rc) return rc;
+            if (Sk > 1) {
+                const int64_t n = (int64_t)OC * C;
+                splitsum_kernel<T><<<stream_grid_bwd(n / 4), 256, 0, s>>>(dweight, wpart, Sk, n);
+            }
+        }
+        if (dbias && km_dw) {
+            const int R = (N + 255) / 256;
+            colpart_kernel<T><<<dim3((OC + 63) / 64, R), 256, 0, s>>>(bpart, dout, N, OC);
+            launch_colsum<T>(dbias, bpart, R, OC, s);
+        }
+        if (km_dinp) dinp = nullptr;  // done
+        if (km_dw) dweight = dbias = nullptr;
+        if (!dinp && !dweight && !dbias) return launch_status();
+    }
+    const int S = dw_splits(N, C, OC, dtype);
     if (dinp) {
         launch_transpose<T>(wt, nullptr, weight, OC, C, OC, s);  // W^T [C, OC]
         rc = launch_matmul(dinp, dout, wt, nullptr, N, OC, C, dtype, s);

@@ -243,16 +243,23 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 // EPI: the epilogue (common.h); res [M,N] is the residual of
 // EPI_BIAS_RESIDUAL and may be `out` itself (each element is read and then
 // written by the same thread).
-// SPLITK: workgroup row blockIdx.y multiplies the k-range [y*K, (y+1)*K) of
-// A and W rows lda elements long and writes its product to out + y*split_out
-// (without SPLITK, rows are K long and lda, split_out are unused).
+// SPLITK: workgroup row blockIdx.y multiplies the k-range [y*K, (y+1)*K) and
+// writes its product to out + y*split_out; A and W rows are then lda and ldb
+// elements long (without SPLITK they are K long and lda, ldb, split_out are
+// unused).
+// TA / TB (fp32): the operand is stored k-major, A as [K][M] (row stride
+// lda), W as [K][N] (row stride ldb): out = A^T-stored . W^T-stored without a
+// transpose pass. Its tile is copied as BK rows of BM (BN) elements and a
+// lane gathers its 4 k-steps with 4 scalar LDS reads; the two lane halves of
+// one read take k-rows 4 apart (k = 8kc + 4h + e), so k-rows with bit 2 set
+// are rotated by 8 chunks (32 banks) and the two halves use disjoint banks.
 template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false,
-          int EPI = EPI_BIAS, bool SPLITK = false>
+          int EPI = EPI_BIAS, bool SPLITK = false, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, const T* __restrict__ A,
                                                                 const T* __restrict__ W,
                                                                 const T* __restrict__ bias, const T* res, int M,
                                                                 int N, int K, int group_m, int remap, int lda,
-                                                                int64_t split_out) {
+                                                                int ldb, int64_t split_out) {
     // RB: bytes of k per tile row (64 or 128); S: LDS stages (S-1 tiles in flight)
     constexpr int NW = WM * WN;
     constexpr int VE = Vec<T>::N;
@@ -265,6 +272,10 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
     constexpr int LA = BM * CH / 64 / NW, LB = BN * CH / 64 / NW;  // copies per wave per tile
     static_assert(LA * 64 * NW == BM * CH && LB * 64 * NW == BN * CH, "tile/wave mismatch");
     constexpr int LPW = LA + LB;
+    static_assert(!(TA || TB) || std::is_same<T, float>::value, "k-major operands: fp32 only");
+    constexpr int CMA = BM * (int)sizeof(T) / 16, CMB = BN * (int)sizeof(T) / 16;  // chunks per k-row
+    constexpr int ROTA = 8, ROTB = 8;
+    static_assert(!(TA || TB) || (CMA >= 16 && CMB >= 16), "k-major tiles need >= 16 chunks per k-row");
     static_assert(LPW * (S - 2) < 64, "vmcnt range");
     constexpr int STAGE = (BM + BN) * BK;  // elements per stage (A tile then W tile)
     constexpr int LDO = BN + VE;           // row stride of the output tile in the epilogue
@@ -278,11 +289,11 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
     const int wm = wid / WN, wn = wid % WN;
     const int h = lane >> 5, r32 = lane & 31;
     if constexpr (SPLITK) {
-        A += (int64_t)blockIdx.y * K;
-        W += (int64_t)blockIdx.y * K;
+        A += (int64_t)blockIdx.y * K * (TA ? lda : 1);
+        W += (int64_t)blockIdx.y * K * (TB ? ldb : 1);
         out += (int64_t)blockIdx.y * split_out;
     }
-    const int ld = SPLITK ? lda : K;
+    const int lda_ = SPLITK || TA ? lda : K, ldb_ = SPLITK || TB ? ldb : K;
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int nwg = tiles_m * tiles_n;
@@ -296,26 +307,42 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
 
     // Chunk q of a tile = row q / CH, slot q % CH; the slot holds logical
     // k-chunk slot ^ ((row / RP) % CH).
+    // k-major operands: chunk q = k-row q / CM, slot q % CM holding the chunk
+    // of m (n) elements (slot - ROT*((row>>2)&1)) mod CM; columns past M (N)
+    // read a clamped (valid) chunk whose results are never stored.
     int64_t offA[LA], offB[LB];
 #pragma unroll
     for (int j = 0; j < LA; j++) {
-        const int q = (wid * LA + j) * 64 + lane, row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
-        offA[j] = (int64_t)min(m0 + row, M - 1) * ld + lc * VE;
+        const int q = (wid * LA + j) * 64 + lane;
+        if constexpr (TA) {
+            const int row = q / CMA, c = (q % CMA + CMA - ROTA * ((row >> 2) & 1)) % CMA;
+            offA[j] = (int64_t)row * lda_ + min(m0 + c * VE, M - VE);
+        } else {
+            const int row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
+            offA[j] = (int64_t)min(m0 + row, M - 1) * lda_ + lc * VE;
+        }
     }
 #pragma unroll
     for (int j = 0; j < LB; j++) {
-        const int q = (wid * LB + j) * 64 + lane, row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
-        offB[j] = (int64_t)min(n0 + row, N - 1) * ld + lc * VE;
+        const int q = (wid * LB + j) * 64 + lane;
+        if constexpr (TB) {
+            const int row = q / CMB, c = (q % CMB + CMB - ROTB * ((row >> 2) & 1)) % CMB;
+            offB[j] = (int64_t)row * ldb_ + min(n0 + c * VE, N - VE);
+        } else {
+            const int row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
+            offB[j] = (int64_t)min(n0 + row, N - 1) * ldb_ + lc * VE;
+        }
     }
     auto issue = [&](int stage, int k0) {
         T* sA = smem + stage * STAGE;
         T* sB = sA + BM * BK;
+        const int64_t ka = TA ? (int64_t)k0 * lda_ : k0, kb = TB ? (int64_t)k0 * ldb_ : k0;
 #pragma unroll
         for (int j = 0; j < LA; j++)
-            copy16_to_lds(A + offA[j] + k0, (lds_void_ptr)(sA + (wid * LA + j) * 64 * VE));
+            copy16_to_lds(A + offA[j] + ka, (lds_void_ptr)(sA + (wid * LA + j) * 64 * VE));
 #pragma unroll
         for (int j = 0; j < LB; j++)
-            copy16_to_lds(W + offB[j] + k0, (lds_void_ptr)(sB + (wid * LB + j) * 64 * VE));
+            copy16_to_lds(W + offB[j] + kb, (lds_void_ptr)(sB + (wid * LB + j) * 64 * VE));
     };
 
     f32x16 acc[TM][TN];
@@ -324,16 +351,37 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
 #pragma unroll
         for (int j = 0; j < TN; j++) acc[i][j] = f32x16{};
 
+    // A k-major tile element (k, m) sits at k*BM + slot*VE + m%VE with slot =
+    // (m/VE + ROT*((k>>2)&1)) mod CM; a fragment's step e is k = (2kc + h)*VE + e.
+    auto tread = [&](const T* sT, int k, int m, auto cm_c, auto rot_c, int width) {
+        constexpr int CM = decltype(cm_c)::value, ROT = decltype(rot_c)::value;
+        // fp32 only (static_assert above): element index = 32-bit word index
+        return reinterpret_cast<const uint32_t*>(sT)[k * width + ((m / VE + ROT * ((k >> 2) & 1)) % CM) * VE + m % VE];
+    };
     auto load_frags = [&](const T* sA, const T* sB, int kc, u32x4 (&fa)[TM], u32x4 (&fb)[TN]) {
 #pragma unroll
         for (int i = 0; i < TM; i++) {
             const int row = wm * TM * 32 + i * 32 + r32;
-            fa[i] = *reinterpret_cast<const u32x4*>(&sA[row * BK + (((2 * kc + h) ^ ((row / RP) % CH)) * VE)]);
+            if constexpr (TA) {
+#pragma unroll
+                for (int e = 0; e < VE; e++)
+                    fa[i][e] = tread(sA, (2 * kc + h) * VE + e, row, std::integral_constant<int, CMA>{},
+                                     std::integral_constant<int, ROTA>{}, BM);
+            } else {
+                fa[i] = *reinterpret_cast<const u32x4*>(&sA[row * BK + (((2 * kc + h) ^ ((row / RP) % CH)) * VE)]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int row = wn * TN * 32 + j * 32 + r32;
-            fb[j] = *reinterpret_cast<const u32x4*>(&sB[row * BK + (((2 * kc + h) ^ ((row / RP) % CH)) * VE)]);
+            if constexpr (TB) {
+#pragma unroll
+                for (int e = 0; e < VE; e++)
+                    fb[j][e] = tread(sB, (2 * kc + h) * VE + e, row, std::integral_constant<int, CMB>{},
+                                     std::integral_constant<int, ROTB>{}, BN);
+            } else {
+                fb[j] = *reinterpret_cast<const u32x4*>(&sB[row * BK + (((2 * kc + h) ^ ((row / RP) % CH)) * VE)]);
+            }
         }
     };
     auto compute = [&](const int stage) {
@@ -500,16 +548,30 @@ static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int 
     if (lda == 0) lda = K;
 #define GEMM_PIPE_LAUNCH(E)                                                                              \
     gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, E><<<grid, WM * WN * 64, 0, s>>>( \
-        out, A, W, bias, res, M, N, K, group_m, remap, lda, split_out)
+        out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out)
     if (splits > 1 || lda != K) {
         gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, EPI_BIAS, true>
-            <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap, lda, split_out);
+            <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out);
         return;
     }
     if (epi == EPI_BIAS_GELU) GEMM_PIPE_LAUNCH(EPI_BIAS_GELU);
     else if (epi == EPI_BIAS_RESIDUAL) GEMM_PIPE_LAUNCH(EPI_BIAS_RESIDUAL);
     else GEMM_PIPE_LAUNCH(EPI_BIAS);
 #undef GEMM_PIPE_LAUNCH
+}
+
+// k-major operand variants (fp32): out [M,N] (+ y*split_out per k-slice y of
+// depth K) from A ([K][M] rows lda apart if TA, else [M][K]) and W ([K][N]
+// rows ldb apart if TB, else [N][K]); bias only without split.
+template <int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE, bool TA, bool TB>
+static void launch_gemm_kmajor(float* out, const float* A, const float* W, const float* bias, int M, int N, int K,
+                               int lda, int ldb, int splits, int64_t split_out, int group_m, int remap,
+                               hipStream_t s) {
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const dim3 grid(nwg, splits);
+    gemm_pipe_kernel<float, WM, WN, TM, TN, RB, S, SCHED, WPE, false, EPI_BIAS, true, TA, TB>
+        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, nullptr, M, N, K, group_m, remap, lda, ldb, split_out);
 }
 
 template <typename T, int WM, int WN, int TM, int TN, int SCHED = 4>

@@ -155,6 +155,29 @@ int launch_matmul_splitk_part(float* part, const float* A, const float* W, int M
     return launch_status();
 }
 
+// fp32 products with k-major operands (no transpose pass): out [M,N] (slice y
+// of `splits` at out + y*M*N) = sum over k of A(k, m) W(k, n), A stored
+// [K][M] (rows lda apart) when ta else [M][K] (lda = K), W stored [K][N]
+// (rows ldb apart) when tb else [N][K]. K (per slice) % 32 == 0; M % 4 == 0
+// when ta, N % 4 == 0 when tb.
+int launch_matmul_kmajor(float* out, const float* A, const float* W, int M, int N, int K, int lda, int ldb, bool ta,
+                         bool tb, int splits, hipStream_t s) {
+    if (K % 32 || splits < 1 || (ta && M % 4) || (tb && N % 4)) return GPT2_ERR_INVALID_ARGUMENT;
+    const int64_t so = (int64_t)M * N;
+    if (ta && tb)
+        launch_gemm_kmajor<4, 1, 1, 3, 128, 4, 4, 0, true, true>(out, A, W, nullptr, M, N, K, lda, ldb, splits, so, 8,
+                                                                1, s);
+    else if (tb)
+        launch_gemm_kmajor<4, 1, 1, 3, 128, 4, 4, 0, false, true>(out, A, W, nullptr, M, N, K, lda, ldb, splits, so, 8,
+                                                                 1, s);
+    else if (ta)
+        launch_gemm_kmajor<4, 1, 1, 3, 128, 4, 4, 0, true, false>(out, A, W, nullptr, M, N, K, lda, ldb, splits, so, 8,
+                                                                 1, s);
+    else
+        return GPT2_ERR_INVALID_ARGUMENT;
+    return launch_status();
+}
+
 // Decode-step GEMM on at most 32 rows (K % 8 == 0). part == nullptr:
 // out = epi(inp W^T + bias) in one split; otherwise fp32 partial sums over
 // `splits` k-ranges into part[splits][M][N], bias and epilogue left to the
