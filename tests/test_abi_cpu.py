@@ -179,3 +179,90 @@ def test_model_validation():
     assert lib.crossentropy_forward(None, None, None, None, None, 0, 200, 256, 0, None) == G.OK
     assert G.generate_workspace_bytes(cfg, 2, 24) >= G.workspace_bytes(cfg, 2, 24)
     assert G.generate_workspace_bytes(cfg, 2, 24) >= G.decode_workspace_bytes(cfg, 2)
+
+
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_backward_workspace_sizes():
+    # LayerNorm backward: dgamma and dbeta partial rows, one per workgroup (<= 512)
+    assert G.layernorm_backward_workspace_size(4096, 768) == 2 * _a256(512 * 768 * 4)
+    assert G.layernorm_backward_workspace_size(16, 64) == 2 * _a256(2 * 64 * 4)
+    # attention backward: D [B,NH,T] fp32
+    assert G.attention_backward_workspace_size(4, 1024, 768, 12) == 4 * 12 * 1024 * 4
+    # linear backward: W^T, dout^T, inp^T (tokens padded to 64), bias partials, split-k partials
+    N, C, OC = 4096, 768, 2304
+    base = _a256(C * OC * 4) + _a256(OC * N * 4) + _a256(C * N * 4) + _a256(N // 64 * OC * 4)
+    assert G.matmul_backward_workspace_size(N, C, OC, 0) == base + _a256(4 * OC * C * 4)  # 4 slices
+    base16 = _a256(C * OC * 2) + _a256(OC * N * 2) + _a256(C * N * 2) + _a256(N // 64 * OC * 4)
+    assert G.matmul_backward_workspace_size(N, C, OC, 1) == base16  # bf16: no split
+    # training activations: per layer x, ln1, att, res1, ln2 [N,C]; qkv [N,3C]; fc, gelu [N,4C];
+    # four fp32 statistics [N]; lse [NH,N]; then xf, lnf [N,C], lnf stats, logits [N,Vp], losses
+    w = I.WORKLOADS["small"]
+    n = w.B * w.T
+    layer = (5 * _a256(n * w.C * 4) + _a256(n * 3 * w.C * 4) + 2 * _a256(n * 4 * w.C * 4) + 4 * _a256(n * 4)
+             + _a256(n * w.NH * 4))
+    tail = 2 * _a256(n * w.C * 4) + 2 * _a256(n * 4) + _a256(n * w.Vp * 4) + _a256(n * 4)
+    assert G.train_acts_bytes(cfg_of(w), w.B, w.T) == w.L * layer + tail
+    assert G.train_workspace_bytes(cfg_of(w), w.B, w.T) >= (6 + 3 + 4) * n * w.C * 4
+
+
+def test_backward_validation_rejects_before_launch():
+    lib = G.load_library()
+    p = ctypes.c_void_p
+    a, b, c, d, e = p(1 << 12), p(1 << 16), p(1 << 20), p(1 << 24), p(1 << 28)
+    odd = p((1 << 12) + 4)
+    big = 1 << 40
+    # fused classifier backward
+    assert lib.crossentropy_backward(None, None, None, b, c, 1.0, 4, 250, 256, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.crossentropy_backward(a, None, d, b, c, 1.0, 4, 250, 256, 0, None) == G.ERR_INVALID_ARGUMENT  # mean w/o losses
+    assert lib.crossentropy_backward(a, None, None, b, c, 1.0, 4, 250, 252, 0, None) == G.ERR_UNSUPPORTED  # Vp % 8
+    assert lib.crossentropy_backward(a, None, None, b, c, 1.0, 4, 300, 256, 0, None) == G.ERR_INVALID_ARGUMENT  # V > Vp
+    assert lib.crossentropy_backward(None, None, None, None, None, 1.0, 0, 250, 256, 0, None) == G.OK
+    # GELU backward
+    assert lib.gelu_backward(a, a, b, 64, 0, None) == G.ERR_INVALID_ARGUMENT  # dinp aliases inp
+    assert lib.gelu_backward(a, b, odd, 64, 0, None) == G.ERR_UNSUPPORTED
+    assert lib.gelu_backward(None, None, None, 0, 1, None) == G.OK
+    # LayerNorm backward
+    args = lambda dinp, dout, N, C, ws: (dinp, None, None, None, dout, b, c, d, d, N, C, 0, e, ws, None)  # noqa: E731
+    assert lib.layernorm_backward(*args(a, a, 4, 64, big)) == G.ERR_INVALID_ARGUMENT  # dinp aliases dout
+    assert lib.layernorm_backward(*args(a, b, 4, 60, big)) == G.ERR_UNSUPPORTED  # C % 8
+    assert lib.layernorm_backward(*args(a, p(1 << 13), 4, 4096, big)) == G.ERR_UNSUPPORTED  # fp32 C > 2048
+    assert lib.layernorm_backward(*args(a, p(1 << 13), 4, 64, 16)) == G.ERR_WORKSPACE_TOO_SMALL
+    assert lib.layernorm_backward(None, None, None, None, None, None, None, None, None, 0, 64, 0, None, 0, None) == G.OK
+    # linear backward
+    assert lib.matmul_backward(a, None, None, a, b, c, 4, 64, 64, 0, e, big, None) == G.ERR_INVALID_ARGUMENT  # alias
+    assert lib.matmul_backward(a, None, None, b, c, None, 4, 64, 64, 0, e, big, None) == G.ERR_INVALID_ARGUMENT  # no W
+    assert lib.matmul_backward(a, None, None, b, c, d, 4, 60, 64, 0, e, big, None) == G.ERR_UNSUPPORTED  # C % 8
+    assert lib.matmul_backward(a, None, None, b, c, d, 4, 64, 64, 0, e, 16, None) == G.ERR_WORKSPACE_TOO_SMALL
+    assert lib.matmul_backward(None, None, None, b, c, d, 4, 64, 64, 0, e, big, None) == G.OK  # nothing asked
+    assert lib.matmul_backward(None, None, None, None, None, None, 0, 64, 64, 0, None, 0, None) == G.OK
+    # attention
+    assert lib.attention_forward_lse(a, None, b, 1, 4, 64, 4, 0, None) == G.ERR_INVALID_ARGUMENT  # no lse
+    assert lib.attention_backward(a, b, c, d, e, 1, 4, 256, 2, 0, p(1 << 30), big, None) == G.ERR_UNSUPPORTED  # hs 128
+    assert lib.attention_backward(a, b, a, d, e, 1, 4, 64, 4, 0, p(1 << 30), big, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.attention_backward(a, b, c, d, e, 1, 4, 64, 4, 0, p(1 << 30), 16, None) == G.ERR_WORKSPACE_TOO_SMALL
+    # encoder backward
+    assert lib.encoder_backward(None, None, a, b, 1, 4, 64, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.encoder_backward(a, None, b, c, 1, 4, 8192, 0, None) == G.ERR_UNSUPPORTED  # fp32 C > 4096
+    assert lib.encoder_backward(None, None, None, None, 0, 4, 64, 0, None) == G.OK
+
+
+def test_training_entries_validation():
+    lib = G.load_library()
+    w = I.WORKLOADS["tiny"]
+    cfg = cfg_of(w)
+    p = ctypes.c_void_p
+    a, b, c, d, e = p(1 << 12), p(1 << 16), p(1 << 20), p(1 << 24), p(1 << 28)
+    big = 1 << 40
+    r = ctypes.byref(cfg)
+    assert lib.gpt2_train_forward(None, None, a, None, c, r, 2, 32, d, big, None) == G.ERR_INVALID_ARGUMENT  # targets
+    assert lib.gpt2_train_forward(None, None, a, b, c, r, 2, 33, d, big, None) == G.ERR_INVALID_ARGUMENT  # T > maxT
+    assert lib.gpt2_train_forward(None, None, a, b, c, r, 2, 32, d, 100, None) == G.ERR_WORKSPACE_TOO_SMALL
+    hs128 = G.make_config(1, 256, 2, 256, 256, 32, 0)  # head size 128: forward only
+    assert lib.gpt2_train_forward(None, None, a, b, c, ctypes.byref(hs128), 1, 4, d, big, None) == G.ERR_UNSUPPORTED
+    assert lib.gpt2_backward(c, a, c, r, 2, 32, d, big, e, big, None) == G.ERR_INVALID_ARGUMENT  # grads == params
+    assert lib.gpt2_backward(b, a, c, r, 2, 32, d, big, e, 100, None) == G.ERR_WORKSPACE_TOO_SMALL
+    assert lib.gpt2_backward(b, a, c, r, 2, 32, d, 100, e, big, None) == G.ERR_WORKSPACE_TOO_SMALL
+    assert lib.gpt2_train_forward(None, None, a, b, c, r, 0, 32, d, 0, None) == G.OK
