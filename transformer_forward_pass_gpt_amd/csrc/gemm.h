@@ -352,21 +352,29 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
         for (int j = 0; j < TN; j++) acc[i][j] = f32x16{};
 
     // A k-major tile element (k, m) sits at k*BM + slot*VE + m%VE with slot =
-    // (m/VE + ROT*((k>>2)&1)) mod CM; a fragment's step e is k = (2kc + h)*VE + e.
-    auto tread = [&](const T* sT, int k, int m, auto cm_c, auto rot_c, int width) {
-        constexpr int CM = decltype(cm_c)::value, ROT = decltype(rot_c)::value;
-        // fp32 only (static_assert above): element index = 32-bit word index
-        return reinterpret_cast<const uint32_t*>(sT)[k * width + ((m / VE + ROT * ((k >> 2) & 1)) % CM) * VE + m % VE];
-    };
+    // (m/VE + ROT*((k>>2)&1)) mod CM. A fragment's step e is k = 8kc + 4h + e
+    // (fp32), whose bit 2 is h: the slot of a lane's column is a per-lane
+    // constant, so every read is that lane offset plus a compile-time one.
+    int colA[TM], colB[TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const int m = wm * TM * 32 + i * 32 + r32;
+        colA[i] = TA ? 4 * h * BM + ((m / VE + ROTA * h) % CMA) * VE + m % VE : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+        const int n = wn * TN * 32 + j * 32 + r32;
+        colB[j] = TB ? 4 * h * BN + ((n / VE + ROTB * h) % CMB) * VE + n % VE : 0;
+    }
     auto load_frags = [&](const T* sA, const T* sB, int kc, u32x4 (&fa)[TM], u32x4 (&fb)[TN]) {
 #pragma unroll
         for (int i = 0; i < TM; i++) {
             const int row = wm * TM * 32 + i * 32 + r32;
             if constexpr (TA) {
+                // fp32 only (static_assert above): element index = 32-bit word index
+                const uint32_t* w = reinterpret_cast<const uint32_t*>(sA) + colA[i] + 8 * kc * BM;
 #pragma unroll
-                for (int e = 0; e < VE; e++)
-                    fa[i][e] = tread(sA, (2 * kc + h) * VE + e, row, std::integral_constant<int, CMA>{},
-                                     std::integral_constant<int, ROTA>{}, BM);
+                for (int e = 0; e < VE; e++) fa[i][e] = w[e * BM];
             } else {
                 fa[i] = *reinterpret_cast<const u32x4*>(&sA[row * BK + (((2 * kc + h) ^ ((row / RP) % CH)) * VE)]);
             }
@@ -375,10 +383,9 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
         for (int j = 0; j < TN; j++) {
             const int row = wn * TN * 32 + j * 32 + r32;
             if constexpr (TB) {
+                const uint32_t* w = reinterpret_cast<const uint32_t*>(sB) + colB[j] + 8 * kc * BN;
 #pragma unroll
-                for (int e = 0; e < VE; e++)
-                    fb[j][e] = tread(sB, (2 * kc + h) * VE + e, row, std::integral_constant<int, CMB>{},
-                                     std::integral_constant<int, ROTB>{}, BN);
+                for (int e = 0; e < VE; e++) fb[j][e] = w[e * BN];
             } else {
                 fb[j] = *reinterpret_cast<const u32x4*>(&sB[row * BK + (((2 * kc + h) ^ ((row / RP) % CH)) * VE)]);
             }
