@@ -35,12 +35,17 @@ __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, flo
     if (row >= N) return;  // wave-uniform
     T* x = inp + (int64_t)row * ldx;  // input rows ldx apart (C, or T*C to take one position per sequence)
     const int cv = C / V;
-    float v[VPL][V];
+    float v[VPL][V], g[VPL][V], bt[VPL][V];
     float s = 0.f;
     // Loads are unconditional (vector index clamped to the row), so every
-    // load of the row is in flight before the first use.
+    // load of the row, and of gamma and beta, is in flight before the first use.
 #pragma unroll
-    for (int i = 0; i < VPL; i++) load_vec(x + min(lane + i * 64, cv - 1) * V, v[i]);
+    for (int i = 0; i < VPL; i++) {
+        const int idx = min(lane + i * 64, cv - 1);
+        load_vec(x + idx * V, v[i]);
+        load_vec(gamma + idx * V, g[i]);
+        load_vec(beta + idx * V, bt[i]);
+    }
     if constexpr (RES) {
         // x <- x + (bias + partials in split order); unused splits read a
         // clamped split and are selected to zero
@@ -105,11 +110,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, flo
     for (int i = 0; i < VPL; i++) {
         int idx = lane + i * 64;
         if (idx < cv) {
-            float g[V], b[V];
-            load_vec(gamma + idx * V, g);
-            load_vec(beta + idx * V, b);
 #pragma unroll
-            for (int j = 0; j < V; j++) v[i][j] = (v[i][j] - mu) * r * g[j] + b[j];
+            for (int j = 0; j < V; j++) v[i][j] = (v[i][j] - mu) * r * g[i][j] + bt[i][j];
             store_vec(y + idx * V, v[i]);
         }
     }
