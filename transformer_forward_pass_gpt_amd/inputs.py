@@ -77,6 +77,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("medium", 24, 1024, 16, 50257, 50304, 1024, 4, 1024, BF16, 103, 203, True),
         Workload("decode", 12, 768, 12, 50257, 50304, 1024, 32, 1, BF16, 104, 201, True,
                  decode_pos=1023, cache_seed=304),
+        # GPT-2 small's width, head size and vocabulary with 2 layers and 64
+        # tokens: small enough for the oracle's whole training step
+        Workload("small_2l", 2, 768, 12, 50257, 50304, 1024, 1, 64, F32, 105, 205, True),
+        Workload("small_2l_bf16", 2, 768, 12, 50257, 50304, 1024, 1, 64, BF16, 105, 205, True),
     ]
 }
 
