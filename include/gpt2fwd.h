@@ -51,7 +51,8 @@ enum {
 /* Token + position embedding (ECE408 Milestone 1 kernel table: Encoder).
  *   out[b,t,:] = wte[tokens[b,t],:] + wpe[t,:]
  * out [B,T,C]; tokens int32 [B,T] (values must lie in [0, rows of wte): not
- * checked on the device); wte [*,C]; wpe [>=T,C]. C % 8 == 0.
+ * checked on the device); wte [*,C]; wpe [>=T,C]. C % 8 == 0,
+ * B*T <= INT32_MAX (else GPT2_ERR_UNSUPPORTED).
  * To embed a single position p for every sequence (decode), pass T = 1 and
  * wpe + p*C. */
 int encoder_forward(void* out, const int32_t* tokens, const void* wte, const void* wpe,

@@ -34,7 +34,7 @@ def announce(*a):
 
 # ----------------------------------------------------------------- encoder
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("B,T,C,V", [(2, 32, 64, 256), (3, 37, 104, 500), (2, 1024, 768, 50304)])
+@pytest.mark.parametrize("B,T,C,V", [(2, 32, 64, 256), (3, 37, 104, 500), (1, 5, 2056, 300), (2, 1024, 768, 50304)])
 def test_encoder(dt, B, T, C, V):
     announce("encoder", dt, B, T, C, V)
     d = DT[dt]

@@ -19,26 +19,45 @@ static unsigned stream_grid(int64_t nvec) {
 
 // out[b,t,:] = wte[tokens[b,t],:] + wpe[t,:]
 // (ECE408 Final Project - GPT-2, Milestone 1, kernel table: Encoder.)
+// One wavefront per row n = b*T + t: the token id is one scalar load shared
+// by the wave, and the lanes stride over the row's 16-byte vectors, kEncU
+// per lane per batch. The position rows do not depend on the token, so their
+// loads are issued before the token arrives; every load of a batch is in
+// flight before the first add (indices clamped into the row; the clamped
+// duplicates are not stored).
+static constexpr int kEncU = 4;
+static constexpr int kEncRows = kThreads / 64;  // rows per workgroup
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void encoder_kernel(T* __restrict__ out,
                                                            const int32_t* __restrict__ tokens,
                                                            const T* __restrict__ wte,
-                                                           const T* __restrict__ wpe, int T_, int C,
-                                                           int64_t nvec) {
+                                                           const T* __restrict__ wpe, int N, int T_, int C) {
     constexpr int V = Vec<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int n = __builtin_amdgcn_readfirstlane(blockIdx.x * kEncRows + (threadIdx.x >> 6));
+    if (n >= N) return;  // wave-uniform
+    const int t = n % T_;
     const int cv = C / V;
-    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < nvec;
-         i += (int64_t)gridDim.x * kThreads) {
-        int64_t n = i / cv;
-        int c = (int)(i - n * cv) * V;
-        int t = (int)(n % T_);
-        int tok = tokens[n];
-        float a[V], b[V];
-        load_vec(wte + (int64_t)tok * C + c, a);
-        load_vec(wpe + (int64_t)t * C + c, b);
+    const T* p = wpe + (int64_t)t * C;
+    T* o = out + (int64_t)n * C;
+    const T* e = nullptr;
+    for (int base = 0; base < cv; base += 64 * kEncU) {
+        float a[kEncU][V], b[kEncU][V];
 #pragma unroll
-        for (int j = 0; j < V; j++) a[j] += b[j];
-        store_vec(out + n * C + c, a);
+        for (int u = 0; u < kEncU; u++) load_vec(p + min(base + lane + 64 * u, cv - 1) * V, b[u]);
+        if (base == 0) e = wte + (int64_t)__builtin_amdgcn_readfirstlane(tokens[n]) * C;
+#pragma unroll
+        for (int u = 0; u < kEncU; u++) load_vec(e + min(base + lane + 64 * u, cv - 1) * V, a[u]);
+#pragma unroll
+        for (int u = 0; u < kEncU; u++) {
+            const int idx = base + lane + 64 * u;
+            if (idx < cv) {
+#pragma unroll
+                for (int j = 0; j < V; j++) a[u][j] += b[u][j];
+                store_vec(o + idx * V, a[u]);
+            }
+        }
     }
 }
 
@@ -79,13 +98,14 @@ __global__ __launch_bounds__(kThreads) void gelu_kernel(T* out, const T* inp, in
 
 int launch_encoder(void* out, const int32_t* tokens, const void* wte, const void* wpe, int B,
                    int T, int C, int dtype, hipStream_t s) {
-    int64_t nvec = (int64_t)B * T * C / (dtype == GPT2_BF16 ? 8 : 4);
+    const int N = B * T;
+    const unsigned grid = (unsigned)((N + kEncRows - 1) / kEncRows);
     if (dtype == GPT2_BF16)
-        encoder_kernel<bf16><<<stream_grid(nvec), kThreads, 0, s>>>(
-            (bf16*)out, tokens, (const bf16*)wte, (const bf16*)wpe, T, C, nvec);
+        encoder_kernel<bf16><<<grid, kThreads, 0, s>>>((bf16*)out, tokens, (const bf16*)wte, (const bf16*)wpe,
+                                                       N, T, C);
     else
-        encoder_kernel<float><<<stream_grid(nvec), kThreads, 0, s>>>(
-            (float*)out, tokens, (const float*)wte, (const float*)wpe, T, C, nvec);
+        encoder_kernel<float><<<grid, kThreads, 0, s>>>((float*)out, tokens, (const float*)wte,
+                                                        (const float*)wpe, N, T, C);
     return launch_status();
 }
 
@@ -121,6 +141,7 @@ extern "C" int encoder_forward(void* out, const int32_t* tokens, const void* wte
     if ((int64_t)B * T * C == 0) return GPT2_OK;
     if (!out || !tokens || !wte || !wpe) return GPT2_ERR_INVALID_ARGUMENT;
     if (C % 8 || !aligned16(out) || !aligned16(wte) || !aligned16(wpe)) return GPT2_ERR_UNSUPPORTED;
+    if ((int64_t)B * T > INT32_MAX) return GPT2_ERR_UNSUPPORTED;  // rows are indexed in 32 bits
     return launch_encoder(out, tokens, wte, wpe, B, T, C, dtype, (hipStream_t)stream);
 }
 
