@@ -48,6 +48,7 @@ template <> struct MfmaS<bf16> {
 };
 
 static constexpr int kBQ = 128;  // queries per workgroup (4 wavefronts x 32)
+static constexpr float kLazyMax = 8.0f;  // running-max slack, log2 units (probabilities < 256)
 static constexpr int kBKV = 64;  // keys per LDS block
 
 // V is kept TRANSPOSED in LDS (Vt[d][key]) so that the k-slots of the P.V
@@ -231,9 +232,17 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
 #pragma unroll
             for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kt][v]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // finite: a processed block always holds key k0 <= every query here
-        const float m_new = fmaxf(m_run, mx * sl2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // The reference max m_run moves only when a block's max exceeds it by
+        // more than kLazyMax (log2 units), so probabilities stay below
+        // 2^kLazyMax and most blocks skip rescaling o. o and l always share
+        // one reference, so o / l is unchanged. The decision is per query (a
+        // multiply by exactly 1 elsewhere), so each query's result depends on
+        // its own scores only; the wave-wide test only skips no-op multiplies.
+        // mx is finite: a processed block always holds key k0 <= every query.
+        const float mb = mx * sl2;
+        const bool grow = mb > m_run + kLazyMax;
+        const float m_new = grow ? mb : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
         float ls = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; kt++)
@@ -246,10 +255,12 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
         ls += __shfl_xor(ls, 32, 64);
         l_run = l_run * alpha + ls;
         m_run = m_new;
+        if (__any(grow)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++)
+            for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-            for (int v = 0; v < 16; v++) o[dt][v] *= alpha;
+                for (int v = 0; v < 16; v++) o[dt][v] *= alpha;
+        }
 
         // O^T += V^T P^T. The k slots of both operands name the same keys.
         if constexpr (F32) {
