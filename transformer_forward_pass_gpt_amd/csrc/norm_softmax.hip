@@ -22,6 +22,26 @@ namespace gpt2 {
 // (rounded) row, as it would after a separate residual add.
 static constexpr int kMaxResSplits = 8;
 
+// Sum over the 64 lanes of a wavefront, the same value in every lane, on
+// DPP lane moves instead of LDS-routed shuffles: lane^1 and lane^2 within each
+// quad, then the half-row and row mirrors (8 and 16 lanes), then the four
+// 16-lane rows read out and added in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_move<0x141>(x);  // row_half_mirror
+    x += dpp_move<0x140>(x);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 template <typename T, int VPL, bool RES>
 __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, float* __restrict__ mean,
                                                         float* __restrict__ rstd, T* __restrict__ inp,
@@ -90,7 +110,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, flo
 #pragma unroll
         for (int j = 0; j < V; j++) s += v[i][j];
     }
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
     const float mu = s / (float)C;
     float ss = 0.f;
 #pragma unroll
@@ -103,7 +123,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, flo
             }
         }
     }
-    ss = wave_sum(ss);
+    ss = wave_sum_dpp(ss);
     const float r = 1.0f / sqrtf(ss / (float)C + eps);
     T* y = out + (int64_t)row * C;
 #pragma unroll
