@@ -47,6 +47,18 @@ template <> struct MfmaS<bf16> {
     }
 };
 
+// Lane l combined with lane l^32 (the other half-wave holds the other 16 keys
+// of the same query), on gfx950's half-wave swap instead of an LDS-routed
+// shuffle. max and + are commutative, so the value is the shuffle's exactly.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 static constexpr int kBQ = 128;  // queries per workgroup (4 wavefronts x 32)
 static constexpr float kLazyMax = 8.0f;  // running-max slack, log2 units (probabilities < 256)
 static constexpr int kBKV = 64;  // keys per LDS block
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
         for (int kt = 0; kt < 2; kt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kt][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = halves_max(mx);
         // The reference max m_run moves only when a block's max exceeds it by
         // more than kLazyMax (log2 units), so probabilities stay below
         // 2^kLazyMax and most blocks skip rescaling o. o and l always share
@@ -252,7 +264,7 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
                 s[kt][v] = p;
                 ls += p;
             }
-        ls += __shfl_xor(ls, 32, 64);
+        ls = halves_sum(ls);
         l_run = l_run * alpha + ls;
         m_run = m_new;
         if (__any(grow)) {
