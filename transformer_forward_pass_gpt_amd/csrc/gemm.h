@@ -260,7 +260,8 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
                                                                 const T* __restrict__ bias, const T* res, int M,
                                                                 int N, int K, int group_m, int remap, int lda,
                                                                 int ldb, int64_t split_out) {
-    // RB: bytes of k per tile row (64 or 128); S: LDS stages (S-1 tiles in flight)
+    // RB: bytes of k per tile row (64 or 128); S: LDS stages (S-1 tiles in flight;
+    // S = 2 is plain double buffering: tile t+1 loads while tile t is multiplied)
     constexpr int NW = WM * WN;
     constexpr int VE = Vec<T>::N;
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
     constexpr int CH = RB / 16;              // 16-byte chunks per tile row
     constexpr int RP = 256 / RB;             // rows sharing one 256-byte bank line
     static_assert(CH == 4 || CH == 8, "64- or 128-byte tile rows");
-    static_assert(S >= 3 && S <= 6, "stages");
+    static_assert(S >= 2 && S <= 6, "stages");
     constexpr int LA = BM * CH / 64 / NW, LB = BN * CH / 64 / NW;  // copies per wave per tile
     static_assert(LA * 64 * NW == BM * CH && LB * 64 * NW == BN * CH, "tile/wave mismatch");
     constexpr int LPW = LA + LB;
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
     for (; kt + S <= nk; kt += S) {
         step(I0{}, kt);
         step(I1{}, kt + 1);
-        step(I2{}, kt + 2);
+        if constexpr (S > 2) step(I2{}, kt + 2);
         if constexpr (S > 3) step(I3{}, kt + 3);
         if constexpr (S > 4) step(I4{}, kt + 4);
         if constexpr (S > 5) step(I5{}, kt + 5);

@@ -35,18 +35,19 @@ struct PipeCfg {
 enum GemmCfg {
     S32 = 0, R64x64, R64x128, R128x96,
     P128x96_S4, P128x96_S5, P256x128_S3A, P128x128_O2,                    // fp32
-    P128x256_O4, P128x256_R3, P256x128_G, P128x128_R4, P128x128_O3, P256x256_W16,  // bf16
+    P128x256_O4, P128x256_R3, P256x128_G, P128x128_R4, P128x128_O3, P256x256_K2,  // bf16
     G_NCFG
 };
 // "_p<S>" = S-stage pipeline; "_o<n>" = registers capped so n wavefronts fit per SIMD (2 or 3
-// workgroups per CU); "_w16" = 16 wavefronts per workgroup; "_k128" = 128-byte k-rows per stage
-// (twice the default bf16 depth); "g" = grouped XCD-aware walk (the fp32 vocabulary tile walks
-// columns instead).
+// workgroups per CU); "_k128" = 128-byte k-rows per stage (twice the default bf16 depth); "g" =
+// grouped XCD-aware walk (the fp32 vocabulary tile walks columns instead). 256x256_p2_k128:
+// 8 wavefronts of 128x64, two stages of 128-byte rows (the L2 sees one 128-byte request per
+// row per k-tile instead of two 64-byte ones; the same bytes in flight as three 64-byte stages).
 static const PipeCfg kCfg[G_NCFG] = {
     {"skinny32", 0},          {"64x64_r", 0},          {"64x128_r", 0},         {"128x96_r", 0},
     {"128x96_p4", 128},       {"128x96_p5", 128},      {"256x128_p3", 128},     {"128x128_p4_o2", 64},
     {"128x256_p3_o4", 64},    {"128x256_p3_k128", 128}, {"256x128_p3g", 128},
-    {"128x128_p4_k128", 128}, {"128x128_p3_o3", 64},   {"256x256_p3_w16", 64},
+    {"128x128_p4_k128", 128}, {"128x128_p3_o3", 64},   {"256x256_p2_k128", 128},
 };
 
 static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
@@ -58,13 +59,13 @@ static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
     }
     // bf16, chosen with operands cold in HBM, as in the forward (a pipeline
     // tuned on cache-resident operands loses 10-30% there): wide projections
-    // use two resident 128x256 workgroups per CU or 256x256 tiles of 16
-    // wavefronts; the narrow (attproj) and deep (fcproj) ones need 128-byte
-    // k-rows per stage, twice the bytes in flight.
-    if (N >= 16384) return P256x256_W16;                        // vocabulary projection
+    // use two resident 128x256 workgroups per CU or two-stage 256x256 tiles;
+    // the narrow (attproj) and deep (fcproj) ones need 128-byte k-rows per
+    // stage, twice the bytes in flight.
+    if (N >= 16384) return P256x256_K2;                         // vocabulary projection
     if (K >= 2048) return M >= 8192 ? P256x128_G : P128x128_R4;    // fcproj
     if (N <= 1024) return M >= 8192 ? P128x256_R3 : P128x128_O3;   // attproj
-    return M >= 8192 ? P128x256_O4 : P256x256_W16;              // qkv, fc
+    return M >= 8192 ? P128x256_O4 : P256x256_K2;               // qkv, fc
 }
 
 static GemmCfg choose_cfg(int M, int N, int K, int dtype) {
@@ -106,9 +107,9 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
                     case P128x128_O3: PIPE(2, 2, 2, 2, 64, 3, 2, 3, 8, 1); break;
                     default:
                         if (N >= 16384)  // vocabulary: column sweep within each row band
-                            PIPE(4, 4, 2, 2, 64, 3, 2, 0, 1, 0);
+                            PIPE(2, 4, 4, 2, 128, 2, 2, 0, 1, 0);
                         else
-                            PIPE(4, 4, 2, 2, 64, 3, 2, 0, 4, 1);
+                            PIPE(2, 4, 4, 2, 128, 2, 2, 0, 4, 1);
                         break;
                 }
             }
