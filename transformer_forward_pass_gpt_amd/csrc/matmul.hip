@@ -35,7 +35,7 @@ struct PipeCfg {
 enum GemmCfg {
     S32 = 0, R64x64, R64x128, R128x96,
     P128x96_S4, P128x96_S5, P256x128_S3A, P128x128_O2,                    // fp32
-    P128x256_O4, P128x256_R3, P256x128_G, P128x128_R4, P128x128_O3, P256x256_K2,  // bf16
+    P128x256_O4, P128x256_R3, P256x128_G, P128x128_R4, P128x128_K3, P256x256_K2, P128x192_K2,  // bf16
     G_NCFG
 };
 // "_p<S>" = S-stage pipeline; "_o<n>" = registers capped so n wavefronts fit per SIMD (2 or 3
@@ -43,11 +43,13 @@ enum GemmCfg {
 // grouped XCD-aware walk (the fp32 vocabulary tile walks columns instead). 256x256_p2_k128:
 // 8 wavefronts of 128x64, two stages of 128-byte rows (the L2 sees one 128-byte request per
 // row per k-tile instead of two 64-byte ones; the same bytes in flight as three 64-byte stages).
+// 128x192_p2_k128: two stages of 128-byte rows in 80 KiB, so two workgroups fill a CU's LDS.
 static const PipeCfg kCfg[G_NCFG] = {
     {"skinny32", 0},          {"64x64_r", 0},          {"64x128_r", 0},         {"128x96_r", 0},
     {"128x96_p4", 128},       {"128x96_p5", 128},      {"256x128_p3", 128},     {"128x128_p4_o2", 64},
     {"128x256_p3_o4", 64},    {"128x256_p3_k128", 128}, {"256x128_p3g", 128},
-    {"128x128_p4_k128", 128}, {"128x128_p3_o3", 64},   {"256x256_p2_k128", 128},
+    {"128x128_p4_k128", 128}, {"128x128_p3_k128", 128}, {"256x256_p2_k128", 128},
+    {"128x192_p2_k128", 128},
 };
 
 static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
@@ -64,7 +66,8 @@ static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
     // stage, twice the bytes in flight.
     if (N >= 16384) return P256x256_K2;                         // vocabulary projection
     if (K >= 2048) return M >= 8192 ? P256x128_G : P128x128_R4;    // fcproj
-    if (N <= 1024) return M >= 8192 ? P128x256_R3 : P128x128_O3;   // attproj
+    if (N <= 1024) return M >= 8192 ? P128x256_R3 : P128x128_K3;   // attproj
+    if (N % 192 == 0) return P128x192_K2;                       // qkv, fc at GPT-2 small widths
     return M >= 8192 ? P128x256_O4 : P256x256_K2;               // qkv, fc
 }
 
@@ -104,7 +107,8 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
                     case P128x256_R3: PIPE(2, 4, 2, 2, 128, 3, 2, 0, 4, 1); break;
                     case P256x128_G: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 8, 1); break;
                     case P128x128_R4: PIPE(2, 2, 2, 2, 128, 4, 2, 0, 8, 1); break;
-                    case P128x128_O3: PIPE(2, 2, 2, 2, 64, 3, 2, 3, 8, 1); break;
+                    case P128x128_K3: PIPE(2, 2, 2, 2, 128, 3, 2, 0, 8, 1); break;
+                    case P128x192_K2: PIPE(2, 2, 2, 3, 128, 2, 2, 2, 4, 1); break;
                     default:
                         if (N >= 16384)  // vocabulary: column sweep within each row band
                             PIPE(2, 4, 4, 2, 128, 2, 2, 0, 1, 0);
