@@ -61,9 +61,9 @@ static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
     }
     // bf16, chosen with operands cold in HBM, as in the forward (a pipeline
     // tuned on cache-resident operands loses 10-30% there): wide projections
-    // use two resident 128x256 workgroups per CU or two-stage 256x256 tiles;
-    // the narrow (attproj) and deep (fcproj) ones need 128-byte k-rows per
-    // stage, twice the bytes in flight.
+    // use two resident two-stage 128x192 workgroups per CU where the width
+    // allows, else 128x256 (two per CU) or two-stage 256x256 tiles; every
+    // 128-byte-row tile halves the L2 requests of a 64-byte-row one.
     if (N >= 16384) return P256x256_K2;                         // vocabulary projection
     if (K >= 2048) return M >= 8192 ? P256x128_G : P128x128_R4;    // fcproj
     if (N <= 1024) return M >= 8192 ? P128x256_R3 : P128x128_K3;   // attproj
