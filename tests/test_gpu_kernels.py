@@ -91,7 +91,9 @@ def test_gelu(dt, n):
 
 # ----------------------------------------------------------------- layernorm
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("N,C", [(64, 64), (37, 104), (4096, 768), (300, 1024), (5, 4096)])
+@pytest.mark.parametrize("N,C", [(64, 64), (37, 104), (4096, 768), (300, 1024), (5, 4096),
+                                 # two rows per wavefront (an odd count of 32-vector groups), odd N
+                                 (37, 768), (33, 384), (7, 256), (9, 1280), (3, 640)])
 def test_layernorm(dt, N, C):
     announce("layernorm", dt, N, C)
     d = DT[dt]

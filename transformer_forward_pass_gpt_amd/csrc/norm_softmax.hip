@@ -141,11 +141,92 @@ __global__ __launch_bounds__(256) void layernorm_kernel(T* __restrict__ out, flo
     }
 }
 
+// Sum over each half-wave (lanes 0-31, 32-63), the half's value in its lanes:
+// the same DPP steps, then the two 16-lane rows of the half added.
+__device__ __forceinline__ float half_sum_dpp(float x) {
+    x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_move<0x141>(x);  // row_half_mirror
+    x += dpp_move<0x140>(x);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+}
+
+// LayerNorm of rows of exactly 32*VPL vectors, two rows per wavefront (lanes
+// 0-31 row 2w, lanes 32-63 row 2w+1), so no lane idles where a row has an odd
+// number of 32-vector groups (bf16 C = 768: 96 vectors, 3 per lane). The
+// statistics are the same two-pass sums, reduced per half-wave. A missing
+// second row (odd N) loads the first row's addresses and stores nothing.
+template <typename T, int VPL>
+__global__ __launch_bounds__(256) void layernorm2_kernel(T* __restrict__ out, float* __restrict__ mean,
+                                                         float* __restrict__ rstd, const T* __restrict__ inp,
+                                                         const T* __restrict__ gamma, const T* __restrict__ beta,
+                                                         int N, int C, float eps, int64_t ldx) {
+    constexpr int V = Vec<T>::N;
+    const int hl = threadIdx.x & 31;
+    const int row0 = 2 * (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+    if (row0 >= N) return;  // wave-uniform
+    const int row = row0 + ((threadIdx.x >> 5) & 1);
+    const bool valid = row < N;
+    const T* x = inp + (int64_t)(valid ? row : row0) * ldx;
+    float v[VPL][V], g[VPL][V], bt[VPL][V];
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        const int idx = hl + i * 32;
+        load_vec(x + idx * V, v[i]);
+        load_vec(gamma + idx * V, g[i]);
+        load_vec(beta + idx * V, bt[i]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; i++)
+#pragma unroll
+        for (int j = 0; j < V; j++) s += v[i][j];
+    s = half_sum_dpp(s);
+    const float mu = s / (float)C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; i++)
+#pragma unroll
+        for (int j = 0; j < V; j++) {
+            const float d = v[i][j] - mu;
+            ss += d * d;
+        }
+    ss = half_sum_dpp(ss);
+    const float r = 1.0f / sqrtf(ss / (float)C + eps);
+    if (!valid) return;
+    T* y = out + (int64_t)row * C;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+#pragma unroll
+        for (int j = 0; j < V; j++) v[i][j] = (v[i][j] - mu) * r * g[i][j] + bt[i][j];
+        store_vec(y + (hl + i * 32) * V, v[i]);
+    }
+    if (hl == 0) {
+        if (mean) mean[row] = mu;
+        if (rstd) rstd[row] = r;
+    }
+}
+
 template <typename T, bool RES>
 static void launch_ln_t(T* out, float* mean, float* rstd, T* inp, const T* g, const T* b, int N, int C,
                         float eps, const float* part, int splits, const T* bias, hipStream_t s, int64_t ldx = 0) {
     if (ldx == 0) ldx = C;
-    const int vpl = (C / Vec<T>::N + 63) / 64;
+    const int cv = C / Vec<T>::N;
+    if (!RES && cv % 64 == 32 && cv <= 160) {  // 1, 3 or 5 groups of 32 vectors: two rows per wavefront
+        const dim3 grid2((N + 7) / 8), block2(256);
+#define LN2_LAUNCH(P) \
+    layernorm2_kernel<T, P><<<grid2, block2, 0, s>>>(out, mean, rstd, inp, g, b, N, C, eps, ldx)
+        if (cv == 32) LN2_LAUNCH(1);
+        else if (cv == 96) LN2_LAUNCH(3);
+        else LN2_LAUNCH(5);
+#undef LN2_LAUNCH
+        return;
+    }
+    const int vpl = (cv + 63) / 64;
     // RES runs on decode-sized batches: one row per workgroup spreads them over CUs
     const int rows = RES ? 1 : 4;
     const dim3 grid((N + rows - 1) / rows), block(64 * rows);
