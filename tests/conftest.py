@@ -17,3 +17,19 @@ def pytest_configure(config):
 def oracle():
     import oracle as _oracle
     return _oracle
+
+
+def pytest_collection_finish(session):
+    """Start the oracle runs of the selected full-size forward checks in
+    background threads, so they overlap the GPU tests collected before them."""
+    if session.config.option.collectonly:
+        return
+    wanted = set()
+    for item in session.items:
+        if getattr(item, "originalname", "") == "test_forward_full_size":
+            callspec = getattr(item, "callspec", None)
+            if callspec is not None and "name" in callspec.params:
+                wanted.add(callspec.params["name"])
+    if wanted:
+        import oracle_bg
+        oracle_bg.prefetch(sorted(wanted))

@@ -64,3 +64,21 @@ def max_abs(x, ref):
 
 def bf16_round(x):
     return I.round_to_bf16(np.asarray(x, np.float32))
+
+
+def tile_rel_max(got, ref, rows=128, cols=128):
+    """Largest norm-relative error over rows x cols tiles of a 2-D array, each
+    tile's norm floored at a tenth of the whole array's rms times the tile's
+    size (so near-zero tiles do not dominate): a tile the GEMMs got wrong
+    shows up here even when the whole-array norm hardly moves."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(r * r))
+    worst = 0.0
+    for i in range(0, r.shape[0], rows):
+        for j in range(0, r.shape[1], cols):
+            rt = r[i:i + rows, j:j + cols]
+            dt = g[i:i + rows, j:j + cols] - rt
+            den = max(np.linalg.norm(rt), 0.1 * rms * np.sqrt(rt.size), 1e-300)
+            worst = max(worst, float(np.linalg.norm(dt) / den))
+    return worst

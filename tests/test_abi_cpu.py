@@ -266,3 +266,74 @@ def test_training_entries_validation():
     assert lib.gpt2_backward(b, a, c, r, 2, 32, d, big, e, 100, None) == G.ERR_WORKSPACE_TOO_SMALL
     assert lib.gpt2_backward(b, a, c, r, 2, 32, d, 100, e, big, None) == G.ERR_WORKSPACE_TOO_SMALL
     assert lib.gpt2_train_forward(None, None, a, b, c, r, 0, 32, d, 0, None) == G.OK
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python binding checks shapes, dtypes and element counts of every
+    tensor before it takes a pointer: CPU tensors reach the placement check
+    only when everything else is right, so each call below must fail on the
+    stated mismatch (ValueError naming the argument), never on placement."""
+    import torch
+    f32, bf, i32 = torch.float32, torch.bfloat16, torch.int32
+
+    def t(*shape, dtype=f32):
+        return torch.zeros(shape, dtype=dtype)
+
+    def rejects(fn, *args, match, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*args, **kw)
+
+    # a call whose tensors are all right fails only on placement
+    rejects(G.matmul_forward, t(4, 16), t(4, 8), t(16, 8), t(16), match="GPU tensor")
+    # linear layer
+    rejects(G.matmul_forward, t(4, 17), t(4, 8), t(16, 8), match="out")          # out size
+    rejects(G.matmul_forward, t(4, 16, dtype=bf), t(4, 8), t(16, 8), match="out")  # out dtype
+    rejects(G.matmul_forward, t(4, 16), t(4, 8), t(16, 9), match="weight")       # weight cols != C
+    rejects(G.matmul_forward, t(4, 16), t(4, 8), t(16, 8, dtype=bf), match="weight")
+    rejects(G.matmul_forward, t(4, 16), t(4, 8), t(16, 8), t(15), match="bias")  # bias length
+    rejects(G.matmul_gelu_forward, t(4, 15), t(4, 8), t(16, 8), match="out")
+    rejects(G.matmul_residual_forward, t(4, 16), t(4, 8), t(16, 8), None, t(4, 15), match="res")
+    rejects(G.matmul_splitk_forward, t(2, 4, 15), t(4, 8), t(16, 8), 2, match="part")
+    # streaming and row kernels
+    rejects(G.gelu_forward, t(10), t(11), match="out")
+    rejects(G.residual_forward, t(10), t(10), t(10, dtype=bf), match="b")
+    rejects(G.layernorm_forward, t(4, 8), t(4, 8), t(7), t(8), match="gamma")
+    rejects(G.layernorm_forward, t(4, 8), t(4, 8), t(8), t(8), mean=t(3), match="mean")
+    rejects(G.layernorm_forward, t(4, 8, dtype=bf), t(4, 8), t(8), t(8), match="out")
+    rejects(G.softmax_forward, t(4, 255), t(4, 256), 200, match="probs")
+    rejects(G.softmax_forward, t(4, 256), t(4, 256), 300, match="V must")
+    rejects(G.attention_forward, t(2, 8, 63), t(2, 8, 192), 4, match="out")
+    rejects(G.attention_forward, t(2, 8, 64), t(2, 8, 190), 4, match="3C")
+    rejects(G.encoder_forward, t(2, 8, 64), t(2, 8), t(100, 64), t(8, 64), match="tokens")  # fp32 ids
+    rejects(G.encoder_forward, t(2, 8, 64), t(2, 8, dtype=i32), t(100, 64), t(7, 64), match="wpe")  # T > rows
+    rejects(G.encoder_forward, t(2, 8, 63), t(2, 8, dtype=i32), t(100, 64), t(8, 64), match="out")
+    rejects(G.crossentropy_forward, t(5), t(4, 256), t(4, dtype=i32), 200, match="losses")
+    rejects(G.crossentropy_forward, t(4), t(4, 256), t(4), 200, match="targets")
+    rejects(G.argmax_forward, t(4, dtype=i32), t(3, 256), 200, match="tokens")
+    # model entries: params, logits and probs against the config
+    w = I.WORKLOADS["tiny"]
+    cfg = cfg_of(w)
+    n = G.param_count(cfg)
+    tok = t(w.B, w.T, dtype=i32)
+    ws = t(G.workspace_bytes(cfg, w.B, w.T), dtype=torch.uint8)
+    lg = t(w.B, w.T, w.Vp)
+    rejects(G.gpt2_forward, lg, None, tok, t(n - 1), cfg, ws, match="params")
+    rejects(G.gpt2_forward, lg, None, tok, t(n, dtype=bf), cfg, ws, match="params")
+    rejects(G.gpt2_forward, t(w.B, w.T, w.Vp, dtype=bf), None, tok, t(n), cfg, ws, match="logits")
+    rejects(G.gpt2_forward, lg, t(w.B, w.T, w.Vp - 8), tok, t(n), cfg, ws, match="probs")
+    rejects(G.gpt2_forward, lg, None, tok.float(), t(n), cfg, ws, match="tokens")
+    rejects(G.gpt2_forward, lg, None, tok, t(n), cfg, ws[:100], match="workspace")
+    rejects(G.gpt2_forward, lg, None, tok, t(n), cfg, ws, match="GPU tensor")
+    hs = w.C // w.NH
+    kc = t(w.L, w.B, w.NH, w.maxT, hs)
+    dws = t(G.decode_workspace_bytes(cfg, w.B), dtype=torch.uint8)
+    rejects(G.gpt2_decode_step, t(w.B, w.Vp), None, t(w.B, dtype=i32), 3, kc, t(w.L, w.B, w.NH, w.maxT - 1, hs),
+            t(n), cfg, dws, match="vcache")
+    rejects(G.gpt2_decode_step, t(w.B, w.Vp + 8), None, t(w.B, dtype=i32), 3, kc, kc, t(n), cfg, dws,
+            match="logits")
+    # backward entries
+    rejects(G.matmul_backward, t(4, 8), t(16, 8), t(16), t(4, 16), t(4, 9), t(16, 8), t(1), match="inp")
+    rejects(G.attention_forward_lse, t(2, 8, 64), t(2, 4, 7), t(2, 8, 192), 4, match="lse")
+    rejects(G.gelu_backward, t(10), t(10), t(9), match="dout")
+    rejects(G.crossentropy_backward, t(4, 255), t(4, 256), t(4, dtype=i32), 200, 0.25, match="dlogits")
+

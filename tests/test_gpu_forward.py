@@ -6,8 +6,10 @@ Bars (the stated parity targets):
   fp32 logits: max|d| <= 1e-3 and ||d||/||ref|| <= 1e-4; top-1 100% on tiny
   bf16 logits: ||d||/||ref|| <= 2e-2
 At the 124M/350M sizes the GPU runs the whole batch and the oracle runs the
-first positions of sequence 0; by the causal invariant those positions are
-exactly what the full-length oracle would produce.
+last sequence (every position at 124M, the first 512 at 350M); by the causal
+invariant a prefix of positions is exactly what the full-length oracle would
+produce. bf16 checks add per-position, per-tile and elementwise bounds to the
+norm bound (check_full_rows).
 """
 import sys
 
@@ -18,7 +20,7 @@ import oracle
 import transformer_forward_pass_gpt_amd as G
 from transformer_forward_pass_gpt_amd import inputs as I
 
-from gpu_util import dev, dev_int, empty, host, host_bits, max_abs, rel_err
+from gpu_util import dev, dev_int, empty, host, host_bits, max_abs, rel_err, tile_rel_max
 
 pytestmark = pytest.mark.gpu
 
@@ -52,11 +54,19 @@ class Model:
 
 
 def check_logits(w, got, ref):
+    """The stated logits bars; for bf16 also per position and elementwise
+    (|d| <= 2^-7 |ref| + 6 * 2e-2 * rms of the position's logits: see
+    check_full_rows)."""
     got = got[..., :w.V]
     ref = ref[..., :w.V]
     assert np.all(np.isfinite(got))
     if w.dtype == I.BF16:
         assert rel_err(got, ref) <= 2e-2
+        g = got.reshape(-1, w.V).astype(np.float64)
+        r = ref.reshape(-1, w.V).astype(np.float64)
+        row_rms = np.sqrt(np.mean(r * r, axis=1))
+        assert np.all(np.linalg.norm(g - r, axis=1) <= 2e-2 * np.linalg.norm(r, axis=1))
+        assert np.all(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 6 * 2e-2 * row_rms[:, None])
     else:
         assert max_abs(got, ref) <= 1e-3
         assert rel_err(got, ref) <= 1e-4
@@ -159,13 +169,58 @@ def test_forward_invariants_bitwise(name):
     assert np.array_equal(host_bits(l3)[0], l0b[0])
 
 
-FULL = [("small", 64), ("small_bf16_b8", 64), ("small_bf16_b4", 64), ("medium", 32)]
+FULL = ["small", "small_bf16_b8", "small_bf16_b4", "medium"]
 
 
-@pytest.mark.parametrize("name,t_check", FULL)
-def test_forward_full_size(name, t_check):
-    """Full batch at T=1024 on the GPU; oracle on the first t_check positions
-    of sequence 0; causal invariant checked at full length."""
+def check_full_rows(w, gl, gp, rl, rp):
+    """Full-size logits and probabilities of one sequence against the oracle.
+
+    fp32: the stated bars (max|d| <= 1e-3, ||d||/||ref|| <= 1e-4) on the whole
+    sequence; probabilities max|d| <= 1e-6; top-1 equal wherever the oracle's
+    top-1/top-2 gap exceeds twice the logit bound.
+    bf16: ||d||/||ref|| <= 2e-2 on the whole sequence AND on every position
+    (row) and every 128x128 tile; elementwise |d| <= 2^-7 |ref| + 6 * 2e-2 *
+    rms(ref row): a row whose error has the 2e-2 norm bound has an error
+    standard deviation of at most 2e-2 rms, and 6 standard deviations cover
+    the largest of the ~5e7 logits of a sequence; 2^-7 |ref| covers the output
+    rounding (2^-9) of large logits. Top-1 equal wherever the oracle's gap
+    exceeds twice that row's elementwise bound. Probabilities: norm-relative
+    2e-2."""
+    V = w.V
+    g = gl[:, :V].astype(np.float64)
+    r = rl[:, :V].astype(np.float64)
+    assert np.all(np.isfinite(g))
+    top2 = np.sort(r, axis=1)[:, -2:]
+    gap = top2[:, 1] - top2[:, 0]
+    same = g.argmax(1) == r.argmax(1)
+    if w.dtype == I.F32:
+        assert max_abs(g, r) <= 1e-3
+        assert rel_err(g, r) <= 1e-4
+        assert max_abs(gp, rp) <= 1e-6
+        decided = gap > 2e-3
+    else:
+        assert rel_err(g, r) <= 2e-2
+        row_rms = np.sqrt(np.mean(r * r, axis=1))
+        row_rel = np.linalg.norm(g - r, axis=1) / np.linalg.norm(r, axis=1)
+        assert row_rel.max() <= 2e-2, (int(row_rel.argmax()), float(row_rel.max()))
+        assert tile_rel_max(g, r) <= 2e-2
+        bound = 2.0 ** -7 * np.abs(r) + 6 * 2e-2 * row_rms[:, None]
+        assert np.all(np.abs(g - r) <= bound)
+        assert rel_err(gp, rp) <= 2e-2
+        decided = gap > 2 * (2.0 ** -7 * top2[:, 1] + 6 * 2e-2 * row_rms)
+    assert decided.sum() >= 1
+    assert np.all(same[decided]), np.nonzero(~same & decided)[0][:10]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size(name):
+    """Full batch at T=1024 on the GPU. The oracle runs the last sequence of
+    the batch (all 1024 positions; 512 for the 350M model), started in the
+    background when the tests were collected, and every position of it is
+    compared: late rows of every composed GEMM and attention over up to 1024
+    keys inside the composed forward. The causal and batch invariants are
+    checked at full size."""
+    import oracle_bg
     announce("forward-full", name)
     w = I.WORKLOADS[name]
     m = Model(w)
@@ -174,14 +229,8 @@ def test_forward_full_size(name, t_check):
     gl = host(logits)
     assert np.all(np.isfinite(gl[..., :w.V]))
     assert np.all(gl[..., w.V:] == 0)
-    rl, rp, _ = oracle.forward(tok[:1, :t_check], m.params_np, w.L, w.C, w.NH, w.V, w.Vp, w.maxT,
-                               w.ln_eps)
-    check_logits(w, gl[:1, :t_check], rl)
-    gp = host(probs)[:1, :t_check]
-    if w.dtype == I.F32:
-        assert max_abs(gp, rp) <= 1e-6
-    else:
-        assert rel_err(gp, rp) <= 2e-2
+    seq, t_check, rl, rp = oracle_bg.get(name)
+    check_full_rows(w, gl[seq, :t_check], host(probs)[seq, :t_check], rl, rp)
     # causal + batch invariants at full size
     tok2 = tok.copy()
     t = 700
