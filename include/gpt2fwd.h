@@ -218,6 +218,21 @@ int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens, int pos,
                      const gpt2_config* cfg /* host */, int B, void* workspace,
                      int64_t workspace_bytes, void* stream);
 
+/* gpt2_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The step's scratch lives in a device
+ * array of GPT2_DECODE_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends; the call itself allocates nothing. Arguments as
+ * gpt2_decode_step. Returns GPT2_ERR_WORKSPACE_TOO_SMALL (before any launch)
+ * when gpt2_decode_workspace_bytes(cfg, B) exceeds GPT2_DECODE_SCRATCH_BYTES
+ * (GPT-2 small needs ~2 MB at B = 32, GPT-2 medium ~2.6 MB). Every call on one
+ * GPU shares that GPU's array: calls that may overlap on one device (other
+ * streams, other host threads) race and must be serialised by the caller. */
+#define GPT2_DECODE_SCRATCH_BYTES (8 << 20)
+int gpt2_decode_step_noalloc(void* logits, void* probs, const int32_t* tokens, int pos,
+                             void* kcache, void* vcache, const void* params,
+                             const gpt2_config* cfg /* host */, int B, void* stream);
+
 /* ------------------------------------------------------------ generation */
 /* Greedy choice (the next-token step of autoregressive prediction, optdl2025
  * NanoGPT project): tokens[n] = argmax over v < V of logits[n, v], the lowest

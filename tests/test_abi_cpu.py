@@ -337,3 +337,26 @@ def test_binding_rejects_mismatched_tensors():
     rejects(G.gelu_backward, t(10), t(10), t(9), match="dout")
     rejects(G.crossentropy_backward, t(4, 255), t(4, 256), t(4, dtype=i32), 200, 0.25, match="dlogits")
 
+
+def test_decode_noalloc_rejects_before_launch():
+    """gpt2_decode_step_noalloc validates like gpt2_decode_step and refuses a
+    step whose scratch would exceed the library's fixed array, before it
+    touches the device (no GPU here)."""
+    lib = G.load_library()
+    p = ctypes.c_void_p
+    a, b, c = p(1 << 12), p(1 << 16), p(1 << 20)
+    tiny = cfg_of(I.WORKLOADS["tiny"])
+    assert lib.gpt2_decode_step_noalloc(a, None, b, 32, c, c, c, ctypes.byref(tiny), 2, None) \
+        == G.ERR_INVALID_ARGUMENT  # pos == maxT
+    assert lib.gpt2_decode_step_noalloc(a, a, b, 3, c, c, c, ctypes.byref(tiny), 2, None) \
+        == G.ERR_INVALID_ARGUMENT  # probs aliases logits
+    assert lib.gpt2_decode_step_noalloc(None, None, None, 3, None, None, None, ctypes.byref(tiny), 0, None) == G.OK
+    # a step needing more than the fixed scratch: 4096 channels, 64 sequences
+    big = G.make_config(2, 4096, 32, 50257, 50304, 2048, 0)
+    assert G.decode_workspace_bytes(big, 64) > G.DECODE_SCRATCH_BYTES
+    assert lib.gpt2_decode_step_noalloc(a, None, b, 5, c, c, c, ctypes.byref(big), 64, None) \
+        == G.ERR_WORKSPACE_TOO_SMALL
+    # GPT-2 small and medium at 32 sequences fit
+    for name in ("decode", "medium"):
+        w = I.WORKLOADS[name]
+        assert G.decode_workspace_bytes(cfg_of(w), 32) <= G.DECODE_SCRATCH_BYTES

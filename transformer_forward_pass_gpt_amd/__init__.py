@@ -39,8 +39,10 @@ EXPORTS = (
     "crossentropy_backward", "gelu_backward", "layernorm_backward_workspace_size", "layernorm_backward",
     "matmul_backward_workspace_size", "matmul_backward", "attention_forward_lse",
     "attention_backward_workspace_size", "attention_backward", "encoder_backward", "gpt2_train_acts_bytes",
-    "gpt2_train_workspace_bytes", "gpt2_train_forward", "gpt2_backward",
+    "gpt2_train_workspace_bytes", "gpt2_train_forward", "gpt2_backward", "gpt2_decode_step_noalloc",
 )
+
+DECODE_SCRATCH_BYTES = 8 << 20  # GPT2_DECODE_SCRATCH_BYTES of the header
 
 
 class GPT2Error(RuntimeError):
@@ -116,6 +118,7 @@ def load_library(path: str = LIB_PATH):
             "gpt2_train_workspace_bytes": (I64, [CP, I, I]),
             "gpt2_train_forward": (I, [P, P, P, P, P, CP, I, I, P, I64, P]),
             "gpt2_backward": (I, [P, P, P, CP, I, I, P, I64, P, I64, P]),
+            "gpt2_decode_step_noalloc": (I, [P, P, P, I, P, P, P, CP, I, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -490,6 +493,24 @@ def gpt2_decode_step(logits, probs, tokens, pos, kcache, vcache, params, cfg: Co
         _dev(logits, "logits"), _dev(probs, "probs"), _dev(tokens, "tokens"), int(pos),
         _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(params, "params"), ctypes.byref(cfg), B,
         _dev(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
+    return logits
+
+
+def gpt2_decode_step_noalloc(logits, probs, tokens, pos, kcache, vcache, params, cfg: Config, stream=None):
+    """gpt2_decode_step with the library's own device scratch instead of a
+    workspace (for callers that cannot allocate); calls that overlap on one
+    GPU race."""
+    lib = load_library()
+    _int32(tokens, "tokens", ndim=1)
+    B = tokens.shape[0]
+    _model_args(cfg, params, None, 0)
+    _cache_args(cfg, kcache, vcache, B)
+    _chk(logits, "logits", dtype=_tdt(cfg.dtype), numel=B * cfg.Vp)
+    _chk(probs, "probs", dtype=_tdt(cfg.dtype), numel=B * cfg.Vp, optional=True)
+    _check("gpt2_decode_step_noalloc", lib.gpt2_decode_step_noalloc(
+        _dev(logits, "logits"), _dev(probs, "probs"), _dev(tokens, "tokens"), int(pos),
+        _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(params, "params"), ctypes.byref(cfg), B,
+        _stream(stream)))
     return logits
 
 

@@ -11,6 +11,8 @@
 // residual adds run in the epilogues of the fc, attproj and fcproj GEMMs
 // (the kernel-fusion item of the llm.c "big stones" list), bit-identical to
 // the separate kernels: 7L + 4 launches.
+#include <mutex>
+
 #include "common.h"
 #include "model.h"
 
@@ -269,6 +271,63 @@ extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens
     const int C = cfg->C, NH = cfg->NH, es = elem_size(cfg->dtype);
     Workspace w = carve((char*)workspace, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT));
     if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    return decode_step_impl(logits, probs, tokens, pos, kcache, vcache, params, cfg, B, w, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------ decode without allocation
+// The decode step's workspace (residual stream, LayerNorm output, qkv,
+// attention output, MLP hidden and the fp32 partials of the attention chunks
+// and the split-k projections) in a file-scope device array instead of a
+// caller buffer. Every GPU the library runs on holds its own copy until the
+// process ends. Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[GPT2_DECODE_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (resolved on the first call
+// made with the device current), or nullptr with the HIP error recorded.
+static void* scratch_address() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        set_last_hip_error(e != hipSuccess ? (int)e : (int)hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            set_last_hip_error(e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol);
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+extern "C" int gpt2_decode_step_noalloc(void* logits, void* probs, const int32_t* tokens, int pos,
+                                        void* kcache, void* vcache, const void* params,
+                                        const gpt2_config* cfg, int B, void* stream) {
+    if (!config_ok(cfg) || B < 0) return GPT2_ERR_INVALID_ARGUMENT;
+    if (B == 0) return GPT2_OK;
+    if (!logits || !tokens || !params || !kcache || !vcache || pos < 0 || pos >= cfg->maxT)
+        return GPT2_ERR_INVALID_ARGUMENT;
+    if (!config_supported(cfg) || !aligned16(logits) || !aligned16(params) || !aligned16(kcache) ||
+        !aligned16(vcache) || (probs && !aligned16(probs)))
+        return GPT2_ERR_UNSUPPORTED;
+    if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
+    const int C = cfg->C, NH = cfg->NH, es = elem_size(cfg->dtype);
+    const int64_t need = carve(nullptr, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT)).bytes;
+    if (need > (int64_t)GPT2_DECODE_SCRATCH_BYTES) return GPT2_ERR_WORKSPACE_TOO_SMALL;
+    void* base = scratch_address();
+    if (!base) return GPT2_ERR_HIP;
+    // Nothing in the carve has to start at zero: every kernel of the step
+    // writes each scratch element before any kernel reads it.
+    const Workspace w = carve((char*)base, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT));
     return decode_step_impl(logits, probs, tokens, pos, kcache, vcache, params, cfg, B, w, (hipStream_t)stream);
 }
 
