@@ -470,8 +470,17 @@ def summarize_kernels(recs, dtype_bf16, key=1):
                 "peak": PEAK["hbm_GBps"], "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["avg_launch_us"] = round(per_launch_s * 1e6, 2)
+    roof["timing"] = "HIP events between consecutive launches on the launch stream, median of passes"
     roof["launches_per_step"] = g["calls"]
     roof["traffic"] = load_traffic(dom)
+    # the same kernel's average duration from the committed rocprofv3 kernel
+    # trace (while its sources are unchanged), and the fraction it gives
+    rp = load_profile_field(dom, "rocprof_avg_us")
+    if rp:
+        work = g["flops"] if g["kind"] in ("gemm", "mfma") else g["bytes"]
+        scale = 1e12 if g["kind"] in ("gemm", "mfma") else 1e9
+        roof["rocprof_avg_launch_us"] = rp
+        roof["frac_rocprof"] = round(work / g["calls"] / (rp * 1e-6) / scale / roof["peak"], 4)
     return table, roof
 
 
@@ -480,6 +489,7 @@ def summarize_kernels(recs, dtype_bf16, key=1):
 KERNEL_SOURCES = {
     "gemm": ("common.h", "gemm.h", "matmul.hip"),
     "attention_decode": ("common.h", "attention.hip"),
+    "attention": ("common.h", "attention.hip"),
 }
 
 
@@ -487,9 +497,10 @@ def kernel_sources(kernel):
     return KERNEL_SOURCES["gemm" if kernel.startswith("gemm_") else kernel]
 
 
-def load_traffic(kernel):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
-    there is none for this kernel or its sources changed since."""
+def load_profile_field(kernel, field):
+    """A per-kernel figure from the committed rocprofv3 runs (profiles/
+    traffic.json), or None if there is none for this kernel or its sources
+    changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -500,9 +511,14 @@ def load_traffic(kernel):
             return None
         if ent.get("source_sha1") != source_sha1(kernel_sources(kernel)):
             return None
-        return ent.get("bytes_per_launch")
+        return ent.get(field)
     except Exception:
         return None
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs."""
+    return load_profile_field(kernel, "bytes_per_launch")
 
 
 def source_sha1(files):
@@ -545,18 +561,51 @@ def profile_kernel(b):
     print(json.dumps(info))
 
 
+def host_info():
+    """The host the CPU baseline ran on: CPU model and logical CPU counts."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    info = {"cpu_model": model, "nproc": os.cpu_count()}
+    try:
+        info["cpus_allowed"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    return info
+
+
+def forward_flops_per_token(w, t):
+    """Algorithmic flops of one position t (0-based): block GEMMs and logits
+    (2 flops per weight, V columns), plus causal attention over t+1 keys."""
+    C, L = w.C, w.L
+    gemm = 2.0 * L * 12 * C * C + 2.0 * C * w.V
+    return gemm + 4.0 * L * C * (t + 1)
+
+
 def cpu_baseline(b, ntok):
     """The oracle, single-threaded, on the first ntok positions of sequence 0
-    (by the causal invariant, exactly those positions of the full workload)."""
+    (by the causal invariant, exactly those positions of the full workload).
+    Early positions attend over fewer keys, so their average work per token is
+    below the full sequence's; the sample string states by how much."""
     import oracle
     w = b.w
     tok = b.tokens_np[:1, :ntok]
     t0 = time.perf_counter()
     oracle.forward(tok, b.params_np, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps)
     dt = time.perf_counter() - t0
+    f_sample = np.mean([forward_flops_per_token(w, t) for t in range(ntok)])
+    f_full = np.mean([forward_flops_per_token(w, t) for t in range(w.T)])
     return {"value": round(ntok / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "sequence 0, positions 0..%d of the same workload (%d tokens, %.1f s, "
-                      "single-threaded C oracle)" % (ntok - 1, ntok, dt)}
+            "host": host_info(),
+            "sample": "sequence 0, positions 0..%d of the same workload (%d tokens, %.1f s, single-threaded C "
+                      "oracle); these positions carry %.1f%% less arithmetic per token than the average over "
+                      "all %d positions, so the rate overstates a whole sequence's by about that"
+                      % (ntok - 1, ntok, dt, 100.0 * (1.0 - f_sample / f_full), w.T)}
 
 
 def cpu_baseline_train(b, ntok):
@@ -570,7 +619,7 @@ def cpu_baseline_train(b, ntok):
     t0 = time.perf_counter()
     oracle.backward(tok, tg, b.params_np, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps)
     dt = time.perf_counter() - t0
-    return {"value": round(ntok / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(ntok / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host_info(),
             "sample": "training step on sequence 0, positions 0..%d with their targets (%d tokens, %.1f s, "
                       "single-threaded C oracle)" % (ntok - 1, ntok, dt)}
 
@@ -587,7 +636,7 @@ def cpu_baseline_decode(b, nseq):
     t0 = time.perf_counter()
     oracle.decode_step(tok, w.decode_pos, kc, vc, b.params_np, w.L, w.C, w.NH, w.V, w.Vp, w.maxT, w.ln_eps)
     dt = time.perf_counter() - t0
-    return {"value": round(nseq / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(nseq / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host_info(),
             "sample": "decode step for sequences 0..%d of the 32 at position %d (%d tokens, %.1f s, "
                       "single-threaded C oracle)" % (nseq - 1, w.decode_pos, nseq, dt)}
 

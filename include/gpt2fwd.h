@@ -119,6 +119,32 @@ int softmax_forward(void* probs, const void* logits, int N, int V, int Vp, int d
 int crossentropy_forward(float* losses, float* mean_loss, void* probs, const void* logits,
                          const int32_t* targets, int N, int V, int Vp, int dtype, void* stream);
 
+/* The vocabulary projection and softmax with the row statistics taken in the
+ * GEMM epilogue (the fused classifier of llm.c "State of the Union [April 22,
+ * 2024]", kernel summaries: fused_classifier_kernel3; the kernel-fusion item
+ * of its "big stones" list). gpt2_forward does not use this pair: on MI355X
+ * the epilogue's exponentials (one per logit, on the vector units while the
+ * matrix cores wait) cost more than the softmax saves, since softmax_forward
+ * already reads the logits once and writes the probabilities once.
+ *
+ * matmul_logits_stats_forward: logits [N,Vp] = inp [N,C] . wte[Vp,C]^T (no
+ * bias), as matmul_forward, and
+ *   stats[n][g] = (m, s),  m = max of the stored logits[n, v],
+ *                          s = sum of exp(logits[n, v] - m)
+ * over the columns v < V of group g = v / 128 (fp32 pairs, stats
+ * [N, ceil(Vp/128), 2]; a group with no column below V holds (-inf, 0)).
+ * Needs C % 32 == 0 (fp32) or C % 64 == 0 (bf16), else GPT2_ERR_UNSUPPORTED.
+ *
+ * softmax_stats_forward: probs [N,Vp] as softmax_forward, from the logits and
+ * the stats above: M = max_g m_g, S = sum_g s_g exp(m_g - M),
+ * probs[n,v] = exp(l_v - M) / S for v < V, 0 for V <= v < Vp. One read of the
+ * logits and one write of the probabilities. probs must not alias logits;
+ * Vp <= 131072. */
+int matmul_logits_stats_forward(void* logits, float* stats, const void* inp, const void* wte, int N, int C,
+                                int V, int Vp, int dtype, void* stream);
+int softmax_stats_forward(void* probs, const void* logits, const float* stats, int N, int V, int Vp,
+                          int dtype, void* stream);
+
 /* ---------------------------------------------------------------- model */
 typedef struct {
     int L;        /* layers */

@@ -177,6 +177,14 @@ def test_model_validation():
     assert lib.crossentropy_forward(a, None, b, b, c, 4, 200, 256, 0, None) == G.ERR_INVALID_ARGUMENT  # probs=logits
     assert lib.crossentropy_forward(a, None, None, b, c, 4, 200, 252, 0, None) == G.ERR_UNSUPPORTED  # Vp % 8
     assert lib.crossentropy_forward(None, None, None, None, None, 0, 200, 256, 0, None) == G.OK
+    # logits with row statistics: V > Vp, missing stats, C not a whole number of k-tiles
+    assert lib.matmul_logits_stats_forward(a, b, c, d, 4, 64, 300, 256, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.matmul_logits_stats_forward(a, None, c, d, 4, 64, 200, 256, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.matmul_logits_stats_forward(a, b, c, d, 4, 48, 200, 256, 0, None) == G.ERR_UNSUPPORTED
+    assert lib.matmul_logits_stats_forward(a, b, c, d, 4, 32, 200, 256, 1, None) == G.ERR_UNSUPPORTED
+    assert lib.softmax_stats_forward(a, a, b, 4, 200, 256, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.softmax_stats_forward(a, b, None, 4, 200, 256, 0, None) == G.ERR_INVALID_ARGUMENT
+    assert lib.softmax_stats_forward(None, None, None, 0, 200, 256, 0, None) == G.OK
     assert G.generate_workspace_bytes(cfg, 2, 24) >= G.workspace_bytes(cfg, 2, 24)
     assert G.generate_workspace_bytes(cfg, 2, 24) >= G.decode_workspace_bytes(cfg, 2)
 

@@ -406,6 +406,64 @@ def test_softmax(dt, N, V, Vp):
         assert np.all(np.abs(got.astype(np.float64).sum(1) - 1) <= 1e-5)
 
 
+# ----------------------------------------------------------------- logits with row statistics
+def _stats_from_logits(logits, V, cols=128):
+    """(max, sum of exp(l - max)) per row and 128-column group of columns < V,
+    in float64 from the stored logits: the definition the entry states."""
+    N, Vp = logits.shape
+    G = (Vp + cols - 1) // cols
+    x = np.full((N, G * cols), -np.inf)
+    x[:, :V] = logits[:, :V]
+    x = x.reshape(N, G, cols)
+    m = x.max(axis=2)
+    with np.errstate(invalid="ignore"):
+        e = np.exp(x - m[:, :, None])
+    s = np.where(np.isfinite(m), np.nansum(np.where(np.isfinite(x), e, 0.0), axis=2), 0.0)
+    return m, s
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C,V,Vp", [(64, 64, 256, 256), (130, 128, 1000, 1008), (300, 64, 129, 136),
+                                      (4096, 768, 50257, 50304), (1, 1024, 50257, 50304)])
+def test_logits_stats(dt, N, C, V, Vp):
+    """matmul_logits_stats_forward + softmax_stats_forward (the fused
+    classifier's one-pass softmax) against the oracle."""
+    announce("logits-stats", dt, N, C, V, Vp)
+    import torch
+    d = DT[dt]
+    a = I.random_tensor(60, (N, C), 1.0, d)
+    w = I.random_tensor(61, (Vp, C), 0.5, d)
+    w[V:] = 0.0
+    G_ = (Vp + 127) // 128
+    logits = empty((N, Vp), d, fill=float("nan"))
+    stats = torch.full((N, G_, 2), float("nan"), dtype=torch.float32, device="cuda")
+    da, dw = dev(a, d), dev(w, d)
+    G.matmul_logits_stats_forward(logits, stats, da, dw, V)
+    probs = empty((N, Vp), d, fill=float("nan"))
+    G.softmax_stats_forward(probs, logits, stats, V)
+    gl, gs, gp = host(logits), host(stats), host(probs)
+    rows = np.arange(N) if N <= 512 else np.array([0, 1, 255, 256, 2047, N - 1])
+    # logits: the oracle's product (and matmul_forward's bits where it picks the same tile)
+    assert rel_err(gl[rows], oracle.matmul(a[rows], w, None)) <= (1e-2 if d == I.BF16 else 1e-5)
+    plain = empty((N, Vp), d)
+    G.matmul_forward(plain, da, dw, None)
+    if "256x" in G.matmul_kernel_config(N, C, Vp, d):
+        assert np.array_equal(host_bits(plain), host_bits(logits))
+    # statistics: exactly the max of the stored logits; the sum within a few ulp
+    m, ssum = _stats_from_logits(gl[rows].astype(np.float64), V)
+    assert np.array_equal(gs[rows, :, 0], m.astype(np.float32))
+    assert np.all(np.abs(gs[rows, :, 1] - ssum) <= 2e-6 * ssum)
+    # probabilities: the oracle's softmax of the stored logits
+    ref = oracle.softmax(gl[rows], V)
+    got = gp[rows]
+    assert np.all(got[:, V:] == 0)
+    if d == I.BF16:
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * ref + 1e-9)
+    else:
+        assert np.all(np.abs(got - ref) <= 1e-6 * ref + 1e-9)
+        assert np.all(np.abs(got.astype(np.float64).sum(1) - 1) <= 1e-5)
+
+
 # ----------------------------------------------------------------- cross-entropy
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N,V,Vp", [(5, 256, 256), (64, 50257, 50304), (3, 1000, 1008), (130, 64, 64)])

@@ -40,6 +40,7 @@ EXPORTS = (
     "matmul_backward_workspace_size", "matmul_backward", "attention_forward_lse",
     "attention_backward_workspace_size", "attention_backward", "encoder_backward", "gpt2_train_acts_bytes",
     "gpt2_train_workspace_bytes", "gpt2_train_forward", "gpt2_backward", "gpt2_decode_step_noalloc",
+    "matmul_logits_stats_forward", "softmax_stats_forward",
 )
 
 DECODE_SCRATCH_BYTES = 8 << 20  # GPT2_DECODE_SCRATCH_BYTES of the header
@@ -119,6 +120,8 @@ def load_library(path: str = LIB_PATH):
             "gpt2_train_forward": (I, [P, P, P, P, P, CP, I, I, P, I64, P]),
             "gpt2_backward": (I, [P, P, P, CP, I, I, P, I64, P, I64, P]),
             "gpt2_decode_step_noalloc": (I, [P, P, P, I, P, P, P, CP, I, P]),
+            "matmul_logits_stats_forward": (I, [P, P, P, P, I, I, I, I, I, P]),
+            "softmax_stats_forward": (I, [P, P, P, I, I, I, I, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -402,6 +405,41 @@ def softmax_forward(probs, logits, V, stream=None):
     _chk(probs, "probs", dtype=logits.dtype, numel=logits.numel())
     _check("softmax_forward", lib.softmax_forward(_dev(probs, "probs"), _dev(logits, "logits"), N,
                                                   V, Vp, dt, _stream(stream)))
+    return probs
+
+
+STAT_COLS = 128  # columns per row-statistics group
+
+
+def stat_groups(Vp: int) -> int:
+    return (Vp + STAT_COLS - 1) // STAT_COLS
+
+
+def matmul_logits_stats_forward(logits, stats, inp, wte, V, stream=None):
+    """logits [N,Vp] = inp [N,C] @ wte[Vp,C]^T and stats fp32 [N, groups, 2]: per row and
+    128-column group, the max and the sum of exp(l - max) over the columns < V."""
+    lib = load_library()
+    dt = _dtype_code(inp)
+    N, C, Vp = _linear_args(inp, wte, None)
+    if not 0 < V <= Vp:
+        raise ValueError("V must lie in [1, %d], got %d" % (Vp, V))
+    _chk(logits, "logits", dtype=inp.dtype, numel=N * Vp)
+    _f32t(stats, "stats", numel=N * stat_groups(Vp) * 2)
+    _check("matmul_logits_stats_forward", lib.matmul_logits_stats_forward(
+        _dev(logits, "logits"), _dev(stats, "stats"), _dev(inp, "inp"), _dev(wte, "wte"), N, C, V, Vp, dt,
+        _stream(stream)))
+    return logits
+
+
+def softmax_stats_forward(probs, logits, stats, V, stream=None):
+    """probs [N,Vp] from logits [N,Vp] and the row statistics of matmul_logits_stats_forward."""
+    lib = load_library()
+    dt = _dtype_code(logits)
+    N, Vp = _vocab_dims(logits, V)
+    _chk(probs, "probs", dtype=logits.dtype, numel=N * Vp)
+    _f32t(stats, "stats", numel=N * stat_groups(Vp) * 2)
+    _check("softmax_stats_forward", lib.softmax_stats_forward(
+        _dev(probs, "probs"), _dev(logits, "logits"), _dev(stats, "stats"), N, V, Vp, dt, _stream(stream)))
     return probs
 
 

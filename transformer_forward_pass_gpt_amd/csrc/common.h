@@ -114,7 +114,12 @@ void set_last_hip_error(int e);
 // nothing, GELU of the rounded y, or a residual r added to the rounded y
 // (each rounded again), i.e. exactly what a separate GELU or residual kernel
 // would compute from the stored product.
-enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2 };
+// EPI_STATS (vocabulary projection, no bias): the stored product plus, per
+// row and per group of kStatCols columns, the max m and the sum of
+// e^{y - m} over the group's columns below a limit V (row statistics for a
+// one-pass softmax).
+enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_STATS = 3 };
+constexpr int kStatCols = 128;
 // Status after a launch: GPT2_OK, or GPT2_ERR_HIP with the code recorded.
 int launch_status();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

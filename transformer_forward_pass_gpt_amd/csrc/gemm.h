@@ -259,7 +259,8 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
                                                                 const T* __restrict__ W,
                                                                 const T* __restrict__ bias, const T* res, int M,
                                                                 int N, int K, int group_m, int remap, int lda,
-                                                                int ldb, int64_t split_out) {
+                                                                int ldb, int64_t split_out,
+                                                                float* __restrict__ stats, int vlim) {
     // RB: bytes of k per tile row (64 or 128); S: LDS stages (S-1 tiles in flight;
     // S = 2 is plain double buffering: tile t+1 loads while tile t is multiplied)
     constexpr int NW = WM * WN;
@@ -512,6 +513,54 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
                     store_vec(out + (int64_t)row * N + col, a);
                 }
             }
+        } else if constexpr (EPI == EPI_STATS) {
+            // the stored tile, then one thread per (row, column group): the
+            // max of the group's stored values of columns < vlim from LDS,
+            // then the sum of e^{y - max} (hardware base-2 exponential of the
+            // scaled difference) in a second pass. Consecutive lanes take
+            // consecutive rows: 528-byte rows put them on distinct banks.
+            static_assert(BN % kStatCols == 0, "stats groups must tile the output tile");
+            constexpr int NG = BN / kStatCols, GCH = kStatCols / VE;
+            const int ngrp = (N + kStatCols - 1) / kStatCols;
+            const float L2E = 1.4426950408889634f;
+#pragma unroll 4
+            for (int c = tid; c < BM * CPR; c += NW * 64) {
+                const int rl = c / CPR, cv = c % CPR;
+                const int row = m0 + rl, col = n0 + cv * VE;
+                if (row < M && col < N)
+                    *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) =
+                        *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]);
+            }
+            for (int p = tid; p < BM * NG; p += NW * 64) {
+                const int rl = p % BM, gi = p / BM;
+                const int row = m0 + rl, c0 = n0 + gi * kStatCols, grp = c0 / kStatCols;
+                const T* src = &so[rl * LDO + gi * kStatCols];
+                float mx = -INFINITY;
+#pragma unroll 4
+                for (int j = 0; j < GCH; j++) {
+                    float y[VE];
+                    unpack_vec<T>(*reinterpret_cast<const u32x4*>(src + j * VE), y);
+#pragma unroll
+                    for (int e = 0; e < VE; e++)
+                        if (c0 + j * VE + e < vlim) mx = fmaxf(mx, y[e]);
+                }
+                float sm = 0.f;
+                if (mx != -INFINITY) {
+#pragma unroll 4
+                    for (int j = 0; j < GCH; j++) {
+                        float y[VE];
+                        unpack_vec<T>(*reinterpret_cast<const u32x4*>(src + j * VE), y);
+#pragma unroll
+                        for (int e = 0; e < VE; e++)
+                            sm += c0 + j * VE + e < vlim ? __builtin_amdgcn_exp2f((y[e] - mx) * L2E) : 0.f;
+                    }
+                }
+                if (row < M && grp < ngrp) {
+                    float* st = stats + ((int64_t)row * ngrp + grp) * 2;
+                    st[0] = mx;
+                    st[1] = sm;
+                }
+            }
         } else {
 #pragma unroll 4
             for (int c = tid; c < BM * CPR; c += NW * 64) {
@@ -549,18 +598,26 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
 template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false>
 static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
                              int group_m, int remap, hipStream_t s, int epi = EPI_BIAS, const T* res = nullptr,
-                             int lda = 0, int splits = 1, int64_t split_out = 0) {
+                             int lda = 0, int splits = 1, int64_t split_out = 0, float* stats = nullptr,
+                             int vlim = 0) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(nwg, splits);
     if (lda == 0) lda = K;
 #define GEMM_PIPE_LAUNCH(E)                                                                              \
     gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, E><<<grid, WM * WN * 64, 0, s>>>( \
-        out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out)
+        out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out, stats, vlim)
     if (splits > 1 || lda != K) {
         gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, EPI_BIAS, true>
-            <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out);
+            <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out,
+                                           nullptr, 0);
         return;
+    }
+    if constexpr (BN % kStatCols == 0) {
+        if (epi == EPI_STATS) {
+            GEMM_PIPE_LAUNCH(EPI_STATS);
+            return;
+        }
     }
     if (epi == EPI_BIAS_GELU) GEMM_PIPE_LAUNCH(EPI_BIAS_GELU);
     else if (epi == EPI_BIAS_RESIDUAL) GEMM_PIPE_LAUNCH(EPI_BIAS_RESIDUAL);
@@ -579,7 +636,8 @@ static void launch_gemm_kmajor(float* out, const float* A, const float* W, const
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(nwg, splits);
     gemm_pipe_kernel<float, WM, WN, TM, TN, RB, S, SCHED, WPE, false, EPI_BIAS, true, TA, TB>
-        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, nullptr, M, N, K, group_m, remap, lda, ldb, split_out);
+        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, nullptr, M, N, K, group_m, remap, lda, ldb, split_out,
+                                       nullptr, 0);
 }
 
 template <typename T, int WM, int WN, int TM, int TN, int SCHED = 4>

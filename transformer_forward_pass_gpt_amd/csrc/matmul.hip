@@ -147,6 +147,26 @@ int launch_matmul(void* out, const void* inp, const void* weight, const void* bi
     return launch_matmul_epi(out, inp, weight, bias, nullptr, N, C, OC, EPI_BIAS, dtype, s);
 }
 
+// Vocabulary projection with row statistics (no bias): out [M,N] = A W^T and
+// stats [M, ceil(N/kStatCols), 2] = (max, sum of e^{y - max}) of the stored
+// y over each group's columns < vlim. Always the vocabulary tiles (fp32
+// 256x128, bf16 256x256), whose rows are 32 16-byte chunks. K must be a whole
+// number of 128-byte k-tiles (fp32 K % 32, bf16 K % 64).
+bool matmul_stats_supported(int K, int dtype) { return K > 0 && K % (dtype == GPT2_BF16 ? 64 : 32) == 0; }
+
+int launch_matmul_stats(void* out, float* stats, const void* inp, const void* weight, int M, int K, int N, int vlim,
+                        int dtype, hipStream_t s) {
+    if (!matmul_stats_supported(K, dtype)) return GPT2_ERR_UNSUPPORTED;
+    if (dtype == GPT2_BF16)
+        launch_gemm_pipe<bf16, 2, 4, 4, 2, 128, 2, 2, 0>((bf16*)out, (const bf16*)inp, (const bf16*)weight, nullptr,
+                                                         M, N, K, 1, 0, s, EPI_STATS, nullptr, 0, 1, 0, stats, vlim);
+    else
+        launch_gemm_pipe<float, 4, 2, 2, 2, 128, 3, 2, 0>((float*)out, (const float*)inp, (const float*)weight,
+                                                          nullptr, M, N, K, 1, 0, s, EPI_STATS, nullptr, 0, 1, 0,
+                                                          stats, vlim);
+    return launch_status();
+}
+
 // Split-k partial products (fp32): part[s] [M,N] = A_s W_s^T for s < splits,
 // where A_s, W_s are the columns s*Kc .. s*Kc+Kc-1 of A [M, lda] and
 // W [N, lda]; one launch, splits x tiles workgroups. For weight gradients,
@@ -263,6 +283,16 @@ extern "C" int matmul_forward(void* out, const void* inp, const void* weight, co
     const int rc = check_linear(out, inp, weight, N, C, OC, dtype);
     if (rc <= 0) return rc;
     return launch_matmul(out, inp, weight, bias, N, C, OC, dtype, (hipStream_t)stream);
+}
+
+extern "C" int matmul_logits_stats_forward(void* logits, float* stats, const void* inp, const void* wte, int N,
+                                           int C, int V, int Vp, int dtype, void* stream) {
+    if (V < 1 || V > Vp) return GPT2_ERR_INVALID_ARGUMENT;
+    const int rc = check_linear(logits, inp, wte, N, C, Vp, dtype);
+    if (rc <= 0) return rc;
+    if (!stats) return GPT2_ERR_INVALID_ARGUMENT;
+    if (!aligned16(stats) || !matmul_stats_supported(C, dtype)) return GPT2_ERR_UNSUPPORTED;
+    return launch_matmul_stats(logits, stats, inp, wte, N, C, Vp, V, dtype, (hipStream_t)stream);
 }
 
 extern "C" const char* matmul_kernel_config(int N, int C, int OC, int dtype) {

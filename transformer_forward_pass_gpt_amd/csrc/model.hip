@@ -178,6 +178,11 @@ extern "C" int gpt2_forward(void* logits, void* probs, const int32_t* tokens, co
     CHECK(run_blocks(w, tokens, P, po, *cfg, B, T, nullptr, nullptr, 0, s));
     CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.lnf_g), at(po.lnf_b), n, C,
                            cfg->ln_eps, dt, s));
+    // The vocabulary softmax holds each row in registers, so it reads the
+    // logits once and writes the probabilities once. The variant with row
+    // statistics from the GEMM epilogue (matmul_logits_stats_forward) was
+    // measured slower: its exponentials run on the vector units while the
+    // matrix cores idle.
     CHECK(launch_matmul(logits, w.ln, at(po.wte), nullptr, n, C, cfg->Vp, dt, s));
     if (probs) CHECK(launch_softmax(probs, logits, n, cfg->V, cfg->Vp, dt, s));
     return GPT2_OK;

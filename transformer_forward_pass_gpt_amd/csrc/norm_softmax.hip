@@ -412,6 +412,82 @@ static void launch_softmax_t(T* probs, const T* logits, int N, int V, int Vp, hi
 #undef SM_LAUNCH
 }
 
+// One-pass vocabulary softmax from the row statistics the logits GEMM wrote
+// (EPI_STATS: per group g of kStatCols columns, m_g = max and s_g = sum of
+// e^{l - m_g} over the group's columns < V): M = max_g m_g,
+// S = sum_g s_g e^{m_g - M}, probs_v = e^{l_v - M} / S for v < V and 0 for
+// V <= v < Vp. As softmax_kernel, one workgroup per row holds the row in
+// registers (every load issued at once), but the max and the sum need no
+// reduction over the row: wavefront 0 combines the groups (fixed order: by
+// lane, then a fixed shuffle tree) while the loads are in flight, and one
+// barrier hands M and 1/S to the others.
+template <typename T, int PT, int NT>
+__global__ __launch_bounds__(NT) void softmax_stats_kernel(T* __restrict__ probs, const T* __restrict__ logits,
+                                                           const float* __restrict__ stats, int V, int Vp, int ngrp) {
+    constexpr int VE = Vec<T>::N;
+    __shared__ float sh[2];
+    const int64_t row = blockIdx.x;
+    const T* x = logits + row * Vp;
+    T* y = probs + row * Vp;
+    const int cv = Vp / VE;
+    float v[PT][VE];
+#pragma unroll
+    for (int i = 0; i < PT; i++) load_vec(x + min((int)threadIdx.x + i * NT, cv - 1) * VE, v[i]);
+    const float L2E = 1.4426950408889634f;
+    if (threadIdx.x < 64) {
+        const float* st = stats + row * ngrp * 2;
+        const int lane = threadIdx.x;
+        float m = -INFINITY;
+        for (int g = lane; g < ngrp; g += 64) m = fmaxf(m, st[2 * g]);
+        m = wave_max(m);
+        float sum = 0.f;
+        for (int g = lane; g < ngrp; g += 64) sum += st[2 * g + 1] * __builtin_amdgcn_exp2f((st[2 * g] - m) * L2E);
+        sum = wave_sum(sum);
+        if (lane == 0) {
+            sh[0] = m;
+            sh[1] = 1.0f / sum;
+        }
+    }
+    __syncthreads();
+    const float m = sh[0], inv = sh[1];
+#pragma unroll
+    for (int i = 0; i < PT; i++) {
+        const int idx = threadIdx.x + i * NT;
+        if (idx < cv) {
+#pragma unroll
+            for (int j = 0; j < VE; j++)
+                v[i][j] = idx * VE + j < V ? __builtin_amdgcn_exp2f((v[i][j] - m) * L2E) * inv : 0.f;
+            store_vec(y + idx * VE, v[i]);
+        }
+    }
+}
+
+int launch_softmax_stats(void* probs, const void* logits, const float* stats, int N, int V, int Vp, int dtype,
+                         hipStream_t s) {
+    const int ngrp = (Vp + kStatCols - 1) / kStatCols;
+    const int cv = Vp / (dtype == GPT2_BF16 ? 8 : 4);
+    const dim3 grid(N);
+#define SMS_LAUNCH(P, NT)                                                                                          \
+    do {                                                                                                           \
+        if (dtype == GPT2_BF16)                                                                                    \
+            softmax_stats_kernel<bf16, P, NT><<<grid, NT, 0, s>>>((bf16*)probs, (const bf16*)logits, stats, V, Vp, \
+                                                                  ngrp);                                           \
+        else                                                                                                       \
+            softmax_stats_kernel<float, P, NT><<<grid, NT, 0, s>>>((float*)probs, (const float*)logits, stats, V,  \
+                                                                   Vp, ngrp);                                      \
+    } while (0)
+    if (cv <= 256) SMS_LAUNCH(1, 256);
+    else if (cv <= 1024) SMS_LAUNCH(1, 1024);
+    else if (cv <= 2048) SMS_LAUNCH(2, 1024);
+    else if (cv <= 4096) SMS_LAUNCH(4, 1024);
+    else if (cv <= 7168) SMS_LAUNCH(7, 1024);
+    else if (cv <= 13312) SMS_LAUNCH(13, 1024);
+    else if (cv <= 16384) SMS_LAUNCH(16, 1024);
+    else SMS_LAUNCH(32, 1024);
+#undef SMS_LAUNCH
+    return launch_status();
+}
+
 // Softmax (probs nullable) with per-row cross-entropy, and the mean loss.
 int launch_softmax_loss(void* probs, float* losses, float* mean, const void* logits, const int32_t* targets, int N,
                         int V, int Vp, int dtype, hipStream_t s) {
@@ -560,6 +636,16 @@ extern "C" int crossentropy_forward(float* losses, float* mean_loss, void* probs
     if (!losses || !logits || !targets || V == 0 || probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
     if (Vp % 8 || Vp > 131072 || !aligned16(logits) || (probs && !aligned16(probs))) return GPT2_ERR_UNSUPPORTED;
     return launch_softmax_loss(probs, losses, mean_loss, logits, targets, N, V, Vp, dtype, (hipStream_t)stream);
+}
+
+extern "C" int softmax_stats_forward(void* probs, const void* logits, const float* stats, int N, int V, int Vp,
+                                     int dtype, void* stream) {
+    if (!valid_dtype(dtype) || N < 0 || V < 1 || V > Vp) return GPT2_ERR_INVALID_ARGUMENT;
+    if (N == 0) return GPT2_OK;
+    if (!probs || !logits || !stats || probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
+    if (Vp % 8 || Vp > 131072 || !aligned16(probs) || !aligned16(logits) || !aligned16(stats))
+        return GPT2_ERR_UNSUPPORTED;
+    return launch_softmax_stats(probs, logits, stats, N, V, Vp, dtype, (hipStream_t)stream);
 }
 
 extern "C" int softmax_forward(void* probs, const void* logits, int N, int V, int Vp, int dtype,
