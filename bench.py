@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--cpu-sample-seqs", type=int, default=32,
                     help="decode workload: sequences the CPU oracle steps")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--elementwise", action="store_true",
+                    help="time the standalone gelu_forward and residual_forward entries (which the forward "
+                         "fuses into GEMM epilogues) on this workload's shapes, each launch after a cache "
+                         "flush; prints their own JSON line")
     ap.add_argument("--profile-kernel", action="store_true",
                     help="counter-collection mode: launch only the dominant kernel (3x: the logits "
                          "GEMM, or the decode attention) and a 256 MiB device copy (calibration)")
@@ -587,6 +591,53 @@ def forward_flops_per_token(w, t):
     return gemm + 4.0 * L * C * (t + 1)
 
 
+def elementwise(b, steps):
+    """gelu_forward on [N, 4C] and residual_forward on [N, C] (N = B*T) with
+    inputs cold in HBM: a 1 GiB buffer (4x the 256 MiB last-level cache) is
+    READ before each launch. A written flush buffer would leave dirty lines
+    whose write-back competes with the timed kernel (a plain device copy then
+    loses a third of its rate). Algorithmic bytes: GELU 2*N*4C*s (read x,
+    write y), residual 3*N*C*s (read a and b, write out). Beside each, a plain
+    device-to-device copy moving the same bytes under the same conditions:
+    the practical streaming rate at that size."""
+    torch, G, w = b.torch, b.G, b.w
+    N, C, es = w.B * w.T, w.C, b.es
+    g_in = torch.randn(N, 4 * C, device="cuda").to(b.tdtype)
+    g_out = torch.empty_like(g_in)
+    ra = torch.randn(N, C, device="cuda").to(b.tdtype)
+    rb = torch.randn(N, C, device="cuda").to(b.tdtype)
+    r_out = torch.empty_like(ra)
+    c_in = torch.empty(3 * N * C * es // 2, dtype=torch.uint8, device="cuda")  # copy of 3*N*C*s bytes total
+    c_out = torch.empty_like(c_in)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        ts = []
+        for i in range(steps + 1):
+            flush.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    res = {}
+    for name, fn, cp, nbytes in (("gelu", lambda: G.gelu_forward(g_out, g_in), lambda: g_out.copy_(g_in),
+                                  2 * N * 4 * C * es),
+                                 ("residual", lambda: G.residual_forward(r_out, ra, rb), lambda: c_out.copy_(c_in),
+                                  3 * N * C * es)):
+        us, cus = timed(fn), timed(cp)
+        gbs = nbytes / us / 1e3
+        res[name] = {"n": int(g_in.numel() if name == "gelu" else ra.numel()), "avg_us": round(us, 2),
+                     "bytes": nbytes, "GBps": round(gbs, 1), "frac_peak": round(gbs / PEAK["hbm_GBps"], 4),
+                     "device_copy_same_bytes_GBps": round(nbytes / cus / 1e3, 1)}
+    return res
+
+
 def cpu_baseline(b, ntok):
     """The oracle, single-threaded, on the first ntok positions of sequence 0
     (by the causal invariant, exactly those positions of the full workload).
@@ -660,6 +711,11 @@ def main():
     b = Bench(w, keep_host_cache=decode and not args.no_cpu_baseline, train=train)
     if args.profile_kernel:
         profile_kernel(b)
+        return
+    if args.elementwise:
+        print(json.dumps({"workload": args.workload, "dtype": "bf16" if w.dtype == I.BF16 else "f32",
+                          "timing": "HIP events around each launch, inputs cold in HBM (1 GiB read before each)",
+                          "kernels": elementwise(b, args.steps)}), flush=True)
         return
     for _ in range(args.warmup):
         b.step()

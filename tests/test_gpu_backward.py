@@ -213,7 +213,10 @@ def test_attention_lse(dt, B, T, C, NH):
     qkv = I.random_tensor(71, (B, T, 3 * C), 1.0, d)
     q, out, lse = _attn_fwd(qkv, NH, d)
     ref = oracle.attention_lse(qkv, NH)
-    assert np.all(np.abs(host(lse) - ref) <= 2e-5 * np.maximum(1.0, np.abs(ref)))
+    # bf16: the normaliser sums the bf16-rounded probabilities of the P.V
+    # product (relative error <= 2^-9), so ln of it moves by <= 2^-9
+    tol = 2e-5 * np.maximum(1.0, np.abs(ref)) + (2.0 ** -8 if d == I.BF16 else 0.0)
+    assert np.all(np.abs(host(lse) - ref) <= tol)
     plain = empty((B, T, C), d)
     G.attention_forward(plain, q, NH)
     assert np.array_equal(host_bits(plain), host_bits(out))

@@ -350,7 +350,10 @@ def test_matmul_full_logits_shape_sampled(dt):
 
 # ----------------------------------------------------------------- attention
 ATT_SHAPES = [(2, 32, 64, 4), (1, 1, 64, 4), (2, 100, 128, 2), (1, 77, 256, 8), (2, 200, 256, 2),
-              (1, 1024, 768, 12), (1, 300, 512, 4)]
+              (1, 1024, 768, 12), (1, 300, 512, 4),
+              # head size 64 (the GPT-2 head): one key, one partial key block, a
+              # ragged second query block, 16 heads, sequences longer than 1024
+              (1, 1, 64, 1), (3, 33, 128, 2), (1, 129, 64, 1), (2, 1024, 1024, 16), (1, 1500, 192, 3)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])

@@ -79,9 +79,8 @@ __device__ __forceinline__ int vt_slot_bf16(int key) {
 // through LDS at the end, in a fixed order. Each iteration stages two key
 // blocks (the even and the odd one); when two iterations' worth fits in LDS
 // the next pair is loaded while the current one is computed.
-// WPE: minimum wavefronts per SIMD the registers must allow (0: none); SB:
-// single-buffered key/value staging (half the LDS).
-template <typename T, int HS, int WPE = 0, bool SB = false>
+// WPE: minimum wavefronts per SIMD the registers must allow (0: none).
+template <typename T, int HS, int WPE = 0>
 __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
                                                              int Tn, int C, int NH, float sl2,
                                                              float* __restrict__ lse) {
@@ -95,7 +94,7 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
     constexpr int LDV = kBKV + VE;  // V^T block [HSP][kBKV], 16-byte row pad
     constexpr int KSZ = kBKV * LDK, VSZ = HSP * LDV;  // elements per block
     constexpr int PAIR = 2 * (KSZ + VSZ);             // one iteration: even + odd block
-    constexpr bool DB = !SB && 2 * PAIR * (int)sizeof(T) <= 160 * 1024;  // double-buffered
+    constexpr bool DB = 2 * PAIR * (int)sizeof(T) <= 160 * 1024;  // double-buffered
     constexpr int NBUF = DB ? 2 : 1;
     constexpr int RV = HS / VE;                                  // 16-byte vectors per key row
     constexpr int NKV = (2 * kBKV * RV + 511) / 512;             // K vectors per thread
@@ -385,28 +384,241 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
     }
 }
 
-// Launch shape from on-box sweeps at the GPT-2 sizes: fp32 asks the register
-// allocator for 3 wavefronts per SIMD; bf16 grids of 768+ workgroups run
-// (head size 64) single-buffered with 3 per SIMD (two workgroups per CU hide
-// each other's staging), the rest double-buffered with one workgroup per CU.
+// ---------------------------------------------------------------------------
+// bf16, head size 64 (GPT-2 small and medium). The same online-softmax
+// algorithm, arranged so the vector units do little beyond the softmax:
+//  - K and V blocks (64 keys) go from HBM/L2 straight to LDS with the
+//    load-to-LDS copies (no VGPR staging, no transposing stores), through a
+//    two-stage ring: block j+1 is in flight while block j is multiplied. A
+//    key row is 128 bytes = 8 chunks of 16; rows are stored with their chunks
+//    permuted (K: slot = chunk ^ ((row/2) % 8), conflict-free for the 16-row
+//    fragment reads; V: slot = chunk ^ 4*((row/2) % 2), conflict-free for the
+//    transposing reads below), the copies fetching the permuted global
+//    chunks instead. Copy and read addresses are per-lane constants plus
+//    wave-uniform or immediate offsets.
+//  - The V^T operand of O^T += V^T P^T is read with gfx950's transposing LDS
+//    read (ds_read_b64_tr_b16): in each 16-lane group, lane 4j+q addresses
+//    4 head dims (4q..4q+3 past the group's base) of key j, and lane i
+//    receives head dim i of keys 0..3. Two reads give a lane the 8 keys its
+//    half of the P^T accumulator holds (16ks+4h+0..3 and 16ks+8+4h+0..3),
+//    so V needs no reordering.
+//  - A block's K fragments are all read before its score products, and its
+//    V^T fragments right after them, so their LDS latency overlaps the
+//    matrix work and the softmax instead of stalling each product.
+// Workgroup: 4 wavefronts x 32 queries (128 queries), each walking all key
+// blocks of the workgroup's causal range; 32 KiB of LDS, <= 168 VGPRs: 3
+// workgroups per CU.
+static constexpr int kAttnD64Waves = 4;
+
+__global__ __launch_bounds__(64 * kAttnD64Waves, 3) void attention_bf16_d64_kernel(
+    bf16* __restrict__ out, const bf16* __restrict__ qkv, int Tn, int C, int NH, float sl2,
+    float* __restrict__ lse) {
+    constexpr int HS = 64, KB = 64;  // head size, keys per block
+    constexpr int BLK = KB * HS;     // elements of one K or V block (8 KiB)
+    constexpr int STAGE = 2 * BLK;   // K block then V block
+    constexpr int BQ = 32 * kAttnD64Waves;
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, r32 = lane & 31;
+    const int qb = gridDim.y - 1 - blockIdx.y;  // longest query blocks first
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
+    const int q0 = qb * BQ, qw = q0 + wid * 32;
+    const int64_t rs = 3 * (int64_t)C;
+    const bf16* base = qkv + (int64_t)b * Tn * rs;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    u32x4 qf[4];  // B operand of S^T = K Q^T: query qw + r32, head dims 16kc + 8h .. +7
+    {
+        const int q = qw + r32;
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++)
+            qf[kc] = q < Tn ? *reinterpret_cast<const u32x4*>(base + (int64_t)q * rs + hd * HS + kc * 16 + h * 8)
+                            : zero;
+    }
+
+    // Copies: wave w moves key rows 16w .. 16w+15 of the K and of the V block
+    // (two 8-row instructions each); lane l takes row 8i + l/8, LDS slot l % 8,
+    // i.e. global chunk slot ^ swizzle(row). Element offsets inside the
+    // sequence (T * 3C < 2^31) for block 0; block j adds j*64 rows. Rows past
+    // the sequence read its last key (finite, and masked).
+    const int crow0 = 16 * wid + (lane >> 3), cslot = lane & 7;
+    int kp[2], vp[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int row = crow0 + 8 * i;
+        kp[i] = row * (int)rs + C + hd * HS + (cslot ^ ((row >> 1) & 7)) * 8;
+        vp[i] = row * (int)rs + 2 * C + hd * HS + (cslot ^ (4 * ((row >> 1) & 1))) * 8;
+    }
+    auto issue = [&](int stage, int j) {
+        bf16* st = smem + stage * STAGE;
+        const int k0 = j * KB;
+        const bool full = k0 + KB <= Tn;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int row = crow0 + 8 * i;
+            const int radd = (full ? k0 : min(k0 + row, Tn - 1) - row) * (int)rs;
+            copy16_to_lds(base + kp[i] + radd, (lds_void_ptr)(st + (16 * wid + 8 * i) * HS));
+            copy16_to_lds(base + vp[i] + radd, (lds_void_ptr)(st + BLK + (16 * wid + 8 * i) * HS));
+        }
+    };
+
+    // K fragment reads: row r32 (+32), chunk (2kc + h) ^ swizzle = 2kc ^ kx
+    const int kx = h ^ ((r32 >> 1) & 7), krow = r32 * HS;
+    // Transposing-read base of this lane: lane 4gj+gq of its 16-lane group
+    // addresses key 4h + gj (+ a compile-time key offset), head dims
+    // gdim + 4gq (+ 32dt); key bit 1 is gj's bit 1, so the V swizzle of the
+    // chunk is a per-lane constant.
+    const int gj = (lane & 15) >> 2, gq = lane & 3;
+    const int vy = (gj >> 1) & 1, vx = 2 * (r32 >> 4) + (gq >> 1);
+    int vbase[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; dt++) vbase[dt] = (4 * h + gj) * HS + (4 * (dt ^ vy) + vx) * 8 + (gq & 1) * 4;
+
+    f32x16 o[2] = {f32x16{}, f32x16{}};  // O^T tiles: head dims 0..31 and 32..63
+    float m_run = -INFINITY;             // reference max of query qw + r32, log2 units
+    float l_part = 0.f;                  // this lane's share of the normaliser (its 16 keys per tile)
+
+    auto block = [&](const bf16* Ks, const bf16* Vs, int k0) {
+        // every K fragment of the block first, then the score products
+        u32x4 ka[4][2];
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++) {
+            const int ko = krow + ((2 * kc) ^ kx) * 8;
+            ka[kc][0] = *reinterpret_cast<const u32x4*>(&Ks[ko]);
+            ka[kc][1] = *reinterpret_cast<const u32x4*>(&Ks[ko + 32 * HS]);
+        }
+        f32x16 sc[2];
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++)
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++)
+                sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kc][kt]),
+                                                                __builtin_bit_cast(bf16x8, qf[kc]),
+                                                                kc ? sc[kt] : f32x16{}, 0, 0, 0);
+        // the V^T fragments of the whole block, read while the softmax runs
+        const lds_v4s_ptr vt = (lds_v4s_ptr)Vs;
+        u32x4 va[2][2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                for (int dt = 0; dt < 2; dt++) {
+                    const int kofs = (kt * 32 + 16 * ks) * HS;  // compile-time element offset
+                    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vt + (vbase[dt] + kofs) / 4);
+                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vt + (vbase[dt] + kofs + 8 * HS) / 4);
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                    va[kt][ks][dt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+                }
+        const int q = qw + r32;
+        if (k0 + KB - 1 > qw) {  // diagonal block: keys after the query are -inf
+#pragma unroll
+            for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++)
+                    if (k0 + kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3) > q) sc[kt][v] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) mx = fmaxf(mx, sc[kt][v]);
+        mx = halves_max(mx);
+        const float mb = mx * sl2;
+        const bool grow = mb > m_run + kLazyMax;
+        const float m_new = grow ? mb : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = m_new;
+        l_part *= alpha;
+        if (__any(grow)) {
+#pragma unroll
+            for (int dt = 0; dt < 2; dt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) o[dt][v] *= alpha;
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                u32x4 pbk;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * ks + 2 * e], sl2, -m_new));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * ks + 2 * e + 1], sl2, -m_new));
+                    l_part += p0 + p1;
+                    pbk[e] = pack_bf16x2(p0, p1);
+                }
+#pragma unroll
+                for (int dt = 0; dt < 2; dt++)
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[kt][ks][dt]),
+                                                                   __builtin_bit_cast(bf16x8, pbk), o[dt], 0, 0, 0);
+            }
+    };
+
+    const int kend = min(Tn, q0 + BQ);
+    const int nkb = (kend + KB - 1) / KB;
+    issue(0, 0);
+    for (int j = 0; j < nkb; j++) {
+        // this wave's copies of block j have landed and its LDS reads of
+        // block j-1 are done; after the barrier every wave's are
+        wait_vmcnt_lds<0>();
+        __builtin_amdgcn_s_barrier();
+        if (j + 1 < nkb) issue((j + 1) & 1, j + 1);
+        const int k0 = j * KB;
+        if (k0 <= qw + 31) block(smem + (j & 1) * STAGE, smem + (j & 1) * STAGE + BLK, k0);
+    }
+
+    const float l_run = halves_sum(l_part);  // both halves' keys
+    const int q = qw + r32;
+    if (q >= Tn) return;
+    const float inv = 1.0f / l_run;
+    if (lse && h == 0) lse[(int64_t)bh * Tn + q] = (m_run + __log2f(l_run)) * 0.6931471805599453f;
+    bf16* orow = out + ((int64_t)b * Tn + q) * C + hd * HS;
+#pragma unroll
+    for (int dt = 0; dt < 2; dt++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int d0 = dt * 32 + 8 * g + 4 * h;
+            u32x2 pk = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                        pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + d0) = pk;
+        }
+}
+
+// Launch shape: fp32 asks the register allocator for as many wavefronts per
+// SIMD as its accumulators allow (3 up to head size 32; 2 from 64, where the
+// kernel needs more than the 168 VGPRs of 3); bf16 (head sizes other than
+// 64, which have their own kernel) runs double-buffered.
 template <typename T, int HS>
 static void launch_attn_hs(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s, float* lse) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)HS);  // log2(e)/sqrt(hs)
     dim3 grid(B * NH, (Tn + kBQ - 1) / kBQ);
     if constexpr (std::is_same<T, float>::value)
-        attention_kernel<T, HS, 3><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
-    else if (HS == 64 && (int64_t)grid.x * grid.y >= 768)
-        attention_kernel<T, HS, 3, HS == 64><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
+        attention_kernel<T, HS, (HS >= 64 ? 2 : 3)><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
     else
         attention_kernel<T, HS><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
 }
 
 template <typename T>
 static void launch_attn_t(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s, float* lse) {
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (C / NH == 64) {
+            const float sl2 = 1.4426950408889634f / 8.0f;  // log2(e)/sqrt(64)
+            dim3 grid(B * NH, (Tn + 32 * kAttnD64Waves - 1) / (32 * kAttnD64Waves));
+            attention_bf16_d64_kernel<<<grid, 64 * kAttnD64Waves, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
+            return;
+        }
+    }
     switch (C / NH) {
         case 16: launch_attn_hs<T, 16>(out, qkv, B, Tn, C, NH, s, lse); break;
         case 32: launch_attn_hs<T, 32>(out, qkv, B, Tn, C, NH, s, lse); break;
-        case 64: launch_attn_hs<T, 64>(out, qkv, B, Tn, C, NH, s, lse); break;
+        case 64:
+            if constexpr (std::is_same<T, float>::value) launch_attn_hs<T, 64>(out, qkv, B, Tn, C, NH, s, lse);
+            break;
         default: launch_attn_hs<T, 128>(out, qkv, B, Tn, C, NH, s, lse); break;
     }
 }

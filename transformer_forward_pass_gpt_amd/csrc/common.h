@@ -105,6 +105,33 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
+// ---- direct global -> LDS copies (gfx950 global_load_lds_dwordx4)
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Copy 16 bytes per lane from global memory to LDS: lane i's bytes land at
+// lds + 16*i (lds is wave-uniform; it goes to M0).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void_ptr lds) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0v), "v"(src)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding AND all of its LDS operations are done (lgkmcnt 0): before the
+// barrier that lets other waves overwrite a stage, this wave's reads of that
+// stage must have completed, not merely been issued.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt simm16 on gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
+}
+
 }  // namespace gpt2
 
 // ------------------------------------------------------------------ host side

@@ -1,21 +1,12 @@
 // HBM-streaming kernels: token+position embedding, residual add, tanh-GELU.
-// Each thread moves 16-byte vectors in a grid-stride loop, so every wavefront
-// issues fully coalesced 1 KiB requests; arithmetic is fp32 and bf16 results
-// are rounded to nearest even.
+// Threads move 16-byte vectors, so every wavefront issues fully coalesced
+// 1 KiB requests; arithmetic is fp32 and bf16 results are rounded to nearest
+// even.
 #include "common.h"
 
 namespace gpt2 {
 
 static constexpr int kThreads = 256;
-
-static unsigned stream_grid(int64_t nvec) {
-    // 256 CUs x 8 resident workgroups keeps enough requests in flight; the
-    // grid-stride loop covers the rest.
-    int64_t g = (nvec + kThreads - 1) / kThreads;
-    if (g > 2048) g = 2048;
-    if (g < 1) g = 1;
-    return (unsigned)g;
-}
 
 // out[b,t,:] = wte[tokens[b,t],:] + wpe[t,:]
 // (ECE408 Final Project - GPT-2, Milestone 1, kernel table: Encoder.)
@@ -61,39 +52,75 @@ __global__ __launch_bounds__(kThreads) void encoder_kernel(T* __restrict__ out,
     }
 }
 
-// out = a + b  (ECE408 Milestone 1, kernel table: Residual.)
-template <typename T>
-__global__ __launch_bounds__(kThreads) void residual_kernel(T* out, const T* a, const T* b,
-                                                            int64_t n) {
-    constexpr int V = Vec<T>::N;
-    const int64_t nvec = n / V;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < nvec; i += stride) {
-        float x[V], y[V];
-        load_vec(a + i * V, x);
-        load_vec(b + i * V, y);
-#pragma unroll
-        for (int j = 0; j < V; j++) x[j] += y[j];
-        store_vec(out + i * V, x);
-    }
-    for (int64_t i = nvec * V + blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n; i += stride)
-        store_scalar(out + i, load_scalar(a + i) + load_scalar(b + i));
+// Residual add and GELU stream their tensors once. Each thread owns kStreamU
+// 16-byte vectors kThreads apart and issues all of their loads before the
+// first use (indices clamped into the tensor; the duplicates are not
+// stored), so a workgroup keeps kStreamU KiB per wavefront in flight: with
+// HBM latency in the microseconds, one load per thread at a time leaves the
+// memory system idle. The grid covers the tensor once; the n % V trailing
+// elements (bf16: up to 7) go to the first threads of the last workgroup.
+static constexpr int kStreamU = 4;
+
+static unsigned stream_blocks(int64_t n, int v) {
+    const int64_t nvec = n / v;
+    const int64_t g = (nvec + (int64_t)kThreads * kStreamU - 1) / ((int64_t)kThreads * kStreamU);
+    return (unsigned)(g < 1 ? 1 : g);
 }
 
+// out = a + b  (ECE408 Milestone 1, kernel table: Residual.)
+template <typename T>
+__global__ __launch_bounds__(kThreads) void residual_kernel(T* out, const T* a, const T* b, int64_t n) {
+    constexpr int V = Vec<T>::N;
+    const int64_t nvec = n / V;
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads * kStreamU + threadIdx.x;
+    if (nvec > 0) {
+        float x[kStreamU][V], y[kStreamU][V];
+#pragma unroll
+        for (int u = 0; u < kStreamU; u++) {
+            const int64_t i = min(i0 + u * kThreads, nvec - 1);
+            load_vec(a + i * V, x[u]);
+            load_vec(b + i * V, y[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamU; u++) {
+            const int64_t i = i0 + u * kThreads;
+            if (i < nvec) {
+#pragma unroll
+                for (int j = 0; j < V; j++) x[u][j] += y[u][j];
+                store_vec(out + i * V, x[u]);
+            }
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x < n - nvec * V) {
+        const int64_t i = nvec * V + threadIdx.x;
+        store_scalar(out + i, load_scalar(a + i) + load_scalar(b + i));
+    }
+}
+
+// out = gelu(inp), tanh form  (ECE408 Milestone 1, kernel table: GELU.)
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gelu_kernel(T* out, const T* inp, int64_t n) {
     constexpr int V = Vec<T>::N;
     const int64_t nvec = n / V;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < nvec; i += stride) {
-        float x[V];
-        load_vec(inp + i * V, x);
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads * kStreamU + threadIdx.x;
+    if (nvec > 0) {
+        float x[kStreamU][V];
 #pragma unroll
-        for (int j = 0; j < V; j++) x[j] = gelu_tanh(x[j]);
-        store_vec(out + i * V, x);
+        for (int u = 0; u < kStreamU; u++) load_vec(inp + min(i0 + u * kThreads, nvec - 1) * V, x[u]);
+#pragma unroll
+        for (int u = 0; u < kStreamU; u++) {
+            const int64_t i = i0 + u * kThreads;
+            if (i < nvec) {
+#pragma unroll
+                for (int j = 0; j < V; j++) x[u][j] = gelu_tanh(x[u][j]);
+                store_vec(out + i * V, x[u]);
+            }
+        }
     }
-    for (int64_t i = nvec * V + blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n; i += stride)
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x < n - nvec * V) {
+        const int64_t i = nvec * V + threadIdx.x;
         store_scalar(out + i, gelu_tanh(load_scalar(inp + i)));
+    }
 }
 
 int launch_encoder(void* out, const int32_t* tokens, const void* wte, const void* wpe, int B,
@@ -111,22 +138,20 @@ int launch_encoder(void* out, const int32_t* tokens, const void* wte, const void
 
 int launch_residual(void* out, const void* a, const void* b, int64_t n, int dtype,
                     hipStream_t s) {
-    int64_t nvec = n / (dtype == GPT2_BF16 ? 8 : 4) + 1;
     if (dtype == GPT2_BF16)
-        residual_kernel<bf16><<<stream_grid(nvec), kThreads, 0, s>>>((bf16*)out, (const bf16*)a,
-                                                                    (const bf16*)b, n);
+        residual_kernel<bf16><<<stream_blocks(n, 8), kThreads, 0, s>>>((bf16*)out, (const bf16*)a,
+                                                                       (const bf16*)b, n);
     else
-        residual_kernel<float><<<stream_grid(nvec), kThreads, 0, s>>>(
-            (float*)out, (const float*)a, (const float*)b, n);
+        residual_kernel<float><<<stream_blocks(n, 4), kThreads, 0, s>>>((float*)out, (const float*)a,
+                                                                        (const float*)b, n);
     return launch_status();
 }
 
 int launch_gelu(void* out, const void* inp, int64_t n, int dtype, hipStream_t s) {
-    int64_t nvec = n / (dtype == GPT2_BF16 ? 8 : 4) + 1;
     if (dtype == GPT2_BF16)
-        gelu_kernel<bf16><<<stream_grid(nvec), kThreads, 0, s>>>((bf16*)out, (const bf16*)inp, n);
+        gelu_kernel<bf16><<<stream_blocks(n, 8), kThreads, 0, s>>>((bf16*)out, (const bf16*)inp, n);
     else
-        gelu_kernel<float><<<stream_grid(nvec), kThreads, 0, s>>>((float*)out, (const float*)inp, n);
+        gelu_kernel<float><<<stream_blocks(n, 4), kThreads, 0, s>>>((float*)out, (const float*)inp, n);
     return launch_status();
 }
 

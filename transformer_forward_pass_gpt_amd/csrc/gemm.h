@@ -204,32 +204,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __re
 // this wave's own copies, then a bare s_barrier (a __syncthreads fence would
 // also wait for the copies still in flight for later tiles). Every copy is
 // complete before the loop exits. Requires K % BK == 0; rows past M or N read
-// a clamped (valid) row whose results are never stored.
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// Copy 16 bytes per lane from global memory to LDS: lane i's bytes land at
-// lds + 16*i (lds is wave-uniform; it goes to M0).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void_ptr lds) {
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(m0v), "v"(src)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Wait until at most N of this wave's vector-memory operations are
-// outstanding AND all of its LDS operations are done (lgkmcnt 0): before the
-// barrier that lets other waves overwrite a stage, this wave's reads of that
-// stage must have completed, not merely been issued.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lds() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // s_waitcnt simm16 on gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
-}
+// a clamped (valid) row whose results are never stored. The copy and wait
+// helpers (copy16_to_lds, wait_vmcnt_lds) are in common.h.
 
 // SCHED: 0 = compiler order; 1, 2 = the backend's iglp strategies 0 and 1;
 // 3 = scheduling groups: after the first k-chunk's fragment reads, every MFMA
