@@ -45,7 +45,7 @@ def ws(nbytes):
 
 # ------------------------------------------------------------ cross-entropy
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("N,V,Vp", [(5, 250, 256), (7, 1000, 1008), (4, 50257, 50304)])
+@pytest.mark.parametrize("N,V,Vp", [(5, 250, 256), (7, 1000, 1008), (4, 50257, 50304), (520, 50257, 50304)])
 def test_crossentropy_backward(dt, N, V, Vp):
     announce("crossentropy_backward", dt, N, V, Vp)
     d = DT[dt]
@@ -70,6 +70,11 @@ def test_crossentropy_backward(dt, N, V, Vp):
     # in place over the logits: same bits
     G.crossentropy_backward(lg, lg, dev_int(tg), V, dloss)
     assert np.array_equal(host_bits(lg), host_bits(dl))
+    if N >= 512:
+        # the many-row kernel form (packed bf16 rows) against the few-row one
+        few = empty((32, Vp), d)
+        G.crossentropy_backward(few, dev(logits[:32], d), dev_int(tg[:32]), V, dloss)
+        assert np.array_equal(host_bits(few), host_bits(dl)[:32])
 
 
 # ------------------------------------------------------------ gelu

@@ -392,7 +392,7 @@ def test_attention_equal_keys_prefix_mean(dt):
 # ----------------------------------------------------------------- softmax
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N,V,Vp", [(64, 256, 256), (5, 1000, 1024), (3, 50257, 50304), (2, 7, 8),
-                                    (4, 100000, 100000)])
+                                    (4, 100000, 100000), (600, 50257, 50304)])
 def test_softmax(dt, N, V, Vp):
     announce("softmax", dt, N, V, Vp)
     d = DT[dt]
@@ -407,6 +407,12 @@ def test_softmax(dt, N, V, Vp):
     else:
         assert np.all(np.abs(got - ref) <= 1e-6 * ref + 1e-9)
         assert np.all(np.abs(got.astype(np.float64).sum(1) - 1) <= 1e-5)
+    if N >= 512:
+        # many rows take the kernel form that keeps the row packed (bf16):
+        # the same values as the few-row form, bit for bit
+        few = empty((32, Vp), d, fill=float("nan"))
+        G.softmax_forward(few, dev(logits[:32], d), V)
+        assert np.array_equal(host_bits(few), host_bits(out)[:32])
 
 
 # ----------------------------------------------------------------- logits with row statistics
@@ -469,7 +475,8 @@ def test_logits_stats(dt, N, C, V, Vp):
 
 # ----------------------------------------------------------------- cross-entropy
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("N,V,Vp", [(5, 256, 256), (64, 50257, 50304), (3, 1000, 1008), (130, 64, 64)])
+@pytest.mark.parametrize("N,V,Vp", [(5, 256, 256), (64, 50257, 50304), (3, 1000, 1008), (130, 64, 64),
+                                    (512, 50257, 50304)])
 def test_crossentropy(dt, N, V, Vp):
     """Per-row losses against the oracle; the probabilities written in the same
     pass equal softmax_forward's bit for bit; the mean against the losses."""

@@ -4,6 +4,8 @@
 // statistics are reduced with cross-lane shuffles in fp32.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace gpt2 {
@@ -285,6 +287,13 @@ int launch_residual_layernorm(void* out, void* x, const float* part, int splits,
 // m = max_{u<V} l_u. One workgroup of up to 1024 threads per row; each
 // thread keeps PT 16-byte vectors of the row in registers between the max,
 // the sum and the write, so HBM sees one read and one write per element.
+// PACKED: the vectors stay as loaded (bf16: two values per register) and each
+// pass widens them again, the exponential is evaluated again for the store:
+// a bf16 row of GPT-2's vocabulary then needs 52 instead of 95 registers, so
+// two 1024-thread workgroups share a CU and one row's loads overlap the
+// other's reductions and stores. Worth it when there are rows for every CU
+// twice over; otherwise the widened copies stay live (shorter chains).
+// Both forms compute the same values in the same order.
 // (llm.c "State of the Union", kernel summaries: the softmax half of
 // fused_classifier_kernel3.)
 template <int NW>
@@ -319,7 +328,7 @@ __device__ __forceinline__ float block_sum(float x, float* sh) {
 // dscale * (p_v - [v == target]), 0 in the padding columns. It may overwrite
 // the logits in place: every element of the row (and the target's logit) is
 // read before the first barrier, and every write comes after it.
-template <typename T, int PT, int NT, bool BWD = false>
+template <typename T, int PT, int NT, bool BWD = false, bool PACKED = false>
 __global__ __launch_bounds__(NT) void softmax_kernel(T* probs, const T* logits, int V, int Vp,
                                                      const int32_t* __restrict__ targets,
                                                      float* __restrict__ losses, float dscale) {
@@ -332,51 +341,124 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* probs, const T* logits, 
     const int cv = Vp / VE;
     const int tg = targets ? targets[row] : 0;
     const float lt = targets ? load_scalar(x + tg) : 0.f;
-    float v[PT][VE];
-    float m = -INFINITY;
     // Every load of the row is issued before the first use: indices past the
     // row are clamped to its last vector and masked, not branched around
     // (a load inside a divergent branch would be waited for at the branch's end).
+    if constexpr (PACKED) {
+        u32x4 raw[PT];
 #pragma unroll
-    for (int i = 0; i < PT; i++) load_vec(x + min((int)threadIdx.x + i * NT, cv - 1) * VE, v[i]);
+        for (int i = 0; i < PT; i++)
+            raw[i] = *reinterpret_cast<const u32x4*>(x + min((int)threadIdx.x + i * NT, cv - 1) * VE);
+        // An empty asm that may rewrite the vectors keeps the compiler from
+        // carrying widened copies (or exponentials) from one pass to the next.
+        auto opaque = [&]() {
 #pragma unroll
-    for (int i = 0; i < PT; i++) {
-        const int idx = threadIdx.x + i * NT;
+            for (int i = 0; i < PT; i++) asm volatile("" : "+v"(raw[i]));
+        };
+        // Elements at or past V (padding columns, or a clamped vector past the
+        // row) become -inf once, so the passes below need no masks.
 #pragma unroll
-        for (int j = 0; j < VE; j++) {
-            if (idx >= cv || idx * VE + j >= V) v[i][j] = -INFINITY;
-            m = fmaxf(m, v[i][j]);
+        for (int i = 0; i < PT; i++) {
+            const int idx = threadIdx.x + i * NT;
+            const int nv = idx < cv ? V - idx * VE : 0;  // valid elements of vector i (when < VE)
+            if constexpr (VE == 8) {
+#pragma unroll
+                for (int w = 0; w < 4; w++) {
+                    const uint32_t lo = 2 * w < nv ? raw[i][w] & 0xffffu : 0xff80u;
+                    const uint32_t hi = 2 * w + 1 < nv ? raw[i][w] >> 16 : 0xff80u;
+                    raw[i][w] = lo | (hi << 16);
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; w++) raw[i][w] = w < nv ? raw[i][w] : 0xff800000u;  // -inf
+            }
         }
-    }
-    m = block_max<NW>(m, sh);
-    // e^{l - m} = 2^{(l - m) log2 e} on the hardware base-2 exponential; the
-    // difference is formed first, so the argument's rounding error scales with
-    // |l - m| (tiny probabilities), not with |l|.
-    const float L2E = 1.4426950408889634f;
-    float s = 0.f;
+        opaque();
+        auto elem = [&](int i, int j) -> float {
+            if constexpr (VE == 8) return bf16_to_f32((raw[i][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+            else return __uint_as_float(raw[i][j]);
+        };
+        float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < PT; i++)
+        for (int i = 0; i < PT; i++)
 #pragma unroll
-        for (int j = 0; j < VE; j++) {
-            v[i][j] = __builtin_amdgcn_exp2f((v[i][j] - m) * L2E);  // 2^-inf = 0 for padding
-            s += v[i][j];
+            for (int j = 0; j < VE; j++) m = fmaxf(m, elem(i, j));
+        m = block_max<NW>(m, sh);
+        opaque();
+        // e^{l - m} = 2^{(l - m) log2 e} on the hardware base-2 exponential; the
+        // difference is formed first, so the argument's rounding error scales with
+        // |l - m| (tiny probabilities), not with |l|.
+        const float L2E = 1.4426950408889634f;
+        auto ex = [&](int i, int j) { return __builtin_amdgcn_exp2f((elem(i, j) - m) * L2E); };  // 2^-inf = 0
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < PT; i++)
+#pragma unroll
+            for (int j = 0; j < VE; j++) s += ex(i, j);
+        s = block_sum<NW>(s, sh);
+        if (losses && threadIdx.x == 0) losses[row] = logf(s) + m - lt;
+        if (!probs) return;
+        const float inv = 1.0f / s;
+        opaque();
+#pragma unroll
+        for (int i = 0; i < PT; i++) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < cv) {
+                float v[VE];
+#pragma unroll
+                for (int j = 0; j < VE; j++) {
+                    if constexpr (BWD)
+                        v[j] = (ex(i, j) * inv - (idx * VE + j == tg ? 1.f : 0.f)) * dscale;
+                    else
+                        v[j] = ex(i, j) * inv;
+                }
+                store_vec(y + idx * VE, v);
+            }
         }
-    s = block_sum<NW>(s, sh);
-    if (losses && threadIdx.x == 0) losses[row] = logf(s) + m - lt;
-    if (!probs) return;
-    const float inv = 1.0f / s;
+    } else {
+        float v[PT][VE];
+        float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < PT; i++) {
-        int idx = threadIdx.x + i * NT;
-        if (idx < cv) {
+        for (int i = 0; i < PT; i++) load_vec(x + min((int)threadIdx.x + i * NT, cv - 1) * VE, v[i]);
+#pragma unroll
+        for (int i = 0; i < PT; i++) {
+            const int idx = threadIdx.x + i * NT;
 #pragma unroll
             for (int j = 0; j < VE; j++) {
-                if constexpr (BWD)
-                    v[i][j] = (v[i][j] * inv - (idx * VE + j == tg ? 1.f : 0.f)) * dscale;
-                else
-                    v[i][j] *= inv;
+                if (idx >= cv || idx * VE + j >= V) v[i][j] = -INFINITY;
+                m = fmaxf(m, v[i][j]);
             }
-            store_vec(y + idx * VE, v[i]);
+        }
+        m = block_max<NW>(m, sh);
+        // e^{l - m} = 2^{(l - m) log2 e} on the hardware base-2 exponential; the
+        // difference is formed first, so the argument's rounding error scales with
+        // |l - m| (tiny probabilities), not with |l|.
+        const float L2E = 1.4426950408889634f;
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < PT; i++)
+#pragma unroll
+            for (int j = 0; j < VE; j++) {
+                v[i][j] = __builtin_amdgcn_exp2f((v[i][j] - m) * L2E);  // 2^-inf = 0 for padding
+                s += v[i][j];
+            }
+        s = block_sum<NW>(s, sh);
+        if (losses && threadIdx.x == 0) losses[row] = logf(s) + m - lt;
+        if (!probs) return;
+        const float inv = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < PT; i++) {
+            int idx = threadIdx.x + i * NT;
+            if (idx < cv) {
+#pragma unroll
+                for (int j = 0; j < VE; j++) {
+                    if constexpr (BWD)
+                        v[i][j] = (v[i][j] * inv - (idx * VE + j == tg ? 1.f : 0.f)) * dscale;
+                    else
+                        v[i][j] *= inv;
+                }
+                store_vec(y + idx * VE, v[i]);
+            }
         }
     }
 }
@@ -402,6 +484,13 @@ static void launch_softmax_t(T* probs, const T* logits, int N, int V, int Vp, hi
         return;
     }
     const int pt = (cv + 1023) / 1024;
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (pt == 7 && N >= 512) {  // GPT-2's vocabulary, many rows
+            softmax_kernel<T, 7, 1024, BWD, true><<<grid, 1024, 0, s>>>(probs, logits, V, Vp, targets, losses,
+                                                                          dscale);
+            return;
+        }
+    }
     if (pt <= 1) SM_LAUNCH(1, 1024);
     else if (pt <= 2) SM_LAUNCH(2, 1024);
     else if (pt <= 4) SM_LAUNCH(4, 1024);
