@@ -66,6 +66,11 @@ def parse():
     ap.add_argument("--profile-kernel", action="store_true",
                     help="counter-collection mode: launch only the dominant kernel (3x: the logits "
                          "GEMM, or the decode attention) and a 256 MiB device copy (calibration)")
+    ap.add_argument("--profile-target", default="vocab",
+                    choices=["vocab", "attention", "qkv", "attproj", "fc", "fcproj"],
+                    help="with --profile-kernel on a prefill workload: which kernel to launch (the "
+                         "vocabulary GEMM, the prefill attention, or one layer-0 projection with its "
+                         "forward epilogue), on the workload's shapes")
     return ap.parse_args()
 
 
@@ -533,12 +538,14 @@ def source_sha1(files):
     return h.hexdigest()
 
 
-def profile_kernel(b):
-    """Counter-collection mode (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE): launch
-    the workload's dominant kernel three times, then one plain 256 MiB
-    device-to-device copy whose known bytes calibrate the counters. Forward
-    workloads: the vocabulary GEMM; decode: attention over the KV cache of
-    layers 0..2 (one decode_attn launch, plus its combine when it splits)."""
+def profile_kernel(b, target="vocab"):
+    """Counter-collection mode (rocprofv3 --pmc): launch the workload's dominant
+    kernel three times, then one plain 256 MiB device-to-device copy whose known
+    bytes calibrate the traffic counters. Forward workloads: the vocabulary GEMM
+    (or, by target, the prefill attention over random q, k, v, or one layer-0
+    projection on random activations with the forward's epilogue); decode:
+    attention over the KV cache of layers 0..2 (one decode_attn launch, plus its
+    combine when it splits)."""
     torch, G, I, w = b.torch, b.G, b.I, b.w
     if b.decode:
         B, C, NH = w.B, w.C, w.NH
@@ -548,6 +555,32 @@ def profile_kernel(b):
         for l in range(3):
             G.attention_decode_forward(att, qkv, b.kcache[l], b.vcache[l], w.decode_pos, NH, aws)
         info = {"kernel": "attention_decode", "shape": [B, NH, w.decode_pos + 1, w.hs]}
+    elif target == "attention":
+        qkv = torch.randn(w.B, w.T, 3 * w.C, device="cuda").to(b.tdtype)
+        att = torch.empty(w.B, w.T, w.C, dtype=b.tdtype, device="cuda")
+        for _ in range(3):
+            G.attention_forward(att, qkv, w.NH)
+        info = {"kernel": "attention", "shape": [w.B, w.T, w.C, w.NH]}
+    elif target != "vocab":
+        N = w.B * w.T
+        offs = I.param_offsets(w.L, w.C, w.maxT, w.Vp)
+
+        def par(name):  # layer 0's slice of a stacked parameter
+            o, shp = offs[name]
+            return b.params[o:o + int(np.prod(shp[1:]))].view(*shp[1:])
+        wgt, bias = par(target + "_w"), par(target + "_b")
+        OC, K = wgt.shape
+        inp = torch.randn(N, K, device="cuda").to(b.tdtype)
+        out = torch.empty(N, OC, dtype=b.tdtype, device="cuda")
+        res = torch.randn(N, OC, device="cuda").to(b.tdtype)
+        for _ in range(3):
+            if target == "fc":
+                G.matmul_gelu_forward(out, inp, wgt, bias)
+            elif target in ("attproj", "fcproj"):
+                G.matmul_residual_forward(out, inp, wgt, bias, res)
+            else:
+                G.matmul_forward(out, inp, wgt, bias)
+        info = {"kernel": G.matmul_kernel_config(N, K, OC, w.dtype), "shape": [N, K, OC]}
     else:
         N = w.B * w.T
         o, shp = I.param_offsets(w.L, w.C, w.maxT, w.Vp)["wte"]
@@ -710,7 +743,7 @@ def main():
         sys.exit(2)
     b = Bench(w, keep_host_cache=decode and not args.no_cpu_baseline, train=train)
     if args.profile_kernel:
-        profile_kernel(b)
+        profile_kernel(b, args.profile_target)
         return
     if args.elementwise:
         print(json.dumps({"workload": args.workload, "dtype": "bf16" if w.dtype == I.BF16 else "f32",
