@@ -312,11 +312,11 @@ def test_residual_layernorm(dt, N, C, splits):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N,C,OC", [(8192, 768, 776), (8200, 768, 3000), (8200, 3072, 768), (600, 3072, 776),
-                                    (2100, 768, 1000)])
+                                    (2100, 768, 1000), (4100, 768, 2304), (4100, 768, 3072)])
 def test_matmul_tile_paths_sampled(dt, N, C, OC):
-    """Shapes that select every pipelined tile (64x64 .. 256x128), with ragged
-    row and column tails; the oracle recomputes sampled rows, including the
-    last (partial) row tile."""
+    """Shapes that select every pipelined tile (64x64 .. 256x128, and the qkv /
+    fc tiles at GPT-2 small's widths), with ragged row and column tails; the
+    oracle recomputes sampled rows, including the last (partial) row tile."""
     announce("matmul-tiles", dt, N, C, OC, G.matmul_kernel_config(N, C, OC, DT[dt]))
     d = DT[dt]
     a = I.random_tensor(24, (N, C), 1.0, d)

@@ -34,10 +34,12 @@ struct PipeCfg {
 };
 enum GemmCfg {
     S32 = 0, R64x64, R64x128, R128x96,
-    P128x96_S4, P128x96_S5, P256x128_S3A, P128x128_O2,                    // fp32
+    P128x96_S4, P128x96_S5, P256x128_S3A, P128x128_O2, P128x288_I, P128x192_R4,  // fp32
     P128x256_O4, P128x256_R3, P256x128_G, P128x128_R4, P128x128_K3, P256x256_K2, P128x192_K2,  // bf16
     G_NCFG
 };
+// fp32 128x288_p2: 4 wavefronts of 32x288 (nine accumulator tiles each), so GPT-2 small's qkv
+// (2304 wide) is 256 tiles, one round of the CUs; 128x192_p4_r64: four stages of 64-byte rows.
 // "_p<S>" = S-stage pipeline; "_o<n>" = registers capped so n wavefronts fit per SIMD (2 or 3
 // workgroups per CU); "_k128" = 128-byte k-rows per stage (twice the default bf16 depth); "g" =
 // grouped XCD-aware walk (the fp32 vocabulary tile walks columns instead). 256x256_p2_k128:
@@ -47,6 +49,7 @@ enum GemmCfg {
 static const PipeCfg kCfg[G_NCFG] = {
     {"skinny32", 0},          {"64x64_r", 0},          {"64x128_r", 0},         {"128x96_r", 0},
     {"128x96_p4", 128},       {"128x96_p5", 128},      {"256x128_p3", 128},     {"128x128_p4_o2", 64},
+    {"128x288_p2", 128},      {"128x192_p4_r64", 64},
     {"128x256_p3_o4", 64},    {"128x256_p3_k128", 128}, {"256x128_p3g", 128},
     {"128x128_p4_k128", 128}, {"128x128_p3_k128", 128}, {"256x256_p2_k128", 128},
     {"128x192_p2_k128", 128},
@@ -57,6 +60,8 @@ static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
         if (N >= 16384) return P256x128_S3A;                 // vocabulary projection
         if (K >= 2048) return P128x96_S5;                    // fcproj
         if (N <= 1024) return P128x96_S4;                    // attproj
+        if (N % 288 == 0) return P128x288_I;                 // qkv at GPT-2 small's width
+        if (N % 192 == 0) return P128x192_R4;                // fc at GPT-2 small's width
         return N >= 3072 ? P128x128_O2 : P128x96_S5;         // fc, qkv
     }
     // bf16, chosen with operands cold in HBM, as in the forward (a pipeline
@@ -103,6 +108,8 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
         case P128x96_S5: PIPE(4, 1, 1, 3, 128, 5, 4, 0, 8, 1); break;
         case P256x128_S3A: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 1, 0); break;
         case P128x128_O2: PIPE(2, 2, 2, 2, 64, 4, 2, 2, 4, 1); break;
+        case P128x288_I: PIPE(4, 1, 1, 9, 128, 2, 1, 0, 8, 1); break;
+        case P128x192_R4: PIPE(2, 2, 2, 3, 64, 4, 2, 0, 4, 1); break;
         default:
             if constexpr (std::is_same<T, bf16>::value) {  // the bf16-only shapes (choose_pipe)
                 switch (choose_cfg(M, N, K, dtype)) {
