@@ -204,7 +204,8 @@ def test_backward_workspace_sizes():
     base = _a256(C * OC * 4) + _a256(OC * N * 4) + _a256(C * N * 4) + _a256(N // 64 * OC * 4)
     assert G.matmul_backward_workspace_size(N, C, OC, 0) == base + _a256(4 * OC * C * 4)  # 4 slices
     base16 = _a256(C * OC * 2) + _a256(OC * N * 2) + _a256(C * N * 2) + _a256(N // 64 * OC * 4)
-    assert G.matmul_backward_workspace_size(N, C, OC, 1) == base16  # bf16: no split
+    # bf16: fp32 partials of 4 slices (108 tiles of 128x128 -> 432 workgroups)
+    assert G.matmul_backward_workspace_size(N, C, OC, 1) == base16 + _a256(4 * OC * C * 4)
     # training activations: per layer x, ln1, att, res1, ln2 [N,C]; qkv [N,3C]; fc, gelu [N,4C];
     # four fp32 statistics [N]; lse [NH,N]; then xf, lnf [N,C], lnf stats, logits [N,Vp], losses
     w = I.WORKLOADS["small"]

@@ -173,10 +173,11 @@ def test_matmul_backward_integer_exact(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("C,OC", [(768, 2304), (3072, 768)])
+@pytest.mark.parametrize("C,OC", [(768, 2304), (3072, 768), (768, 768)])
 def test_matmul_backward_gpt2_small_sampled(dt, C, OC):
-    """B4 T1024 shapes; dinp on sampled rows and dweight/dbias on sampled output
-    features, each from the oracle on the corresponding slice."""
+    """B4 T1024 shapes (the weight gradient in 4, 1 and 8 k-slices for bf16);
+    dinp on sampled rows and dweight/dbias on sampled output features, each
+    from the oracle on the corresponding slice."""
     announce("matmul_backward_full", dt, C, OC)
     d = DT[dt]
     N = 4096

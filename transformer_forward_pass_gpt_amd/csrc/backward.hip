@@ -18,6 +18,7 @@ namespace gpt2 {
 
 int launch_matmul(void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
 int launch_matmul_splitk_part(float*, const float*, const float*, int, int, int, int, int, hipStream_t);
+int launch_matmul_splitk_part(float*, const bf16*, const bf16*, int, int, int, int, int, hipStream_t);
 int launch_matmul_kmajor(float*, const float*, const float*, int, int, int, int, int, bool, bool, int, hipStream_t);
 
 static constexpr int kBwdThreads = 256;
@@ -347,16 +348,23 @@ static void launch_transpose(T* out, float* colpart, const T* in, int R, int Cc,
 // 64, so the K loop of the pipelined GEMM has no tail.
 static int64_t round64(int64_t n) { return (n + 63) / 64 * 64; }
 
-// Split-k count for the weight gradient (fp32): its OC x C output in 128x96
-// tiles is often far below the chip's 256 CUs while K = Np is deep, so the
-// token range is cut into up to 8 slices (each a whole number of 32-deep
-// k-tiles, at least 256 deep) until there are >= 512 workgroups. bf16 keeps
-// one slice (its partial products would be rounded to bf16).
+// Split-k count for the weight gradient: its OC x C output (fp32 in 128x96
+// tiles, bf16 in 128x128) is often far below the chip's 256 CUs while K = Np
+// is deep, so the token range is cut into up to 8 slices (each a whole number
+// of k-tiles, 32 deep for fp32 and 64 for bf16, at least 256 deep) until there
+// are >= 512 workgroups (fp32) or >= 256 (bf16, one 128x128 workgroup per
+// CU; outputs of 128 or more tiles stay whole: two half-depth rounds take as
+// long as one full one, plus the partials' traffic). The slices' products are
+// fp32 partial sums in both dtypes, added in slice order by splitsum_kernel.
 static int dw_splits(int N, int C, int OC, int dtype) {
-    if (dtype != GPT2_F32) return 1;
-    const int64_t Np = round64(N), tiles = (int64_t)((OC + 127) / 128) * ((C + 95) / 96);
+    const bool f32 = dtype == GPT2_F32;
+    const int64_t Np = round64(N), kt = f32 ? 32 : 64;
+    const int64_t tiles = (int64_t)((OC + 127) / 128) * ((C + (f32 ? 95 : 127)) / (f32 ? 96 : 128));
+    const int64_t target = f32 ? 512 : 256;
+    if (!f32 && tiles >= 128) return 1;
     int s = 1;
-    while (s < 8 && tiles * s < 512 && (Np / (2 * s)) % 32 == 0 && Np / (2 * s) >= 256 && Np % (2 * s) == 0) s *= 2;
+    while (s < 8 && tiles * s < target && (Np / (2 * s)) % kt == 0 && Np / (2 * s) >= 256 && Np % (2 * s) == 0)
+        s *= 2;
     return s;
 }
 
@@ -389,7 +397,7 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
     p += align256((int64_t)C * Np * es);
     float* bpart = (float*)p;
     p += align256(Np / 64 * OC * 4);
-    float* wpart = (float*)p;  // split-k partials of dweight (fp32 only)
+    float* wpart = (float*)p;  // split-k partials of dweight
     int rc = GPT2_OK;
     if constexpr (std::is_same<T, float>::value) {
         // k-major operands read in place: dinp = dout . W with W as stored
@@ -427,15 +435,12 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
     if (dweight || dbias) launch_transpose<T>(doutT, dbias ? bpart : nullptr, dout, N, OC, (int)Np, s);
     if (dweight) {
         launch_transpose<T>(inpT, nullptr, inp, N, C, (int)Np, s);
-        if constexpr (std::is_same<T, float>::value) {
-            if (S > 1) {
-                rc = launch_matmul_splitk_part(wpart, doutT, inpT, OC, C, (int)(Np / S), (int)Np, S, s);
-                if (rc) return rc;
-                const int64_t n = (int64_t)OC * C;
-                splitsum_kernel<T><<<stream_grid_bwd(n / 4), 256, 0, s>>>(dweight, wpart, S, n);
-            }
-        }
-        if (S == 1) {
+        if (S > 1) {
+            rc = launch_matmul_splitk_part(wpart, doutT, inpT, OC, C, (int)(Np / S), (int)Np, S, s);
+            if (rc) return rc;
+            const int64_t n = (int64_t)OC * C;
+            splitsum_kernel<T><<<stream_grid_bwd(n / 4), 256, 0, s>>>(dweight, wpart, S, n);
+        } else {
             rc = launch_matmul(dweight, doutT, inpT, nullptr, OC, (int)Np, C, dtype, s);
             if (rc) return rc;
         }

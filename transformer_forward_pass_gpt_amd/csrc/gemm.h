@@ -223,6 +223,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __re
 // writes its product to out + y*split_out; A and W rows are then lda and ldb
 // elements long (without SPLITK they are K long and lda, ldb, split_out are
 // unused).
+// TO: the output type; fp32 products of bf16 operands (split-k partial sums
+// that a later fp32 sum reduces) take the plain epilogue only.
 // TA / TB (fp32): the operand is stored k-major, A as [K][M] (row stride
 // lda), W as [K][N] (row stride ldb): out = A^T-stored . W^T-stored without a
 // transpose pass. Its tile is copied as BK rows of BM (BN) elements and a
@@ -230,10 +232,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __re
 // one read take k-rows 4 apart (k = 8kc + 4h + e), so k-rows with bit 2 set
 // are rotated by 8 chunks (32 banks) and the two halves use disjoint banks.
 template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false,
-          int EPI = EPI_BIAS, bool SPLITK = false, bool TA = false, bool TB = false>
-__global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, const T* __restrict__ A,
+          int EPI = EPI_BIAS, bool SPLITK = false, bool TA = false, bool TB = false, typename TO = T>
+__global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, const T* __restrict__ A,
                                                                 const T* __restrict__ W,
-                                                                const T* __restrict__ bias, const T* res, int M,
+                                                                const T* __restrict__ bias, const TO* res, int M,
                                                                 int N, int K, int group_m, int remap, int lda,
                                                                 int ldb, int64_t split_out,
                                                                 float* __restrict__ stats, int vlim) {
@@ -256,10 +258,13 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
     static_assert(!(TA || TB) || (CMA >= 16 && CMB >= 16), "k-major tiles need >= 16 chunks per k-row");
     static_assert(LPW * (S - 2) < 64, "vmcnt range");
     constexpr int STAGE = (BM + BN) * BK;  // elements per stage (A tile then W tile)
-    constexpr int LDO = BN + VE;           // row stride of the output tile in the epilogue
+    constexpr int VO = Vec<TO>::N;          // output elements per 16-byte vector
+    static_assert(std::is_same<TO, T>::value || (EPI == EPI_BIAS && !TA && !TB), "wider output: plain products only");
+    constexpr int LDO = BN + VO;           // row stride of the output tile in the epilogue
     // stage the output tile through LDS when it fits in 160 KiB
-    constexpr bool STAGED = !DIRECT && BM * LDO * (int)sizeof(T) <= 160 * 1024;
-    constexpr int SMEM = (STAGED && BM * LDO > S * STAGE) ? BM * LDO : S * STAGE;
+    constexpr bool STAGED = !DIRECT && BM * LDO * (int)sizeof(TO) <= 160 * 1024;
+    constexpr int SOUT = BM * LDO * (int)sizeof(TO) / (int)sizeof(T);  // staged tile, in T elements
+    constexpr int SMEM = (STAGED && SOUT > S * STAGE) ? SOUT : S * STAGE;
     __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -445,7 +450,7 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
     // elements.
     if constexpr (STAGED) {
         __builtin_amdgcn_s_barrier();
-        T* so = smem;
+        TO* so = reinterpret_cast<TO*>(smem);
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int cl = wn * TN * 32 + j * 32 + r32;
@@ -462,7 +467,7 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
         }
         __builtin_amdgcn_s_waitcnt((0xF) | (7 << 4) | (0x0 << 8) | (3 << 14));  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        constexpr int CPR = BN / VE;  // 16-byte chunks per tile row
+        constexpr int CPR = BN / VO;  // 16-byte chunks per tile row
         if constexpr (EPI == EPI_BIAS_RESIDUAL) {
             // every residual chunk of this thread is loaded before the first
             // add (rows and columns clamped into the matrix; out-of-range
@@ -472,20 +477,20 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
 #pragma unroll
             for (int j = 0; j < NCH; j++) {
                 const int c = min(tid + j * NW * 64, BM * CPR - 1);
-                const int row = min(m0 + c / CPR, M - 1), col = min(n0 + (c % CPR) * VE, N - VE);
+                const int row = min(m0 + c / CPR, M - 1), col = min(n0 + (c % CPR) * VO, N - VO);
                 rv[j] = *reinterpret_cast<const u32x4*>(res + (int64_t)row * N + col);
             }
 #pragma unroll
             for (int j = 0; j < NCH; j++) {
                 const int c = tid + j * NW * 64;
                 const int rl = c / CPR, cv = c % CPR;
-                const int row = m0 + rl, col = n0 + cv * VE;
+                const int row = m0 + rl, col = n0 + cv * VO;
                 if (c < BM * CPR && row < M && col < N) {
-                    float a[VE], r[VE];
-                    unpack_vec<T>(*reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]), a);
-                    unpack_vec<T>(rv[j], r);
+                    float a[VO], r[VO];
+                    unpack_vec<TO>(*reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VO]), a);
+                    unpack_vec<TO>(rv[j], r);
 #pragma unroll
-                    for (int e = 0; e < VE; e++) a[e] += r[e];
+                    for (int e = 0; e < VO; e++) a[e] += r[e];
                     store_vec(out + (int64_t)row * N + col, a);
                 }
             }
@@ -496,39 +501,39 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
             // scaled difference) in a second pass. Consecutive lanes take
             // consecutive rows: 528-byte rows put them on distinct banks.
             static_assert(BN % kStatCols == 0, "stats groups must tile the output tile");
-            constexpr int NG = BN / kStatCols, GCH = kStatCols / VE;
+            constexpr int NG = BN / kStatCols, GCH = kStatCols / VO;
             const int ngrp = (N + kStatCols - 1) / kStatCols;
             const float L2E = 1.4426950408889634f;
 #pragma unroll 4
             for (int c = tid; c < BM * CPR; c += NW * 64) {
                 const int rl = c / CPR, cv = c % CPR;
-                const int row = m0 + rl, col = n0 + cv * VE;
+                const int row = m0 + rl, col = n0 + cv * VO;
                 if (row < M && col < N)
                     *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) =
-                        *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]);
+                        *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VO]);
             }
             for (int p = tid; p < BM * NG; p += NW * 64) {
                 const int rl = p % BM, gi = p / BM;
                 const int row = m0 + rl, c0 = n0 + gi * kStatCols, grp = c0 / kStatCols;
-                const T* src = &so[rl * LDO + gi * kStatCols];
+                const TO* src = &so[rl * LDO + gi * kStatCols];
                 float mx = -INFINITY;
 #pragma unroll 4
                 for (int j = 0; j < GCH; j++) {
-                    float y[VE];
-                    unpack_vec<T>(*reinterpret_cast<const u32x4*>(src + j * VE), y);
+                    float y[VO];
+                    unpack_vec<TO>(*reinterpret_cast<const u32x4*>(src + j * VO), y);
 #pragma unroll
-                    for (int e = 0; e < VE; e++)
-                        if (c0 + j * VE + e < vlim) mx = fmaxf(mx, y[e]);
+                    for (int e = 0; e < VO; e++)
+                        if (c0 + j * VO + e < vlim) mx = fmaxf(mx, y[e]);
                 }
                 float sm = 0.f;
                 if (mx != -INFINITY) {
 #pragma unroll 4
                     for (int j = 0; j < GCH; j++) {
-                        float y[VE];
-                        unpack_vec<T>(*reinterpret_cast<const u32x4*>(src + j * VE), y);
+                        float y[VO];
+                        unpack_vec<TO>(*reinterpret_cast<const u32x4*>(src + j * VO), y);
 #pragma unroll
-                        for (int e = 0; e < VE; e++)
-                            sm += c0 + j * VE + e < vlim ? __builtin_amdgcn_exp2f((y[e] - mx) * L2E) : 0.f;
+                        for (int e = 0; e < VO; e++)
+                            sm += c0 + j * VO + e < vlim ? __builtin_amdgcn_exp2f((y[e] - mx) * L2E) : 0.f;
                     }
                 }
                 if (row < M && grp < ngrp) {
@@ -541,10 +546,10 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(T* out, con
 #pragma unroll 4
             for (int c = tid; c < BM * CPR; c += NW * 64) {
                 const int rl = c / CPR, cv = c % CPR;
-                const int row = m0 + rl, col = n0 + cv * VE;
+                const int row = m0 + rl, col = n0 + cv * VO;
                 if (row < M && col < N)
                     *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) =
-                        *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VE]);
+                        *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VO]);
             }
         }
     } else {
@@ -612,8 +617,8 @@ static void launch_gemm_kmajor(float* out, const float* A, const float* W, const
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(nwg, splits);
     gemm_pipe_kernel<float, WM, WN, TM, TN, RB, S, SCHED, WPE, false, EPI_BIAS, true, TA, TB>
-        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, nullptr, M, N, K, group_m, remap, lda, ldb, split_out,
-                                       nullptr, 0);
+        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, static_cast<const float*>(nullptr), M, N, K, group_m, remap,
+                                       lda, ldb, split_out, nullptr, 0);
 }
 
 template <typename T, int WM, int WN, int TM, int TN, int SCHED = 4>

@@ -190,6 +190,18 @@ int launch_matmul_splitk_part(float* part, const float* A, const float* W, int M
     return launch_status();
 }
 
+// The same with bf16 operands: fp32 partial products (no rounding to bf16
+// before the fp32 sum of the slices), 128x128 tiles; Kc % 64 == 0.
+int launch_matmul_splitk_part(float* part, const bf16* A, const bf16* W, int M, int N, int Kc, int lda, int splits,
+                              hipStream_t s) {
+    if (Kc % 64 || splits < 1 || (int64_t)Kc * splits > lda) return GPT2_ERR_INVALID_ARGUMENT;
+    const int nwg = ((M + 127) / 128) * ((N + 127) / 128);
+    gemm_pipe_kernel<bf16, 2, 2, 2, 2, 128, 3, 2, 0, false, EPI_BIAS, true, false, false, float>
+        <<<dim3(nwg, splits), 256, 0, s>>>(part, A, W, nullptr, nullptr, M, N, Kc, 8, 1, lda, lda, (int64_t)M * N,
+                                           nullptr, 0);
+    return launch_status();
+}
+
 // fp32 products with k-major operands (no transpose pass): out [M,N] (slice y
 // of `splits` at out + y*M*N) = sum over k of A(k, m) W(k, n), A stored
 // [K][M] (rows lda apart) when ta else [M][K] (lda = K), W stored [K][N]
