@@ -230,7 +230,7 @@ def test_attention_lse(dt, B, T, C, NH):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("B,T,C,NH", [(2, 32, 64, 4), (1, 77, 64, 2), (2, 200, 128, 2), (1, 1, 64, 1),
-                                      (1, 130, 64, 1)])
+                                      (1, 130, 64, 1), (3, 257, 192, 3)])
 def test_attention_backward(dt, B, T, C, NH):
     announce("attention_backward", dt, B, T, C, NH)
     d = DT[dt]

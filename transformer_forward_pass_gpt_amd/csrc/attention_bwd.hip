@@ -756,6 +756,336 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(bf16* __restrict_
         }
 }
 
+// ---------------------------------------------------------- bf16, hs = 64
+// The same two walks at head size 64 (GPT-2 small and medium) with the
+// forward kernel's operand machinery: every 64-row operand tile goes from
+// HBM/L2 to LDS by load-to-LDS copies (no VGPR staging), twice, in two chunk
+// permutations of its 128-byte rows: for the row reads of the head-dim
+// contractions (S, dP: slot = chunk ^ ((row/2) % 8), conflict-free 16-row
+// fragment reads), and for the transposing reads (ds_read_b64_tr_b16) that
+// give the query / key contractions their transposed operand (slot = chunk ^
+// 4*((row/2) % 2)): in each 16-lane group lane 4j+q addresses 4 head dims of
+// row j, lane i receives head dim i of rows 0..3, so two reads give a lane the
+// 8 rows 16j' + 4h + 0..3 and 16j' + 8 + 4h + 0..3 that pack8 takes from the
+// accumulator. Two stages: tile t+1 lands while tile t is multiplied. Rows
+// past the sequence copy its last row (finite; their P and dS are 0).
+namespace bwd64 {
+constexpr int HS = 64, TILE = kAB * HS;  // one 64 x 64 bf16 operand tile
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+// Per-lane copy offsets (elements, inside the head's row) of the two 8-row
+// copy instructions of wave wid: rows 16 wid + 8i + lane/8, LDS slot lane % 8.
+struct CopyRows {
+    int row[2], offr[2], offt[2];
+    __device__ __forceinline__ CopyRows(int wid, int lane) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            row[i] = 16 * wid + 8 * i + (lane >> 3);
+            offr[i] = ((lane & 7) ^ ((row[i] >> 1) & 7)) * 8;
+            offt[i] = ((lane & 7) ^ (4 * ((row[i] >> 1) & 1))) * 8;
+        }
+    }
+};
+
+// Copy rows r0 .. r0+63 of a [rows, ld] tensor's head columns (src points at
+// the head's first column) into the row-read tile tr and, if tt, the
+// transposing-read tile tt; rows clamped to the sequence.
+__device__ __forceinline__ void copy_tile(const CopyRows& cr, const bf16* src, int64_t ld, int r0, int Tn, int wid,
+                                          bf16* tr, bf16* tt) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const bf16* rp = src + (int64_t)min(r0 + cr.row[i], Tn - 1) * ld;
+        copy16_to_lds(rp + cr.offr[i], (lds_void_ptr)(tr + (16 * wid + 8 * i) * HS));
+        if (tt) copy16_to_lds(rp + cr.offt[i], (lds_void_ptr)(tt + (16 * wid + 8 * i) * HS));
+    }
+}
+
+// Row-read fragment: row `row` (a multiple of 16 plus r32) of a row-read tile,
+// head dims 16i + 8h .. +7.
+__device__ __forceinline__ u32x4 row_frag(const bf16* t, int row, int i, int h) {
+    return *reinterpret_cast<const u32x4*>(t + row * HS + ((2 * i + h) ^ ((row >> 1) & 7)) * 8);
+}
+
+// Transposed fragment of a transposing-read tile: A[head dim 32 dt + r32][k-slot]
+// with k-slots = rows r0 + 16j' pattern above (r0 a multiple of 16).
+struct TrRead {
+    int vbase[2];
+    __device__ __forceinline__ TrRead(int lane) {
+        const int h = lane >> 5, r32 = lane & 31;
+        const int gj = (lane & 15) >> 2, gq = lane & 3;
+        const int vy = (gj >> 1) & 1, vx = 2 * (r32 >> 4) + (gq >> 1);
+#pragma unroll
+        for (int dt = 0; dt < 2; dt++) vbase[dt] = (4 * h + gj) * HS + (4 * (dt ^ vy) + vx) * 8 + (gq & 1) * 4;
+    }
+    __device__ __forceinline__ u32x4 operator()(const bf16* t, int r0, int dt) const {
+        const lds_v4s_ptr p = (lds_v4s_ptr)t;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p + (vbase[dt] + r0 * HS) / 4);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p + (vbase[dt] + (r0 + 8) * HS) / 4);
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    }
+};
+}  // namespace bwd64
+
+// dK, dV (bf16, hs 64): workgroup and wave roles as attn_bwd_dkv_kernel.
+__global__ __launch_bounds__(256) void attn_bwd_dkv_bf16_d64_kernel(bf16* __restrict__ dqkv,
+                                                                    const bf16* __restrict__ qkv,
+                                                                    const bf16* __restrict__ dout,
+                                                                    const float* __restrict__ lse,
+                                                                    const float* __restrict__ Dg, int Tn, int C,
+                                                                    int NH, float sl2, float scale) {
+    using namespace bwd64;
+    constexpr int DT = 2;
+    constexpr int STAGE = 4 * TILE + 4 * kAB;  // Q, Q^T-read, dO, dO^T-read tiles; lse2, D (fp32 = 2 bf16 each)
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kc = wid & 1, par = wid >> 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
+    const int kb = blockIdx.y;
+    const int k0 = kb * kAB + kc * 32, key = k0 + r32;
+    const int64_t rs = 3 * (int64_t)C;
+    const bf16* base = qkv + (int64_t)b * Tn * rs;
+    const bf16* qsrc = base + hd * HS;
+    const bf16* dsrc = dout + (int64_t)b * Tn * C + hd * HS;
+    const float* lrow = lse + (int64_t)bh * Tn;
+    const float* drow = Dg + (int64_t)bh * Tn;
+    const float L2E = 1.4426950408889634f;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    // this lane's key and value row: B operands of S = Q K^T and dP = dO V^T
+    u32x4 kf[4], vf[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const bf16* kr = base + (int64_t)min(key, Tn - 1) * rs + C + hd * HS + 16 * i + 8 * h;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kr);
+        const u32x4 c = *reinterpret_cast<const u32x4*>(kr + C);
+        kf[i] = key < Tn ? a : z4;
+        vf[i] = key < Tn ? c : z4;
+    }
+
+    const CopyRows cr(wid, lane);
+    const TrRead trr(lane);
+    float rl = 0.f, rD = 0.f;
+    auto issue = [&](int st, int qt) {
+        bf16* s0 = smem + st * STAGE;
+        copy_tile(cr, qsrc, rs, qt * kAB, Tn, wid, s0, s0 + TILE);
+        copy_tile(cr, dsrc, C, qt * kAB, Tn, wid, s0 + 2 * TILE, s0 + 3 * TILE);
+        if (tid < kAB) {  // after the copies: the compiler's wait for these never counts them
+            const int q = min(qt * kAB + tid, Tn - 1);
+            rl = lrow[q];
+            rD = drow[q];
+        }
+    };
+    auto put_stats = [&](int st, int qt) {
+        float* sL = reinterpret_cast<float*>(smem + st * STAGE + 4 * TILE);
+        if (tid < kAB) {
+            const bool ok = qt * kAB + tid < Tn;
+            sL[tid] = ok ? rl * L2E : 0.f;
+            sL[kAB + tid] = ok ? rD : 0.f;
+        }
+    };
+
+    f32x16 dv[DT], dk[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) dv[dt] = dk[dt] = f32x16{};
+
+    auto compute = [&](int st, int qt) {
+        const bf16* sQ = smem + st * STAGE;
+        const bf16* sQt = sQ + TILE;
+        const bf16* sO = sQ + 2 * TILE;
+        const bf16* sOt = sQ + 3 * TILE;
+        const float* sL = reinterpret_cast<const float*>(sQ + 4 * TILE);
+        const float* sD = sL + kAB;
+        const int qb = qt * kAB + par * 32;
+        if (qb + 31 < k0) return;  // every query precedes every key: P = 0
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            s = mfma_bf16(row_frag(sQ, par * 32 + r32, i, h), kf[i], s);
+            dp = mfma_bf16(row_frag(sO, par * 32 + r32, i, h), vf[i], dp);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = 8 * (v >> 2) + 4 * h + (v & 3), q = qb + m;
+            const bool on = key <= q && q < Tn;
+            const float p = on ? __builtin_amdgcn_exp2f(s[v] * sl2 - sL[par * 32 + m]) : 0.f;
+            s[v] = p;
+            dp[v] = p * (dp[v] - sD[par * 32 + m]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const u32x4 pb = pack8(s, j), sb = pack8(dp, j);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                dv[dt] = mfma_bf16(trr(sOt, par * 32 + 16 * j, dt), pb, dv[dt]);
+                dk[dt] = mfma_bf16(trr(sQt, par * 32 + 16 * j, dt), sb, dk[dt]);
+            }
+        }
+    };
+
+    const int nqt = (Tn + kAB - 1) / kAB;
+    issue(0, kb);
+    put_stats(0, kb);
+    for (int qt = kb; qt < nqt; qt++) {
+        const int st = (qt - kb) & 1;
+        // this wave's copies of tile qt have landed (and its reads of the
+        // other stage are done); after the barrier every wave's have
+        wait_vmcnt_lds<0>();
+        __builtin_amdgcn_s_barrier();
+        if (qt + 1 < nqt) issue(st ^ 1, qt + 1);
+        compute(st, qt);
+        if (qt + 1 < nqt) put_stats(st ^ 1, qt + 1);
+    }
+    wait_vmcnt_lds<0>();
+    __builtin_amdgcn_s_barrier();  // every wave is done with the stages before the merge reuses them
+
+    float* mg = reinterpret_cast<float*>(smem) + kc * (2 * DT * 16 * 64);
+    if (par == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                mg[((2 * dt) * 16 + v) * 64 + lane] = dv[dt][v];
+                mg[((2 * dt + 1) * 16 + v) * 64 + lane] = dk[dt][v];
+            }
+    }
+    __syncthreads();
+    if (par == 1 || key >= Tn) return;
+    bf16* drow_k = dqkv + ((int64_t)b * Tn + key) * rs + C + hd * HS;
+    bf16* drow_v = drow_k + C;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int d0 = dt * 32 + 8 * g + 4 * h;
+            float x[4], y[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int v = 4 * g + e;
+                x[e] = dv[dt][v] + mg[((2 * dt) * 16 + v) * 64 + lane];
+                y[e] = (dk[dt][v] + mg[((2 * dt + 1) * 16 + v) * 64 + lane]) * scale;
+            }
+            store4(drow_v + d0, x[0], x[1], x[2], x[3]);
+            store4(drow_k + d0, y[0], y[1], y[2], y[3]);
+        }
+}
+
+// dQ (bf16, hs 64): workgroup and wave roles as attn_bwd_dq_kernel.
+__global__ __launch_bounds__(256) void attn_bwd_dq_bf16_d64_kernel(bf16* __restrict__ dqkv,
+                                                                   const bf16* __restrict__ qkv,
+                                                                   const bf16* __restrict__ dout,
+                                                                   const float* __restrict__ lse,
+                                                                   const float* __restrict__ Dg, int Tn, int C,
+                                                                   int NH, float sl2, float scale) {
+    using namespace bwd64;
+    constexpr int DT = 2;
+    constexpr int STAGE = 3 * TILE;  // K, K^T-read, V tiles
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qc = wid & 1, par = wid >> 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
+    const int qt = gridDim.y - 1 - blockIdx.y;  // the last (longest) query tiles first
+    const int qw = qt * kAB + qc * 32, q = qw + r32;
+    const int64_t rs = 3 * (int64_t)C;
+    const bf16* base = qkv + (int64_t)b * Tn * rs;
+    const float L2E = 1.4426950408889634f;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    u32x4 qf[4], df[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(base + (int64_t)min(q, Tn - 1) * rs + hd * HS + 16 * i + 8 * h);
+        const u32x4 c = *reinterpret_cast<const u32x4*>(dout + ((int64_t)b * Tn + min(q, Tn - 1)) * C + hd * HS +
+                                                        16 * i + 8 * h);
+        qf[i] = q < Tn ? a : z4;
+        df[i] = q < Tn ? c : z4;
+    }
+    const float l2 = q < Tn ? lse[(int64_t)bh * Tn + q] * L2E : 0.f;
+    const float Dq = q < Tn ? Dg[(int64_t)bh * Tn + q] : 0.f;
+
+    const CopyRows cr(wid, lane);
+    const TrRead trr(lane);
+    auto issue = [&](int st, int kt) {
+        bf16* s0 = smem + st * STAGE;
+        copy_tile(cr, base + C + hd * HS, rs, kt * kAB, Tn, wid, s0, s0 + TILE);
+        copy_tile(cr, base + 2 * C + hd * HS, rs, kt * kAB, Tn, wid, s0 + 2 * TILE, nullptr);
+    };
+
+    f32x16 dq[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) dq[dt] = f32x16{};
+
+    auto compute = [&](int st, int kt) {
+        const bf16* sK = smem + st * STAGE;
+        const bf16* sKt = sK + TILE;
+        const bf16* sV = sK + 2 * TILE;
+        const int kbse = kt * kAB + par * 32;
+        if (kbse > qw + 31) return;  // every key follows every query
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            s = mfma_bf16(row_frag(sK, par * 32 + r32, i, h), qf[i], s);
+            dp = mfma_bf16(row_frag(sV, par * 32 + r32, i, h), df[i], dp);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+            const bool on = kbse + m <= q && q < Tn;
+            const float p = on ? __builtin_amdgcn_exp2f(s[v] * sl2 - l2) : 0.f;
+            dp[v] = p * (dp[v] - Dq);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const u32x4 sb = pack8(dp, j);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) dq[dt] = mfma_bf16(trr(sKt, par * 32 + 16 * j, dt), sb, dq[dt]);
+        }
+    };
+
+    const int nkt = qt + 1;
+    issue(0, 0);
+    for (int kt = 0; kt < nkt; kt++) {
+        const int st = kt & 1;
+        wait_vmcnt_lds<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + 1 < nkt) issue(st ^ 1, kt + 1);
+        compute(st, kt);
+    }
+    wait_vmcnt_lds<0>();
+    __builtin_amdgcn_s_barrier();
+
+    float* mg = reinterpret_cast<float*>(smem) + qc * (DT * 16 * 64);
+    if (par == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) mg[(dt * 16 + v) * 64 + lane] = dq[dt][v];
+    }
+    __syncthreads();
+    if (par == 1 || q >= Tn) return;
+    bf16* drow = dqkv + ((int64_t)b * Tn + q) * rs + hd * HS;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int d0 = dt * 32 + 8 * g + 4 * h;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int v = 4 * g + e;
+                x[e] = (dq[dt][v] + mg[(dt * 16 + v) * 64 + lane]) * scale;
+            }
+            store4(drow + d0, x[0], x[1], x[2], x[3]);
+        }
+}
+
 int64_t attention_backward_workspace_bytes(int B, int T, int NH) { return ((int64_t)B * NH * T * 4 + 255) & ~255LL; }
 
 template <typename T, int HS>
@@ -767,8 +1097,13 @@ static void launch_attn_bwd_hs(T* dqkv, const T* dout, const T* qkv, const T* ou
     attn_bwd_dot_kernel<T, HS><<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(D, dout, out, B, Tn, C, NH);
     const dim3 grid(B * NH, (Tn + kAB - 1) / kAB);
     if constexpr (std::is_same<T, bf16>::value) {
-        attn_bwd_dkv_bf16_kernel<HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
-        attn_bwd_dq_bf16_kernel<HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+        if constexpr (HS == 64) {
+            attn_bwd_dkv_bf16_d64_kernel<<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+            attn_bwd_dq_bf16_d64_kernel<<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+        } else {
+            attn_bwd_dkv_bf16_kernel<HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+            attn_bwd_dq_bf16_kernel<HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
+        }
     } else {
         attn_bwd_dkv_kernel<T, HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
         attn_bwd_dq_kernel<T, HS><<<grid, 256, 0, s>>>(dqkv, qkv, dout, lse, D, Tn, C, NH, sl2, scale);
