@@ -163,10 +163,14 @@ def test_matmul_backward(dt, N, C, OC):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_matmul_backward_integer_exact(dt):
-    announce("matmul_backward_integer", dt)
+@pytest.mark.parametrize("N,C,OC", [(96, 64, 136), (128, 72, 192)])
+def test_matmul_backward_integer_exact(dt, N, C, OC):
+    """Small-integer operands: every product and sum is exact in fp32 and the
+    results (|x| <= 216 for these seeds) in bf16. (96, 64, 136): contractions
+    that are not whole bf16 k-tiles (transposed operands in bf16); (128, 72,
+    192): both products on k-major operands read in place in both dtypes."""
+    announce("matmul_backward_integer", dt, N, C, OC)
     d = DT[dt]
-    N, C, OC = 96, 64, 136
     x, wt, dy, dx, dw, db = _linear_case(d, N, C, OC, 51, integer=True)
     rx, rw, rb = oracle.matmul_backward(dy, x, wt)
     assert np.array_equal(dx, rx) and np.array_equal(dw, rw) and np.array_equal(db, rb)
@@ -175,7 +179,7 @@ def test_matmul_backward_integer_exact(dt):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("C,OC", [(768, 2304), (3072, 768), (768, 768)])
 def test_matmul_backward_gpt2_small_sampled(dt, C, OC):
-    """B4 T1024 shapes (the weight gradient in 4, 1 and 8 k-slices for bf16);
+    """B4 T1024 shapes (the weight gradient in 4, 4 and 8 k-slices for bf16);
     dinp on sampled rows and dweight/dbias on sampled output features, each
     from the oracle on the corresponding slice."""
     announce("matmul_backward_full", dt, C, OC)

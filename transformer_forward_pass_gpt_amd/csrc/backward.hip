@@ -20,6 +20,9 @@ int launch_matmul(void*, const void*, const void*, const void*, int, int, int, i
 int launch_matmul_splitk_part(float*, const float*, const float*, int, int, int, int, int, hipStream_t);
 int launch_matmul_splitk_part(float*, const bf16*, const bf16*, int, int, int, int, int, hipStream_t);
 int launch_matmul_kmajor(float*, const float*, const float*, int, int, int, int, int, bool, bool, int, hipStream_t);
+int launch_matmul_kmajor(float*, const bf16*, const bf16*, int, int, int, int, int, bool, bool, int, float*,
+                         hipStream_t);
+int launch_matmul_kmajor(bf16*, const bf16*, const bf16*, int, int, int, int, int, bool, bool, int, hipStream_t);
 
 static constexpr int kBwdThreads = 256;
 
@@ -133,18 +136,24 @@ __global__ __launch_bounds__(256) void colpart_kernel(float* __restrict__ part, 
 }
 
 // out[i] = sum_{s < S} part[s * n + i] (s ascending), n = M*N elements, 16
-// bytes of T per thread: the split-k partial products of a weight gradient.
+// bytes of T per thread: the split-k partial products of a weight gradient;
+// then, when out2 is given, the same over the n2 elements of part2 into out2
+// (the slices' bias-gradient partials), in the same launch. n, n2 % V == 0.
 template <typename T>
-__global__ __launch_bounds__(256) void splitsum_kernel(T* out, const float* __restrict__ part, int S, int64_t n) {
+__global__ __launch_bounds__(256) void splitsum_kernel(T* out, const float* __restrict__ part, int S, int64_t n,
+                                                       T* out2, const float* __restrict__ part2, int n2) {
     constexpr int V = Vec<T>::N;
-    const int64_t nvec = n / V;
-    for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256) {
+    const int64_t nvec = n / V, nall = nvec + (out2 ? n2 / V : 0);
+    for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < nall; i += (int64_t)gridDim.x * 256) {
+        const bool first = i < nvec;
+        const float* src = first ? part + i * V : part2 + (i - nvec) * V;
+        const int64_t stride = first ? n : n2;
         float a[V];
 #pragma unroll
         for (int j = 0; j < V; j++) a[j] = 0.f;
         for (int sp = 0; sp < S; sp++) {
             float b[V];
-            const float* p = part + (int64_t)sp * n + i * V;
+            const float* p = src + (int64_t)sp * stride;
 #pragma unroll
             for (int j = 0; j < V; j += 4) {
                 const float4 x = *reinterpret_cast<const float4*>(p + j);
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(256) void splitsum_kernel(T* out, const float* __re
 #pragma unroll
             for (int j = 0; j < V; j++) a[j] += b[j];
         }
-        store_vec(out + i * V, a);
+        store_vec(first ? out + i * V : out2 + (i - nvec) * V, a);
     }
 }
 
@@ -339,13 +348,17 @@ static void launch_transpose(T* out, float* colpart, const T* in, int R, int Cc,
 
 // ---------------------------------------------------------- linear backward
 // For out = inp W^T + b (inp [N,C], W [OC,C]) and dout [N,OC]:
-//   dinp = dout W          : the NT GEMM of dout against W^T [C, OC]
-//   dW   = dout^T inp      : the NT GEMM of dout^T [OC, Np] against inp^T [C, Np]
-//   db   = column sums of dout (partials from the dout transpose)
-// The MFMA GEMM wants both operands K-contiguous, so the operands whose
-// contraction index is their row index are transposed first (tiled, 16-byte
-// traffic both ways); the token dimension is zero-padded to Np, a multiple of
-// 64, so the K loop of the pipelined GEMM has no tail.
+//   dinp = dout W          : contraction over OC, for which W [OC][C] is k-major
+//   dW   = dout^T inp      : contraction over the N tokens, for which dout and
+//                            inp are both k-major
+//   db   = column sums of dout
+// When the contraction is a whole number of k-tiles (fp32 32, bf16 64) the
+// GEMM reads the k-major operands in place (fp32: scalar LDS gathers; bf16:
+// transposing LDS reads). Otherwise the operands whose contraction index is
+// their row index are transposed first (tiled, 16-byte traffic both ways),
+// the token dimension zero-padded to Np, a multiple of 64, so the K loop of
+// the pipelined GEMM has no tail; the bias partials then come from the dout
+// transpose.
 static int64_t round64(int64_t n) { return (n + 63) / 64 * 64; }
 
 // Split-k count for the weight gradient: its OC x C output (fp32 in 128x96
@@ -368,18 +381,24 @@ static int dw_splits(int N, int C, int OC, int dtype) {
     return s;
 }
 
-// The same rule for the k-major fp32 path, whose k-range is the N tokens
-// themselves (N % 32 == 0): slices of N/S rows, each a multiple of 32.
-static int dw_splits_kmajor(int N, int C, int OC) {
-    const int64_t tiles = (int64_t)((OC + 127) / 128) * ((C + 95) / 96);
+// The k-major paths, whose k-range is the N tokens themselves: slices of N/S
+// rows, each a whole number of k-tiles. fp32 (N % 32 == 0, 128x96 tiles): the
+// rule above. bf16 (N % 64 == 0, 128x128 tiles, two workgroups per CU):
+// slices until there are >= 384 workgroups, each slice >= 512 tokens deep
+// (GPT-2 small at 8192 tokens: fc and fcproj 4 slices, qkv 4, attproj 8).
+static int dw_splits_kmajor(int N, int C, int OC, int dtype) {
+    const bool f32 = dtype == GPT2_F32;
+    const int kt = f32 ? 32 : 64, target = f32 ? 512 : 384, depth = f32 ? 256 : 512;
+    const int64_t tiles = (int64_t)((OC + 127) / 128) * ((C + (f32 ? 95 : 127)) / (f32 ? 96 : 128));
     int s = 1;
-    while (s < 8 && tiles * s < 512 && N % (2 * s) == 0 && (N / (2 * s)) % 32 == 0 && N / (2 * s) >= 256) s *= 2;
+    while (s < 8 && tiles * s < target && N % (2 * s) == 0 && (N / (2 * s)) % kt == 0 && N / (2 * s) >= depth)
+        s *= 2;
     return s;
 }
 
 int64_t matmul_backward_workspace_bytes(int N, int C, int OC, int dtype) {
     const int64_t es = elem_size(dtype), Np = round64(N);
-    const int S = std::max(dw_splits(N, C, OC, dtype), dtype == GPT2_F32 ? dw_splits_kmajor(N, C, OC) : 1);
+    const int S = std::max(dw_splits(N, C, OC, dtype), dw_splits_kmajor(N, C, OC, dtype));
     return align256((int64_t)C * OC * es) + align256((int64_t)OC * Np * es) + align256((int64_t)C * Np * es) +
            align256(Np / 64 * OC * 4) + (S > 1 ? align256((int64_t)S * OC * C * 4) : 0);
 }
@@ -399,23 +418,40 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
     p += align256(Np / 64 * OC * 4);
     float* wpart = (float*)p;  // split-k partials of dweight
     int rc = GPT2_OK;
-    if constexpr (std::is_same<T, float>::value) {
-        // k-major operands read in place: dinp = dout . W with W as stored
-        // ([OC][C] is k-major for this product), dW = dout^T . inp with both as
-        // stored; the bias from a two-stage column sum of dout
-        const bool km_dinp = OC % 32 == 0, km_dw = N % 32 == 0;
+    {
+        // k-major operands read in place when the contraction is a whole
+        // number of k-tiles (fp32 32, bf16 64): dinp = dout . W with W as
+        // stored ([OC][C] is k-major for this product; fp32 only: in bf16 the
+        // transpose of W is small and the row-major tile shapes chosen per
+        // problem are faster), dW = dout^T . inp with both as stored; the bias
+        // from a two-stage column sum of dout
+        constexpr bool f32 = std::is_same<T, float>::value;
+        constexpr int kt = f32 ? 32 : 64;
+        const bool km_dinp = f32 && OC % kt == 0, km_dw = N % kt == 0;
         if (dinp && km_dinp) {
             rc = launch_matmul_kmajor(dinp, dout, weight, N, C, OC, OC, C, false, true, 1, s);
             if (rc) return rc;
         }
         if (dweight && km_dw) {
-            const int Sk = dw_splits_kmajor(N, C, OC);
-            rc = launch_matmul_kmajor(Sk > 1 ? wpart : dweight, dout, inp, OC, C, N / Sk, OC, C, true, true, Sk, s);
+            const int Sk = dw_splits_kmajor(N, C, OC, dtype);
+            // bf16 in slices: the bias partials come from the product's own
+            // reads of dout (per slice, into bpart: Sk <= 8 <= N/64 rows) and
+            // are summed with the weight slices
+            T* db_fused = !f32 && Sk > 1 ? dbias : nullptr;
+            if constexpr (f32)
+                rc = launch_matmul_kmajor(Sk > 1 ? wpart : dweight, dout, inp, OC, C, N / Sk, OC, C, true, true, Sk, s);
+            else if (Sk > 1)
+                rc = launch_matmul_kmajor(wpart, dout, inp, OC, C, N / Sk, OC, C, true, true, Sk,
+                                          db_fused ? bpart : nullptr, s);
+            else
+                rc = launch_matmul_kmajor(dweight, dout, inp, OC, C, N, OC, C, true, true, 1, s);
             if (rc) return rc;
             if (Sk > 1) {
                 const int64_t n = (int64_t)OC * C;
-                splitsum_kernel<T><<<stream_grid_bwd(n / 4), 256, 0, s>>>(dweight, wpart, Sk, n);
+                splitsum_kernel<T><<<stream_grid_bwd((n + OC) / 4), 256, 0, s>>>(dweight, wpart, Sk, n, db_fused,
+                                                                                 bpart, OC);
             }
+            if (db_fused) dbias = nullptr;  // done
         }
         if (dbias && km_dw) {
             const int R = (N + 255) / 256;
@@ -426,6 +462,8 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
         if (km_dw) dweight = dbias = nullptr;
         if (!dinp && !dweight && !dbias) return launch_status();
     }
+    // otherwise (a ragged contraction) the transposed operands, token range
+    // zero-padded to Np
     const int S = dw_splits(N, C, OC, dtype);
     if (dinp) {
         launch_transpose<T>(wt, nullptr, weight, OC, C, OC, s);  // W^T [C, OC]
@@ -439,7 +477,7 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
             rc = launch_matmul_splitk_part(wpart, doutT, inpT, OC, C, (int)(Np / S), (int)Np, S, s);
             if (rc) return rc;
             const int64_t n = (int64_t)OC * C;
-            splitsum_kernel<T><<<stream_grid_bwd(n / 4), 256, 0, s>>>(dweight, wpart, S, n);
+            splitsum_kernel<T><<<stream_grid_bwd(n / 4), 256, 0, s>>>(dweight, wpart, S, n, nullptr, nullptr, 0);
         } else {
             rc = launch_matmul(dweight, doutT, inpT, nullptr, OC, (int)Np, C, dtype, s);
             if (rc) return rc;

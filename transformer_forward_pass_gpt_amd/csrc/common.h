@@ -145,7 +145,13 @@ void set_last_hip_error(int e);
 // row and per group of kStatCols columns, the max m and the sum of
 // e^{y - m} over the group's columns below a limit V (row statistics for a
 // one-pass softmax).
-enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_STATS = 3 };
+// EPI_ASUM (weight gradients, bf16 A stored k-major, no bias): the stored
+// product plus the sum of A(k, m) over the launch's k-range for every m, i.e.
+// the column sums of the stored A rows (the bias gradient of a linear layer
+// is the column sum of its output gradient, which is this A), taken from the
+// fragments the product already reads, written as fp32 to stats[slice * M + m]
+// by the workgroups of output tile column 0.
+enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_STATS = 3, EPI_ASUM = 4 };
 constexpr int kStatCols = 128;
 // Status after a launch: GPT2_OK, or GPT2_ERR_HIP with the code recorded.
 int launch_status();

@@ -225,12 +225,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __re
 // unused).
 // TO: the output type; fp32 products of bf16 operands (split-k partial sums
 // that a later fp32 sum reduces) take the plain epilogue only.
-// TA / TB (fp32): the operand is stored k-major, A as [K][M] (row stride
-// lda), W as [K][N] (row stride ldb): out = A^T-stored . W^T-stored without a
-// transpose pass. Its tile is copied as BK rows of BM (BN) elements and a
-// lane gathers its 4 k-steps with 4 scalar LDS reads; the two lane halves of
-// one read take k-rows 4 apart (k = 8kc + 4h + e), so k-rows with bit 2 set
-// are rotated by 8 chunks (32 banks) and the two halves use disjoint banks.
+// TA / TB: the operand is stored k-major, A as [K][M] (row stride lda), W as
+// [K][N] (row stride ldb): out = A^T-stored . W^T-stored without a transpose
+// pass. Its tile is copied as BK rows of BM (BN) elements.
+//  - fp32: a lane gathers its 4 k-steps with 4 scalar LDS reads; the two lane
+//    halves of one read take k-rows 4 apart (k = 8kc + 4h + e), so k-rows
+//    with bit 2 set are rotated by 8 chunks (32 banks) and the two halves use
+//    disjoint banks.
+//  - bf16: transposing reads (ds_read_b64_tr_b16). In each 16-lane group,
+//    lane 4j+q addresses k-row j and 4 columns; lane i receives column i of
+//    the 4 k-rows. Read r of k-step kc addresses k-rows 16kc + 8h + 4r + j,
+//    so a lane gets k = 16kc + 8h + 0..7 of its column, the same k order as
+//    a row-major fragment (the two operand forms mix). Chunk c of k-row k is
+//    stored in slot c ^ 4(k % 4): the 4 k-rows one lane half reads land in 4
+//    different 64-byte bank quarters (BM, BN multiples of 128).
 template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE = 0, bool DIRECT = false,
           int EPI = EPI_BIAS, bool SPLITK = false, bool TA = false, bool TB = false, typename TO = T>
 __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, const T* __restrict__ A,
@@ -252,14 +260,16 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
     constexpr int LA = BM * CH / 64 / NW, LB = BN * CH / 64 / NW;  // copies per wave per tile
     static_assert(LA * 64 * NW == BM * CH && LB * 64 * NW == BN * CH, "tile/wave mismatch");
     constexpr int LPW = LA + LB;
-    static_assert(!(TA || TB) || std::is_same<T, float>::value, "k-major operands: fp32 only");
+    constexpr bool KBF = std::is_same<T, bf16>::value;  // k-major bf16: transposing reads
     constexpr int CMA = BM * (int)sizeof(T) / 16, CMB = BN * (int)sizeof(T) / 16;  // chunks per k-row
     constexpr int ROTA = 8, ROTB = 8;
     static_assert(!(TA || TB) || (CMA >= 16 && CMB >= 16), "k-major tiles need >= 16 chunks per k-row");
+    static_assert(!KBF || ((!TA || CMA % 16 == 0) && (!TB || CMB % 16 == 0)), "bf16 k-major: BM, BN % 128 == 0");
     static_assert(LPW * (S - 2) < 64, "vmcnt range");
     constexpr int STAGE = (BM + BN) * BK;  // elements per stage (A tile then W tile)
     constexpr int VO = Vec<TO>::N;          // output elements per 16-byte vector
-    static_assert(std::is_same<TO, T>::value || (EPI == EPI_BIAS && !TA && !TB), "wider output: plain products only");
+    static_assert(std::is_same<TO, T>::value || EPI == EPI_BIAS || EPI == EPI_ASUM, "wider output: plain products only");
+    static_assert(EPI != EPI_ASUM || (TA && KBF), "A sums: bf16 k-major A only");
     constexpr int LDO = BN + VO;           // row stride of the output tile in the epilogue
     // stage the output tile through LDS when it fits in 160 KiB
     constexpr bool STAGED = !DIRECT && BM * LDO * (int)sizeof(TO) <= 160 * 1024;
@@ -298,7 +308,8 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
     for (int j = 0; j < LA; j++) {
         const int q = (wid * LA + j) * 64 + lane;
         if constexpr (TA) {
-            const int row = q / CMA, c = (q % CMA + CMA - ROTA * ((row >> 2) & 1)) % CMA;
+            const int row = q / CMA;
+            const int c = KBF ? (q % CMA) ^ (4 * (row & 3)) : (q % CMA + CMA - ROTA * ((row >> 2) & 1)) % CMA;
             offA[j] = (int64_t)row * lda_ + min(m0 + c * VE, M - VE);
         } else {
             const int row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
@@ -309,7 +320,8 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
     for (int j = 0; j < LB; j++) {
         const int q = (wid * LB + j) * 64 + lane;
         if constexpr (TB) {
-            const int row = q / CMB, c = (q % CMB + CMB - ROTB * ((row >> 2) & 1)) % CMB;
+            const int row = q / CMB;
+            const int c = KBF ? (q % CMB) ^ (4 * (row & 3)) : (q % CMB + CMB - ROTB * ((row >> 2) & 1)) % CMB;
             offB[j] = (int64_t)row * ldb_ + min(n0 + c * VE, N - VE);
         } else {
             const int row = q / CH, lc = (q % CH) ^ ((row / RP) % CH);
@@ -334,27 +346,47 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
 #pragma unroll
         for (int j = 0; j < TN; j++) acc[i][j] = f32x16{};
 
-    // A k-major tile element (k, m) sits at k*BM + slot*VE + m%VE with slot =
-    // (m/VE + ROT*((k>>2)&1)) mod CM. A fragment's step e is k = 8kc + 4h + e
-    // (fp32), whose bit 2 is h: the slot of a lane's column is a per-lane
+    // fp32: a k-major tile element (k, m) sits at k*BM + slot*VE + m%VE with
+    // slot = (m/VE + ROT*((k>>2)&1)) mod CM. A fragment's step e is k = 8kc +
+    // 4h + e, whose bit 2 is h: the slot of a lane's column is a per-lane
     // constant, so every read is that lane offset plus a compile-time one.
+    // bf16: the transposing read's address for k-step 0, read 0: k-row 8h + j
+    // (j = lane/4 % 4), columns c0 + 16(lane/16 % 2) + 4(lane % 4) .. +3 of the
+    // lane's 32-column tile c0; slot (column/8) ^ 4j since k-row % 4 = j.
+    const int tj = (lane >> 2) & 3, tq = lane & 3, tg = (lane >> 4) & 1;
+    auto kcol = [&](int c0, int LD) {
+        return (8 * h + tj) * LD + (((c0 >> 3) + 2 * tg + (tq >> 1)) ^ (4 * tj)) * 8 + 4 * (tq & 1);
+    };
     int colA[TM], colB[TN];
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const int m = wm * TM * 32 + i * 32 + r32;
-        colA[i] = TA ? 4 * h * BM + ((m / VE + ROTA * h) % CMA) * VE + m % VE : 0;
+        colA[i] = !TA ? 0 : KBF ? kcol(wm * TM * 32 + i * 32, BM) : 4 * h * BM + ((m / VE + ROTA * h) % CMA) * VE + m % VE;
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
         const int n = wn * TN * 32 + j * 32 + r32;
-        colB[j] = TB ? 4 * h * BN + ((n / VE + ROTB * h) % CMB) * VE + n % VE : 0;
+        colB[j] = !TB ? 0 : KBF ? kcol(wn * TN * 32 + j * 32, BN) : 4 * h * BN + ((n / VE + ROTB * h) % CMB) * VE + n % VE;
     }
+    // bf16 k-step kc of a k-major tile with LD columns: the two transposing
+    // reads of k-rows 16kc + 8h + j and 16kc + 8h + 4 + j
+    auto tr_frag = [&](const T* t, int col, int kc, int LD) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+        const lds_v4s_ptr p = (lds_v4s_ptr)t;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p + (col + 16 * kc * LD) / 4);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p + (col + (16 * kc + 4) * LD) / 4);
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
     auto load_frags = [&](const T* sA, const T* sB, int kc, u32x4 (&fa)[TM], u32x4 (&fb)[TN]) {
 #pragma unroll
         for (int i = 0; i < TM; i++) {
             const int row = wm * TM * 32 + i * 32 + r32;
-            if constexpr (TA) {
-                // fp32 only (static_assert above): element index = 32-bit word index
+            if constexpr (TA && KBF) {
+                fa[i] = tr_frag(sA, colA[i], kc, BM);
+            } else if constexpr (TA) {
+                // fp32: element index = 32-bit word index
                 const uint32_t* w = reinterpret_cast<const uint32_t*>(sA) + colA[i] + 8 * kc * BM;
 #pragma unroll
                 for (int e = 0; e < VE; e++) fa[i][e] = w[e * BM];
@@ -365,7 +397,9 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int row = wn * TN * 32 + j * 32 + r32;
-            if constexpr (TB) {
+            if constexpr (TB && KBF) {
+                fb[j] = tr_frag(sB, colB[j], kc, BN);
+            } else if constexpr (TB) {
                 const uint32_t* w = reinterpret_cast<const uint32_t*>(sB) + colB[j] + 8 * kc * BN;
 #pragma unroll
                 for (int e = 0; e < VE; e++) fb[j][e] = w[e * BN];
@@ -374,6 +408,13 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
             }
         }
     };
+    // EPI_ASUM: the waves of tile column 0 with wn == 0 (each A row once) add
+    // up their A fragments: lane (h, r32) sums k = 16kc + 8h .. +7 of row r32
+    // of each of its TM row tiles; the two halves are combined at the end.
+    float asum[TM];
+#pragma unroll
+    for (int i = 0; i < TM; i++) asum[i] = 0.f;
+    const bool asum_on = EPI == EPI_ASUM && n0 == 0 && wn == 0;
     auto compute = [&](const int stage) {
         const T* sA = smem + stage * STAGE;
         const T* sB = sA + BM * BK;
@@ -393,6 +434,18 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
 #pragma unroll
                     for (int j = 0; j < TN; j++)
                         Mfma32<T>::step(acc[i][j], fa[kc & 1][i], fb[kc & 1][j], e);
+            if constexpr (EPI == EPI_ASUM) {
+                if (asum_on) {
+#pragma unroll
+                    for (int i = 0; i < TM; i++) {
+                        float t = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            t += __uint_as_float(fa[kc & 1][i][e] << 16) + __uint_as_float(fa[kc & 1][i][e] & 0xffff0000u);
+                        asum[i] += t;
+                    }
+                }
+            }
         }
     };
 
@@ -440,6 +493,18 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
     if constexpr (S > 3) { if (kt + 2 < nk) step(I2{}, kt + 2); }
     if constexpr (S > 4) { if (kt + 3 < nk) step(I3{}, kt + 3); }
     if constexpr (S > 5) { if (kt + 4 < nk) step(I4{}, kt + 4); }
+
+    if constexpr (EPI == EPI_ASUM) {
+        if (asum_on) {
+            float* dst = stats + (SPLITK ? (int64_t)blockIdx.y * M : 0);
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const float v = asum[i] + __shfl_xor(asum[i], 32, 64);
+                const int m = m0 + wm * TM * 32 + i * 32 + r32;
+                if (h == 0 && m < M) dst[m] = v;
+            }
+        }
+    }
 
     // Epilogue through LDS: every copy has landed (the last step waited for
     // vmcnt 0); once all waves are past this barrier the stage memory is
@@ -606,19 +671,21 @@ static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int 
 #undef GEMM_PIPE_LAUNCH
 }
 
-// k-major operand variants (fp32): out [M,N] (+ y*split_out per k-slice y of
-// depth K) from A ([K][M] rows lda apart if TA, else [M][K]) and W ([K][N]
-// rows ldb apart if TB, else [N][K]); bias only without split.
-template <int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE, bool TA, bool TB>
-static void launch_gemm_kmajor(float* out, const float* A, const float* W, const float* bias, int M, int N, int K,
-                               int lda, int ldb, int splits, int64_t split_out, int group_m, int remap,
-                               hipStream_t s) {
+// k-major operand variants: out [M,N] (+ y*split_out per k-slice y of depth
+// K) from A ([K][M] rows lda apart if TA, else [M][K]) and W ([K][N] rows ldb
+// apart if TB, else [N][K]); bias only without split. TO: the output type.
+template <int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE, bool TA, bool TB, typename T,
+          typename TO, int EPI = EPI_BIAS>
+static void launch_gemm_kmajor(TO* out, const T* A, const T* W, const typename std::enable_if<true, T>::type* bias,
+                               int M, int N, int K, int lda, int ldb,
+                               int splits, int64_t split_out, int group_m, int remap, hipStream_t s,
+                               float* stats = nullptr) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(nwg, splits);
-    gemm_pipe_kernel<float, WM, WN, TM, TN, RB, S, SCHED, WPE, false, EPI_BIAS, true, TA, TB>
-        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, static_cast<const float*>(nullptr), M, N, K, group_m, remap,
-                                       lda, ldb, split_out, nullptr, 0);
+    gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, false, EPI, true, TA, TB, TO>
+        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, static_cast<const TO*>(nullptr), M, N, K, group_m, remap,
+                                       lda, ldb, split_out, stats, 0);
 }
 
 template <typename T, int WM, int WN, int TM, int TN, int SCHED = 4>

@@ -225,6 +225,43 @@ int launch_matmul_kmajor(float* out, const float* A, const float* W, int M, int 
     return launch_status();
 }
 
+// bf16 weight-gradient products, both operands k-major (no transpose pass),
+// fp32 accumulation: slice y of `splits` (k-range y*K .. y*K+K-1) gives
+// part + y*M*N (fp32 partial sums); the bf16 overload writes out [M,N] in one
+// slice. A stored [K][M] (rows lda apart), W stored [K][N] (rows ldb apart),
+// out = A^T W. asum (nullable, partial-sum form only): asum[y*M + m] = the
+// sum of A(k, m) over slice y's k-range (fp32), taken from the fragments the
+// product reads. K (per slice) % 64 == 0, M % 8 == 0, N % 8 == 0. 128x128
+// tiles, two stages in 64 KiB, so two workgroups share a CU (on MI355X this
+// beat 3- and 4-stage single-resident and 128x256 / 256x128 tiles on every
+// GPT-2 weight-gradient shape swept, with the split counts of the caller).
+template <typename TO>
+static int launch_kmajor_bf16(TO* out, const bf16* A, const bf16* W, int M, int N, int K, int lda, int ldb, bool ta,
+                              bool tb, int splits, float* asum, hipStream_t s) {
+    if (!ta || !tb || K % 64 || K <= 0 || splits < 1 || M % 8 || N % 8) return GPT2_ERR_INVALID_ARGUMENT;
+    if constexpr (std::is_same<TO, float>::value) {
+        if (asum) {
+            launch_gemm_kmajor<2, 2, 2, 2, 128, 2, 2, 0, true, true, bf16, TO, EPI_ASUM>(
+                out, A, W, nullptr, M, N, K, lda, ldb, splits, (int64_t)M * N, 8, 1, s, asum);
+            return launch_status();
+        }
+    }
+    launch_gemm_kmajor<2, 2, 2, 2, 128, 2, 2, 0, true, true>(out, A, W, nullptr, M, N, K, lda, ldb, splits,
+                                                            (int64_t)M * N, 8, 1, s);
+    return launch_status();
+}
+
+int launch_matmul_kmajor(float* part, const bf16* A, const bf16* W, int M, int N, int K, int lda, int ldb, bool ta,
+                         bool tb, int splits, float* asum, hipStream_t s) {
+    return launch_kmajor_bf16(part, A, W, M, N, K, lda, ldb, ta, tb, splits, asum, s);
+}
+
+int launch_matmul_kmajor(bf16* out, const bf16* A, const bf16* W, int M, int N, int K, int lda, int ldb, bool ta,
+                         bool tb, int splits, hipStream_t s) {
+    if (splits != 1) return GPT2_ERR_INVALID_ARGUMENT;
+    return launch_kmajor_bf16(out, A, W, M, N, K, lda, ldb, ta, tb, 1, static_cast<float*>(nullptr), s);
+}
+
 // Decode-step GEMM on at most 32 rows (K % 8 == 0). part == nullptr:
 // out = epi(inp W^T + bias) in one split; otherwise fp32 partial sums over
 // `splits` k-ranges into part[splits][M][N], bias and epilogue left to the
