@@ -19,7 +19,10 @@ namespace gpt2 {
 int launch_matmul(void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
 int launch_matmul_splitk_part(float*, const float*, const float*, int, int, int, int, int, hipStream_t);
 int launch_matmul_splitk_part(float*, const bf16*, const bf16*, int, int, int, int, int, hipStream_t);
-int launch_matmul_kmajor(float*, const float*, const float*, int, int, int, int, int, bool, bool, int, hipStream_t);
+int launch_matmul_epi(void*, const void*, const void*, const void*, const void*, int, int, int, int, int,
+                      hipStream_t);
+int launch_matmul_kmajor(float*, const float*, const float*, int, int, int, int, int, bool, bool, int, hipStream_t,
+                         const float* = nullptr);
 int launch_matmul_kmajor(float*, const bf16*, const bf16*, int, int, int, int, int, bool, bool, int, float*,
                          hipStream_t);
 int launch_matmul_kmajor(bf16*, const bf16*, const bf16*, int, int, int, int, int, bool, bool, int, hipStream_t);
@@ -36,20 +39,6 @@ static unsigned stream_grid_bwd(int64_t nvec) {
 static inline int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
 
 // ------------------------------------------------------------ GELU backward
-// d/dx [x s(2u)] with s the logistic function, u = sqrt(2/pi)(x + 0.044715 x^3)
-// (s(2u) = (1 + tanh u)/2, the forward's form):
-//   g'(x) = s + x s (1 - s) 2u',  u' = sqrt(2/pi)(1 + 3 * 0.044715 x^2),
-// with 1 - s = e s for e = e^{-2u}, so nothing cancels as s -> 1. u is
-// clamped at -40 so e stays finite (g' is below 1e-30 there either way).
-__device__ __forceinline__ float gelu_tanh_grad(float x) {
-    const float k = 0.7978845608028654f;  // sqrt(2/pi)
-    const float x2 = x * x;
-    const float u = fmaxf(k * x * (1.0f + 0.044715f * x2), -40.0f);
-    const float e = __expf(-2.0f * u);
-    const float sg = __builtin_amdgcn_rcpf(1.0f + e);
-    return sg + x * (sg * sg * e) * (2.0f * k) * (1.0f + 3.0f * 0.044715f * x2);
-}
-
 // dinp = dout * g'(inp); dinp may be dout (each element is read, then written
 // by the same thread).
 template <typename T>
@@ -405,7 +394,7 @@ int64_t matmul_backward_workspace_bytes(int N, int C, int OC, int dtype) {
 
 template <typename T>
 static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, const T* inp, const T* weight, int N,
-                               int C, int OC, int dtype, void* ws, hipStream_t s) {
+                               int C, int OC, int dtype, void* ws, hipStream_t s, const T* gelu_in) {
     const int64_t es = sizeof(T), Np = round64(N);
     char* p = (char*)ws;
     T* wt = (T*)p;
@@ -429,7 +418,8 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
         constexpr int kt = f32 ? 32 : 64;
         const bool km_dinp = f32 && OC % kt == 0, km_dw = N % kt == 0;
         if (dinp && km_dinp) {
-            rc = launch_matmul_kmajor(dinp, dout, weight, N, C, OC, OC, C, false, true, 1, s);
+            if constexpr (f32)
+                rc = launch_matmul_kmajor(dinp, dout, weight, N, C, OC, OC, C, false, true, 1, s, gelu_in);
             if (rc) return rc;
         }
         if (dweight && km_dw) {
@@ -467,7 +457,7 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
     const int S = dw_splits(N, C, OC, dtype);
     if (dinp) {
         launch_transpose<T>(wt, nullptr, weight, OC, C, OC, s);  // W^T [C, OC]
-        rc = launch_matmul(dinp, dout, wt, nullptr, N, OC, C, dtype, s);
+        rc = launch_matmul_epi(dinp, dout, wt, nullptr, gelu_in, N, OC, C, gelu_in ? EPI_DGELU : EPI_BIAS, dtype, s);
         if (rc) return rc;
     }
     if (dweight || dbias) launch_transpose<T>(doutT, dbias ? bpart : nullptr, dout, N, OC, (int)Np, s);
@@ -487,13 +477,19 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
     return launch_status();
 }
 
+// gelu_in (nullable, [N, C]): the input gradient comes out already through the
+// backward of the GELU whose output was `inp` (dinp = (dout W) o g'(gelu_in),
+// each factor rounded as the separate GELU backward rounds it).
 int launch_matmul_backward(void* dinp, void* dweight, void* dbias, const void* dout, const void* inp,
-                           const void* weight, int N, int C, int OC, int dtype, void* ws, hipStream_t s) {
+                           const void* weight, int N, int C, int OC, int dtype, void* ws, hipStream_t s,
+                           const void* gelu_in) {
     if (dtype == GPT2_BF16)
         return launch_matmul_bwd_t<bf16>((bf16*)dinp, (bf16*)dweight, (bf16*)dbias, (const bf16*)dout,
-                                         (const bf16*)inp, (const bf16*)weight, N, C, OC, dtype, ws, s);
+                                         (const bf16*)inp, (const bf16*)weight, N, C, OC, dtype, ws, s,
+                                         (const bf16*)gelu_in);
     return launch_matmul_bwd_t<float>((float*)dinp, (float*)dweight, (float*)dbias, (const float*)dout,
-                                      (const float*)inp, (const float*)weight, N, C, OC, dtype, ws, s);
+                                      (const float*)inp, (const float*)weight, N, C, OC, dtype, ws, s,
+                                      (const float*)gelu_in);
 }
 
 // --------------------------------------------------------- encoder backward
@@ -689,7 +685,7 @@ extern "C" int matmul_backward(void* dinp, void* dweight, void* dbias, const voi
     if (dinp && (dinp == dout || dinp == inp || dinp == weight)) return GPT2_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < matmul_backward_workspace_bytes(N, C, OC, dtype)) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     return launch_matmul_backward(dinp, dweight, dbias, dout, inp, weight, N, C, OC, dtype, workspace,
-                                  (hipStream_t)stream);
+                                  (hipStream_t)stream, nullptr);
 }
 
 extern "C" int encoder_backward(void* dwte, void* dwpe, const void* dout, const int32_t* tokens, int B, int T, int C,

@@ -93,6 +93,20 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + __expf(k2 * u));
 }
 
+// d/dx [x s(2u)] with s the logistic function, u = sqrt(2/pi)(x + 0.044715 x^3)
+// (s(2u) = (1 + tanh u)/2, the forward's form):
+//   g'(x) = s + x s (1 - s) 2u',  u' = sqrt(2/pi)(1 + 3 * 0.044715 x^2),
+// with 1 - s = e s for e = e^{-2u}, so nothing cancels as s -> 1. u is
+// clamped at -40 so e stays finite (g' is below 1e-30 there either way).
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+    const float k = 0.7978845608028654f;  // sqrt(2/pi)
+    const float x2 = x * x;
+    const float u = fmaxf(k * x * (1.0f + 0.044715f * x2), -40.0f);
+    const float e = __expf(-2.0f * u);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+    return sg + x * (sg * sg * e) * (2.0f * k) * (1.0f + 3.0f * 0.044715f * x2);
+}
+
 // Reductions across the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -151,7 +165,11 @@ void set_last_hip_error(int e);
 // is the column sum of its output gradient, which is this A), taken from the
 // fragments the product already reads, written as fp32 to stats[slice * M + m]
 // by the workgroups of output tile column 0.
-enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_STATS = 3, EPI_ASUM = 4 };
+// EPI_DGELU (the backward of a GELU whose output fed the forward product):
+// y = acc + bias rounded to the output type, times g'(x) for x = res[row][col]
+// (the GELU's input), rounded again: what a separate GELU backward computes
+// from the stored product.
+enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_STATS = 3, EPI_ASUM = 4, EPI_DGELU = 5 };
 constexpr int kStatCols = 128;
 // Status after a launch: GPT2_OK, or GPT2_ERR_HIP with the code recorded.
 int launch_status();

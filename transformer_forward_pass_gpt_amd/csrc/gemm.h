@@ -174,12 +174,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __re
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                // residual read with the row clamped, outside the bounds branch
-                const float r = EPI == EPI_BIAS_RESIDUAL ? load_scalar(res + (int64_t)min(row, M - 1) * N + col) : 0.f;
+                // residual (GELU input) read with the row clamped, outside the bounds branch
+                const float r = EPI == EPI_BIAS_RESIDUAL || EPI == EPI_DGELU
+                                    ? load_scalar(res + (int64_t)min(row, M - 1) * N + col)
+                                    : 0.f;
                 if (row < M) {
                     float y = acc[i][j][v] + bv;
                     if constexpr (EPI == EPI_BIAS_GELU) y = gelu_tanh(storage_round(out, y));
                     if constexpr (EPI == EPI_BIAS_RESIDUAL) y = storage_round(out, y) + r;
+                    if constexpr (EPI == EPI_DGELU) y = storage_round(out, y) * gelu_tanh_grad(r);
                     store_scalar(out + (int64_t)row * N + col, y);
                 }
             }
@@ -217,8 +220,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __re
 // store the output straight from the accumulators (no LDS staging), which
 // keeps the LDS footprint at the stages alone.
 // EPI: the epilogue (common.h); res [M,N] is the residual of
-// EPI_BIAS_RESIDUAL and may be `out` itself (each element is read and then
-// written by the same thread).
+// EPI_BIAS_RESIDUAL or the GELU input of EPI_DGELU and may be `out` itself
+// (each element is read and then written by the same thread).
 // SPLITK: workgroup row blockIdx.y multiplies the k-range [y*K, (y+1)*K) and
 // writes its product to out + y*split_out; A and W rows are then lda and ldb
 // elements long (without SPLITK they are K long and lda, ldb, split_out are
@@ -533,10 +536,10 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
         __builtin_amdgcn_s_waitcnt((0xF) | (7 << 4) | (0x0 << 8) | (3 << 14));  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         constexpr int CPR = BN / VO;  // 16-byte chunks per tile row
-        if constexpr (EPI == EPI_BIAS_RESIDUAL) {
-            // every residual chunk of this thread is loaded before the first
-            // add (rows and columns clamped into the matrix; out-of-range
-            // chunks are then not stored), so the loads overlap
+        if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_DGELU) {
+            // every residual (GELU input) chunk of this thread is loaded
+            // before the first use (rows and columns clamped into the matrix;
+            // out-of-range chunks are then not stored), so the loads overlap
             constexpr int NCH = (BM * CPR + NW * 64 - 1) / (NW * 64);
             u32x4 rv[NCH];
 #pragma unroll
@@ -555,7 +558,10 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
                     unpack_vec<TO>(*reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VO]), a);
                     unpack_vec<TO>(rv[j], r);
 #pragma unroll
-                    for (int e = 0; e < VO; e++) a[e] += r[e];
+                    for (int e = 0; e < VO; e++) {
+                        if constexpr (EPI == EPI_DGELU) a[e] *= gelu_tanh_grad(r[e]);
+                        else a[e] += r[e];
+                    }
                     store_vec(out + (int64_t)row * N + col, a);
                 }
             }
@@ -628,12 +634,14 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    const float r =
-                        EPI == EPI_BIAS_RESIDUAL ? load_scalar(res + (int64_t)min(row, M - 1) * N + col) : 0.f;
+                    const float r = EPI == EPI_BIAS_RESIDUAL || EPI == EPI_DGELU
+                                        ? load_scalar(res + (int64_t)min(row, M - 1) * N + col)
+                                        : 0.f;
                     if (row < M) {
                         float y = acc[i][j][v] + bv;
                         if constexpr (EPI == EPI_BIAS_GELU) y = gelu_tanh(storage_round(out, y));
                         if constexpr (EPI == EPI_BIAS_RESIDUAL) y = storage_round(out, y) + r;
+                        if constexpr (EPI == EPI_DGELU) y = storage_round(out, y) * gelu_tanh_grad(r);
                         store_scalar(out + (int64_t)row * N + col, y);
                     }
                 }
@@ -667,6 +675,7 @@ static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int 
     }
     if (epi == EPI_BIAS_GELU) GEMM_PIPE_LAUNCH(EPI_BIAS_GELU);
     else if (epi == EPI_BIAS_RESIDUAL) GEMM_PIPE_LAUNCH(EPI_BIAS_RESIDUAL);
+    else if (epi == EPI_DGELU) GEMM_PIPE_LAUNCH(EPI_DGELU);
     else GEMM_PIPE_LAUNCH(EPI_BIAS);
 #undef GEMM_PIPE_LAUNCH
 }
@@ -679,13 +688,13 @@ template <int WM, int WN, int TM, int TN, int RB, int S, int SCHED, int WPE, boo
 static void launch_gemm_kmajor(TO* out, const T* A, const T* W, const typename std::enable_if<true, T>::type* bias,
                                int M, int N, int K, int lda, int ldb,
                                int splits, int64_t split_out, int group_m, int remap, hipStream_t s,
-                               float* stats = nullptr) {
+                               float* stats = nullptr, const TO* res = nullptr) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(nwg, splits);
     gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, false, EPI, true, TA, TB, TO>
-        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, static_cast<const TO*>(nullptr), M, N, K, group_m, remap,
-                                       lda, ldb, split_out, stats, 0);
+        <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap, lda, ldb, split_out, stats,
+                                       0);
 }
 
 template <typename T, int WM, int WN, int TM, int TN, int SCHED = 4>
@@ -703,6 +712,7 @@ static void launch_gemm_cfg(T* out, const T* A, const T* W, const T* bias, int M
     gemm_kernel<T, WM, WN, TM, TN, BK, ILV, E><<<nwg, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap)
     if (epi == EPI_BIAS_GELU) GEMM_CFG_LAUNCH(EPI_BIAS_GELU);
     else if (epi == EPI_BIAS_RESIDUAL) GEMM_CFG_LAUNCH(EPI_BIAS_RESIDUAL);
+    else if (epi == EPI_DGELU) GEMM_CFG_LAUNCH(EPI_DGELU);
     else GEMM_CFG_LAUNCH(EPI_BIAS);
 #undef GEMM_CFG_LAUNCH
 }
@@ -860,6 +870,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_lds_kernel(T* out, float*
                 if constexpr (EPI == EPI_BIAS_GELU) x = gelu_tanh(storage_round(out, x));
                 if constexpr (EPI == EPI_BIAS_RESIDUAL)
                     x = storage_round(out, x) + load_scalar(res + (int64_t)row * N + col);
+                if constexpr (EPI == EPI_DGELU)
+                    x = storage_round(out, x) * gelu_tanh_grad(load_scalar(res + (int64_t)row * N + col));
                 store_scalar(out + (int64_t)row * N + col, x);
             }
         }

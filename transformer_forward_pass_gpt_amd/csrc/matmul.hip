@@ -19,6 +19,7 @@ static void launch_skinny(T* out, float* part, const T* A, const T* W, const T* 
 #define SKINNY_LAUNCH(E) gemm_skinny_lds_kernel<T, 8, 1, E><<<grid, 512, 0, s>>>(out, part, A, W, bias, res, M, N, K)
     if (epi == EPI_BIAS_GELU) SKINNY_LAUNCH(EPI_BIAS_GELU);
     else if (epi == EPI_BIAS_RESIDUAL) SKINNY_LAUNCH(EPI_BIAS_RESIDUAL);
+    else if (epi == EPI_DGELU) SKINNY_LAUNCH(EPI_DGELU);
     else SKINNY_LAUNCH(EPI_BIAS);
 #undef SKINNY_LAUNCH
 }
@@ -140,7 +141,8 @@ const char* matmul_config_name(int N, int C, int OC, int dtype) {
     return g_cfg_name;
 }
 
-// out = epi(inp W^T + bias [, res]); res may alias out (EPI_BIAS_RESIDUAL).
+// out = epi(inp W^T + bias [, res]); res (the residual of EPI_BIAS_RESIDUAL,
+// the GELU input of EPI_DGELU) may alias out.
 int launch_matmul_epi(void* out, const void* inp, const void* weight, const void* bias, const void* res, int N,
                       int C, int OC, int epi, int dtype, hipStream_t s) {
     if (dtype == GPT2_BF16)
@@ -206,11 +208,18 @@ int launch_matmul_splitk_part(float* part, const bf16* A, const bf16* W, int M, 
 // of `splits` at out + y*M*N) = sum over k of A(k, m) W(k, n), A stored
 // [K][M] (rows lda apart) when ta else [M][K] (lda = K), W stored [K][N]
 // (rows ldb apart) when tb else [N][K]. K (per slice) % 32 == 0; M % 4 == 0
-// when ta, N % 4 == 0 when tb.
+// when ta, N % 4 == 0 when tb. gelu_in (nullable; W k-major alone, one
+// slice): the EPI_DGELU epilogue with that [M,N] GELU input.
 int launch_matmul_kmajor(float* out, const float* A, const float* W, int M, int N, int K, int lda, int ldb, bool ta,
-                         bool tb, int splits, hipStream_t s) {
+                         bool tb, int splits, hipStream_t s, const float* gelu_in) {
     if (K % 32 || splits < 1 || (ta && M % 4) || (tb && N % 4)) return GPT2_ERR_INVALID_ARGUMENT;
     const int64_t so = (int64_t)M * N;
+    if (gelu_in) {
+        if (ta || !tb || splits != 1) return GPT2_ERR_INVALID_ARGUMENT;
+        launch_gemm_kmajor<4, 1, 1, 3, 128, 4, 4, 0, false, true, float, float, EPI_DGELU>(
+            out, A, W, nullptr, M, N, K, lda, ldb, 1, so, 8, 1, s, nullptr, gelu_in);
+        return launch_status();
+    }
     if (ta && tb)
         launch_gemm_kmajor<4, 1, 1, 3, 128, 4, 4, 0, true, true>(out, A, W, nullptr, M, N, K, lda, ldb, splits, so, 8,
                                                                 1, s);

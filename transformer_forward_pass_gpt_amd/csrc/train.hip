@@ -30,12 +30,11 @@ int launch_gelu(void*, const void*, int64_t, int, hipStream_t);
 int launch_crossentropy_backward(void*, float*, float*, const void*, const int32_t*, float, int, int, int, int,
                                  hipStream_t);
 int launch_matmul_backward(void*, void*, void*, const void*, const void*, const void*, int, int, int, int, void*,
-                           hipStream_t);
+                           hipStream_t, const void* gelu_in);
 int64_t matmul_backward_workspace_bytes(int N, int C, int OC, int dtype);
 int launch_layernorm_backward(void*, void*, void*, const void*, const void*, const void*, const void*, const float*,
                               const float*, int, int, int, void*, hipStream_t);
 int64_t layernorm_backward_workspace_bytes(int N, int C);
-int launch_gelu_backward(void*, const void*, const void*, int64_t, int, hipStream_t);
 int launch_attention_backward(void*, const void*, const void*, const void*, const float*, int, int, int, int, int,
                               void*, hipStream_t);
 int64_t attention_backward_workspace_bytes(int B, int T, int NH);
@@ -236,24 +235,25 @@ extern "C" int gpt2_backward(void* grads, const int32_t* tokens, const void* par
     launch_zero(gat(po.wpe), (int64_t)cfg->maxT * C * es, s);
     // classifier: d(lnf out) and the logits' part of d(wte)
     CHECK(launch_matmul_backward(w.dC, gat(po.wte), nullptr, A + al.logits, A + al.lnf, at(po.wte), n, C, cfg->Vp, dt,
-                                 w.step, s));
+                                 w.step, s, nullptr));
     CHECK(launch_layernorm_backward(w.dres, gat(po.lnf_g), gat(po.lnf_b), nullptr, w.dC, A + al.xf, at(po.lnf_g),
                                     (const float*)(A + al.lnf_mean), (const float*)(A + al.lnf_rstd), n, C, dt, w.step,
                                     s));
     for (int l = L - 1; l >= 0; l--) {
         const LayerActs a = layer_acts(A, al, l);
+        // d(fc pre-activation) straight from the product: the GELU backward
+        // is the input gradient's epilogue
         CHECK(launch_matmul_backward(w.d4, gat(po.fp_w + l * 4 * C64 * C64), gat(po.fp_b + l * C64), w.dres, a.fchg,
-                                     at(po.fp_w + l * 4 * C64 * C64), n, 4 * C, C, dt, w.step, s));
-        CHECK(launch_gelu_backward(w.d4, a.fch, w.d4, N * 4 * C64, dt, s));
+                                     at(po.fp_w + l * 4 * C64 * C64), n, 4 * C, C, dt, w.step, s, a.fch));
         CHECK(launch_matmul_backward(w.dC, gat(po.fc_w + l * 4 * C64 * C64), gat(po.fc_b + l * 4 * C64), w.d4, a.ln2,
-                                     at(po.fc_w + l * 4 * C64 * C64), n, C, 4 * C, dt, w.step, s));
+                                     at(po.fc_w + l * 4 * C64 * C64), n, C, 4 * C, dt, w.step, s, nullptr));
         CHECK(launch_layernorm_backward(w.dres, gat(po.ln2_g + l * C64), gat(po.ln2_b + l * C64), w.dres, w.dC, a.res1,
                                         at(po.ln2_g + l * C64), a.ln2_mean, a.ln2_rstd, n, C, dt, w.step, s));
         CHECK(launch_matmul_backward(w.dC, gat(po.ap_w + l * C64 * C64), gat(po.ap_b + l * C64), w.dres, a.att,
-                                     at(po.ap_w + l * C64 * C64), n, C, C, dt, w.step, s));
+                                     at(po.ap_w + l * C64 * C64), n, C, C, dt, w.step, s, nullptr));
         CHECK(launch_attention_backward(w.dqkv, w.dC, a.qkv, a.att, a.lse, B, T, C, cfg->NH, dt, w.step, s));
         CHECK(launch_matmul_backward(w.dC, gat(po.qkv_w + l * 3 * C64 * C64), gat(po.qkv_b + l * 3 * C64), w.dqkv,
-                                     a.ln1, at(po.qkv_w + l * 3 * C64 * C64), n, C, 3 * C, dt, w.step, s));
+                                     a.ln1, at(po.qkv_w + l * 3 * C64 * C64), n, C, 3 * C, dt, w.step, s, nullptr));
         CHECK(launch_layernorm_backward(w.dres, gat(po.ln1_g + l * C64), gat(po.ln1_b + l * C64), w.dres, w.dC, a.x,
                                         at(po.ln1_g + l * C64), a.ln1_mean, a.ln1_rstd, n, C, dt, w.step, s));
     }
