@@ -71,9 +71,10 @@ static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
     // allows, else 128x256 (two per CU) or two-stage 256x256 tiles; every
     // 128-byte-row tile halves the L2 requests of a 64-byte-row one.
     if (N >= 16384) return P256x256_K2;                         // vocabulary projection
-    if (K >= 2048) {  // fcproj: enough tiles for the 256 CUs at GPT-2 small's width
+    if (K >= 2048) {  // fcproj (and the training step's vocabulary input gradient, K = Vp):
+        // enough tiles for the 256 CUs at GPT-2 small's width
         if (M >= 8192) return P128x256_R3;
-        return (K <= 3072 && N <= 768) ? P128x96_S4 : P128x128_R4;
+        return N <= 768 ? P128x96_S4 : P128x128_R4;
     }
     if (N <= 1024) return M >= 8192 ? P128x256_R3 : P128x128_K3;   // attproj
     if (N % 192 == 0) return P128x192_K2;                       // qkv, fc at GPT-2 small widths
