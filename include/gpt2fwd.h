@@ -251,7 +251,7 @@ int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens, int pos,
  * until the process ends; the call itself allocates nothing. Arguments as
  * gpt2_decode_step. Returns GPT2_ERR_WORKSPACE_TOO_SMALL (before any launch)
  * when gpt2_decode_workspace_bytes(cfg, B) exceeds GPT2_DECODE_SCRATCH_BYTES
- * (GPT-2 small needs ~2 MB at B = 32, GPT-2 medium ~2.6 MB). Every call on one
+ * (GPT-2 small needs ~2.8 MB at B = 32, GPT-2 medium ~3.7 MB). Every call on one
  * GPU shares that GPU's array: calls that may overlap on one device (other
  * streams, other host threads) race and must be serialised by the caller. */
 #define GPT2_DECODE_SCRATCH_BYTES (8 << 20)

@@ -821,37 +821,64 @@ int64_t decode_workspace_bytes(int B, int C, int NH, int maxT) {
 }
 
 template <typename T, int HS>
-static void launch_decode_hs(T* out, const T* qkv_new, T* kc, T* vc, int B, int pos, int maxT,
-                             int C, int NH, float* part, hipStream_t s) {
+static int launch_decode_hs(T* out, const T* qkv_new, T* kc, T* vc, int B, int pos, int maxT,
+                            int C, int NH, float* part, hipStream_t s, bool combine) {
     constexpr int CHUNK = decode_chunk<T, HS>();
     static_assert(CHUNK >= kDecMinChunk, "workspace bound");
     const float sl2 = 1.4426950408889634f / sqrtf((float)HS);
     const int nsplit = (pos + 1 + CHUNK - 1) / CHUNK;
     decode_attn_kernel<T, HS><<<dim3(nsplit, B * NH), kDecThreads, 0, s>>>(out, part, qkv_new, kc, vc, pos,
                                                                            maxT, C, NH, sl2);
-    if (nsplit > 1) decode_combine_kernel<T, HS><<<B * NH, HS, 0, s>>>(out, part, nsplit, C, NH);
+    if (nsplit > 1 && combine) decode_combine_kernel<T, HS><<<B * NH, HS, 0, s>>>(out, part, nsplit, C, NH);
+    return nsplit;
 }
 
 template <typename T>
-static void launch_decode_t(T* out, const T* qkv_new, T* kc, T* vc, int B, int pos, int maxT,
-                            int C, int NH, float* part, hipStream_t s) {
+static int launch_decode_t(T* out, const T* qkv_new, T* kc, T* vc, int B, int pos, int maxT,
+                           int C, int NH, float* part, hipStream_t s, bool combine) {
     switch (C / NH) {
-        case 16: launch_decode_hs<T, 16>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s); break;
-        case 32: launch_decode_hs<T, 32>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s); break;
-        case 64: launch_decode_hs<T, 64>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s); break;
-        default: launch_decode_hs<T, 128>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s); break;
+        case 16: return launch_decode_hs<T, 16>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s, combine);
+        case 32: return launch_decode_hs<T, 32>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s, combine);
+        case 64: return launch_decode_hs<T, 64>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s, combine);
+        default: return launch_decode_hs<T, 128>(out, qkv_new, kc, vc, B, pos, maxT, C, NH, part, s, combine);
     }
 }
 
+// Key chunks of a decode attention at position pos (the grid's x extent).
+template <typename T, int HS>
+static int decode_splits_hs(int pos) {
+    constexpr int CHUNK = decode_chunk<T, HS>();
+    return (pos + 1 + CHUNK - 1) / CHUNK;
+}
+template <typename T>
+static int decode_splits_t(int pos, int hs) {
+    switch (hs) {
+        case 16: return decode_splits_hs<T, 16>(pos);
+        case 32: return decode_splits_hs<T, 32>(pos);
+        case 64: return decode_splits_hs<T, 64>(pos);
+        default: return decode_splits_hs<T, 128>(pos);
+    }
+}
+int decode_attention_splits(int pos, int hs, int dtype) {
+    return dtype == GPT2_BF16 ? decode_splits_t<bf16>(pos, hs) : decode_splits_t<float>(pos, hs);
+}
+
+// nsplit_out (nullable): when given, a split attention (more than one chunk
+// of keys) leaves its fp32 partials in `part` for the consumer to merge
+// (launch_skinny_gemm_acomb) instead of launching the combine, and
+// *nsplit_out receives the chunk count (1: `out` was written).
 int launch_attention_decode(void* out, const void* qkv_new, void* kcache, void* vcache, int B,
                             int pos, int maxT, int C, int NH, int dtype, float* part,
-                            hipStream_t s) {
+                            hipStream_t s, int* nsplit_out) {
+    const bool combine = nsplit_out == nullptr;
+    int ns;
     if (dtype == GPT2_BF16)
-        launch_decode_t<bf16>((bf16*)out, (const bf16*)qkv_new, (bf16*)kcache, (bf16*)vcache, B,
-                              pos, maxT, C, NH, part, s);
+        ns = launch_decode_t<bf16>((bf16*)out, (const bf16*)qkv_new, (bf16*)kcache, (bf16*)vcache, B,
+                                   pos, maxT, C, NH, part, s, combine);
     else
-        launch_decode_t<float>((float*)out, (const float*)qkv_new, (float*)kcache, (float*)vcache,
-                               B, pos, maxT, C, NH, part, s);
+        ns = launch_decode_t<float>((float*)out, (const float*)qkv_new, (float*)kcache, (float*)vcache,
+                                    B, pos, maxT, C, NH, part, s, combine);
+    if (nsplit_out) *nsplit_out = ns;
     return launch_status();
 }
 
@@ -898,5 +925,5 @@ extern "C" int attention_decode_forward(void* out, const void* qkv_new, void* kc
         return GPT2_ERR_UNSUPPORTED;
     if (workspace_bytes < decode_workspace_bytes(B, C, NH, maxT)) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     return launch_attention_decode(out, qkv_new, kcache, vcache, B, pos, maxT, C, NH, dtype,
-                                   (float*)workspace, (hipStream_t)stream);
+                                   (float*)workspace, (hipStream_t)stream, nullptr);
 }

@@ -271,7 +271,8 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
     static_assert(LPW * (S - 2) < 64, "vmcnt range");
     constexpr int STAGE = (BM + BN) * BK;  // elements per stage (A tile then W tile)
     constexpr int VO = Vec<TO>::N;          // output elements per 16-byte vector
-    static_assert(std::is_same<TO, T>::value || EPI == EPI_BIAS || EPI == EPI_ASUM, "wider output: plain products only");
+    static_assert(std::is_same<TO, T>::value || EPI == EPI_BIAS || EPI == EPI_ASUM,
+                  "wider output: plain products only");
     static_assert(EPI != EPI_ASUM || (TA && KBF), "A sums: bf16 k-major A only");
     constexpr int LDO = BN + VO;           // row stride of the output tile in the epilogue
     // stage the output tile through LDS when it fits in 160 KiB
@@ -364,12 +365,16 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const int m = wm * TM * 32 + i * 32 + r32;
-        colA[i] = !TA ? 0 : KBF ? kcol(wm * TM * 32 + i * 32, BM) : 4 * h * BM + ((m / VE + ROTA * h) % CMA) * VE + m % VE;
+        colA[i] = !TA   ? 0
+                  : KBF ? kcol(wm * TM * 32 + i * 32, BM)
+                        : 4 * h * BM + ((m / VE + ROTA * h) % CMA) * VE + m % VE;
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
         const int n = wn * TN * 32 + j * 32 + r32;
-        colB[j] = !TB ? 0 : KBF ? kcol(wn * TN * 32 + j * 32, BN) : 4 * h * BN + ((n / VE + ROTB * h) % CMB) * VE + n % VE;
+        colB[j] = !TB   ? 0
+                  : KBF ? kcol(wn * TN * 32 + j * 32, BN)
+                        : 4 * h * BN + ((n / VE + ROTB * h) % CMB) * VE + n % VE;
     }
     // bf16 k-step kc of a k-major tile with LD columns: the two transposing
     // reads of k-rows 16kc + 8h + j and 16kc + 8h + 4 + j
@@ -443,8 +448,10 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
                     for (int i = 0; i < TM; i++) {
                         float t = 0.f;
 #pragma unroll
-                        for (int e = 0; e < 4; e++)
-                            t += __uint_as_float(fa[kc & 1][i][e] << 16) + __uint_as_float(fa[kc & 1][i][e] & 0xffff0000u);
+                        for (int e = 0; e < 4; e++) {
+                            const uint32_t x = fa[kc & 1][i][e];
+                            t += __uint_as_float(x << 16) + __uint_as_float(x & 0xffff0000u);
+                        }
                         asum[i] += t;
                     }
                 }
@@ -755,12 +762,19 @@ template <> struct Mfma16<bf16> {
 // out = EPI(bias + sum) (res: the residual of EPI_BIAS_RESIDUAL, may be out);
 // otherwise it writes the fp32 partial sums part[y][M][N] (no bias), which
 // the consumer adds in split order.
-template <typename T, int NW, int PF, int EPI>
+// ACOMB: A is the output of a split decode attention, given as its fp32
+// partials apart[(row*NH + head)*asplits + s] = (o[hs], m, l) (NH = K/hs,
+// 1 <= asplits <= kAcombMax); each lane merges its 16-byte piece of A from
+// them (the arithmetic and order of decode_combine_kernel, rounded to T)
+// and writes it where the load-to-LDS copy would have put it.
+constexpr int kAcombMax = 2;
+template <typename T, int NW, int PF, int EPI, bool ACOMB = false>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_lds_kernel(T* out, float* __restrict__ part,
                                                                   const T* __restrict__ A,
                                                                   const T* __restrict__ W,
                                                                   const T* __restrict__ bias, const T* res, int M,
-                                                                  int N, int K) {
+                                                                  int N, int K, const float* __restrict__ apart,
+                                                                  int asplits, int hs) {
     constexpr int VE = Vec<T>::N;
     constexpr int CK = 128 / (int)sizeof(T);  // k per chunk: one 128-byte line per row
     constexpr int TILE = 32 * 128;            // bytes of one 32-row chunk tile
@@ -785,7 +799,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_lds_kernel(T* out, float*
     for (int q = 0; q < 4; q++) {
         const int row = 8 * q + (lane >> 3);
         gsl[q] = ((lane & 7) ^ ((row >> 1) & 7)) * VE;
-        srcA[q] = A + (int64_t)(row < M ? row : 0) * K;
+        srcA[q] = ACOMB ? nullptr : A + (int64_t)(row < M ? row : 0) * K;
         srcW[q] = W + (int64_t)(n0 + row < N ? n0 + row : 0) * K;
     }
     float bcol[2] = {0.f, 0.f};
@@ -814,8 +828,68 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_lds_kernel(T* out, float*
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int off = min(c * CK + gsl[q], K - VE);  // K % 8 == 0: slots are whole
-                copy16_to_lds(srcA[q] + off, (lds_void_ptr)(st + q * 1024));
+                if constexpr (!ACOMB) copy16_to_lds(srcA[q] + off, (lds_void_ptr)(st + q * 1024));
                 copy16_to_lds(srcW[q] + off, (lds_void_ptr)(st + TILE + q * 1024));
+            }
+            if constexpr (ACOMB) {
+                // after the W copies are in flight: row 8q + lane/8, elements
+                // off .. off+VE-1 (one head, hs % VE == 0) of the merged output.
+                // Every partial load of the batch is issued before the first
+                // use (8-byte loads: records are hs + 2 floats, hs % 8 == 0;
+                // rows past M read row 0 and are not used).
+                float2 pm[4][kAcombMax], po[4][kAcombMax][VE / 2];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int row = 8 * q + (lane >> 3);
+                    const int off = min(c * CK + gsl[q], K - VE);
+                    const int hd = off / hs, d0 = off % hs;
+                    const float* pp = apart + ((int64_t)(row < M ? row : 0) * (K / hs) + hd) * asplits * (hs + 2);
+#pragma unroll
+                    for (int sp = 0; sp < kAcombMax; sp++) {
+                        const float* rec = pp + min(sp, asplits - 1) * (hs + 2);
+                        pm[q][sp] = *reinterpret_cast<const float2*>(rec + hs);
+#pragma unroll
+                        for (int e = 0; e < VE / 2; e++)
+                            po[q][sp][e] = *reinterpret_cast<const float2*>(rec + d0 + 2 * e);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int row = 8 * q + (lane >> 3);
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int sp = 0; sp < kAcombMax; sp++)
+                        if (sp < asplits) mx = fmaxf(mx, pm[q][sp].x);
+                    float L = 0.f, o[VE];
+#pragma unroll
+                    for (int e = 0; e < VE; e++) o[e] = 0.f;
+#pragma unroll
+                    for (int sp = 0; sp < kAcombMax; sp++) {
+                        if (sp < asplits) {
+                            const float m = pm[q][sp].x;
+                            const float wgt = m == -INFINITY ? 0.f : exp2f(m - mx);
+                            L += pm[q][sp].y * wgt;
+#pragma unroll
+                            for (int e = 0; e < VE / 2; e++) {
+                                o[2 * e] += po[q][sp][e].x * wgt;
+                                o[2 * e + 1] += po[q][sp][e].y * wgt;
+                            }
+                        }
+                    }
+                    u32x4 v = zero;
+                    if (row < M) {
+#pragma unroll
+                        for (int e = 0; e < VE; e++) o[e] = o[e] / L;
+                        if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+                            for (int e = 0; e < 4; e++) v[e] = __float_as_uint(o[e]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; e++) v[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+                        }
+                    }
+                    *reinterpret_cast<u32x4*>(st + q * 1024 + lane * 16) = v;
+                }
             }
         }
         wait_vmcnt_lds<0>();

@@ -16,7 +16,8 @@ template <typename T>
 static void launch_skinny(T* out, float* part, const T* A, const T* W, const T* bias, const T* res, int M, int N,
                           int K, int splits, int epi, hipStream_t s) {
     const dim3 grid((N + 31) / 32, splits);
-#define SKINNY_LAUNCH(E) gemm_skinny_lds_kernel<T, 8, 1, E><<<grid, 512, 0, s>>>(out, part, A, W, bias, res, M, N, K)
+#define SKINNY_LAUNCH(E) \
+    gemm_skinny_lds_kernel<T, 8, 1, E><<<grid, 512, 0, s>>>(out, part, A, W, bias, res, M, N, K, nullptr, 0, 0)
     if (epi == EPI_BIAS_GELU) SKINNY_LAUNCH(EPI_BIAS_GELU);
     else if (epi == EPI_BIAS_RESIDUAL) SKINNY_LAUNCH(EPI_BIAS_RESIDUAL);
     else if (epi == EPI_DGELU) SKINNY_LAUNCH(EPI_DGELU);
@@ -271,6 +272,29 @@ int launch_matmul_kmajor(bf16* out, const bf16* A, const bf16* W, int M, int N, 
     if (splits != 1) return GPT2_ERR_INVALID_ARGUMENT;
     return launch_kmajor_bf16(out, A, W, M, N, K, lda, ldb, ta, tb, 1, static_cast<float*>(nullptr), s);
 }
+
+// Decode-step projection of a split attention's output (at most 32 rows):
+// part[y][M][N] (fp32 partial sums over `splits` k-ranges, no bias) of A W^T
+// with A [M, K] the merge of the attention's fp32 partials apart (per row and
+// head of size hs, asplits chunks of (o[hs], m, l)), merged while the product
+// loads them: the attention's separate combine launch is not needed. K % 8 == 0,
+// hs % 8 == 0, K % hs == 0, 1 <= asplits <= skinny_acomb_max_splits().
+int launch_skinny_gemm_acomb(float* part, const float* apart, int asplits, int hs, const void* weight, int M, int K,
+                             int N, int splits, int dtype, hipStream_t s) {
+    if (M < 1 || M > 32 || K % 8 || hs < 8 || hs % 8 || K % hs || splits < 1 || asplits < 1 ||
+        asplits > kAcombMax || !part || !apart)
+        return GPT2_ERR_INVALID_ARGUMENT;
+    const dim3 grid((N + 31) / 32, splits);
+    if (dtype == GPT2_BF16)
+        gemm_skinny_lds_kernel<bf16, 8, 1, EPI_BIAS, true><<<grid, 512, 0, s>>>(
+            nullptr, part, nullptr, (const bf16*)weight, nullptr, nullptr, M, N, K, apart, asplits, hs);
+    else
+        gemm_skinny_lds_kernel<float, 8, 1, EPI_BIAS, true><<<grid, 512, 0, s>>>(
+            nullptr, part, nullptr, (const float*)weight, nullptr, nullptr, M, N, K, apart, asplits, hs);
+    return launch_status();
+}
+
+int skinny_acomb_max_splits() { return kAcombMax; }
 
 // Decode-step GEMM on at most 32 rows (K % 8 == 0). part == nullptr:
 // out = epi(inp W^T + bias) in one split; otherwise fp32 partial sums over

@@ -38,11 +38,15 @@ int launch_matmul_epi(void*, const void*, const void*, const void*, const void*,
                       hipStream_t);
 int launch_attention(void*, const void*, int, int, int, int, int, hipStream_t, float*);
 int launch_attention_decode(void*, const void*, void*, void*, int, int, int, int, int, int, float*,
-                            hipStream_t);
+                            hipStream_t, int* nsplit_out);
+int decode_attention_splits(int pos, int hs, int dtype);
 int64_t decode_workspace_bytes(int B, int C, int NH, int maxT);
 bool attention_head_size_ok(int hs);
 int launch_skinny_gemm(void*, float*, const void*, const void*, const void*, int, int, int, int, int, int,
                        hipStream_t);
+int launch_skinny_gemm_acomb(float* part, const float* apart, int asplits, int hs, const void* weight, int M, int K,
+                             int N, int splits, int dtype, hipStream_t s);
+int skinny_acomb_max_splits();
 int launch_kv_store(void*, void*, const void*, int, int, int, int, int, int, hipStream_t);
 int launch_argmax(int32_t*, int32_t*, int, const void*, int, int, int, int, hipStream_t);
 int launch_layernorm_rows(void*, const void*, int64_t, const void*, const void*, int, int, float, int, hipStream_t);
@@ -57,21 +61,21 @@ int skinny_split_count(int K, int N, int es);
 static constexpr int kSkinnyRows = 32;
 static constexpr int kMaxSplits = 8;
 
-static int64_t decode_part_bytes(int B, int C, int NH, int maxT) {
-    const int64_t att = decode_workspace_bytes(B, C, NH, maxT);
-    const int64_t split = B <= kSkinnyRows ? (int64_t)kMaxSplits * B * C * 4 : 0;
-    return att > split ? att : split;
-}
-
+// fp32 partials of the decode step: the attention's key chunks, and (skinny
+// path) the split-k projections. They are separate: the attproj product
+// reads the first while it writes the second.
+static int64_t decode_apart_bytes(int B, int C, int NH, int maxT) { return decode_workspace_bytes(B, C, NH, maxT); }
+static int64_t decode_part_bytes(int B, int C) { return B <= kSkinnyRows ? (int64_t)kMaxSplits * B * C * 4 : 0; }
 
 // Workspace: residual stream x [N,C], LayerNorm output [N,C], qkv [N,3C],
-// attention output [N,C], projection output [N,C], MLP hidden [N,4C].
+// attention output [N,C], MLP hidden [N,4C], the attention's partials and
+// the projections' partials.
 struct Workspace {
     char *x, *ln, *qkv, *att, *fc;
-    float* part;
+    float *apart, *part;
     int64_t bytes;
 };
-static Workspace carve(char* base, int64_t N, int64_t C, int es, int64_t part_bytes) {
+static Workspace carve(char* base, int64_t N, int64_t C, int es, int64_t apart_bytes, int64_t part_bytes) {
     Workspace w;
     int64_t o = 0;
     auto take = [&](int64_t n) { char* p = base ? base + o : nullptr; o += align256(n); return p; };
@@ -80,9 +84,13 @@ static Workspace carve(char* base, int64_t N, int64_t C, int es, int64_t part_by
     w.qkv = take(N * 3 * C * es);
     w.att = take(N * C * es);
     w.fc = take(N * 4 * C * es);
+    w.apart = (float*)take(apart_bytes);
     w.part = (float*)take(part_bytes);
     w.bytes = o;
     return w;
+}
+static Workspace decode_carve(char* base, int B, int C, int NH, int maxT, int es) {
+    return carve(base, B, C, es, decode_apart_bytes(B, C, NH, maxT), decode_part_bytes(B, C));
 }
 
 }  // namespace gpt2
@@ -115,7 +123,7 @@ extern "C" int64_t gpt2_param_count(const gpt2_config* cfg) {
 
 extern "C" int64_t gpt2_workspace_bytes(const gpt2_config* cfg, int B, int T) {
     if (!config_ok(cfg) || B < 0 || T < 0) return -1;
-    return carve(nullptr, (int64_t)B * T, cfg->C, elem_size(cfg->dtype), 0).bytes;
+    return carve(nullptr, (int64_t)B * T, cfg->C, elem_size(cfg->dtype), 0, 0).bytes;
 }
 
 // Embedding and the L blocks over B x T tokens; the residual stream ends in
@@ -167,7 +175,7 @@ extern "C" int gpt2_forward(void* logits, void* probs, const int32_t* tokens, co
     const int64_t N = (int64_t)B * T;
     const int C = cfg->C, L = cfg->L, dt = cfg->dtype, es = elem_size(dt);
     if (N > INT32_MAX / 4) return GPT2_ERR_UNSUPPORTED;
-    Workspace w = carve((char*)workspace, N, C, es, 0);
+    Workspace w = carve((char*)workspace, N, C, es, 0, 0);
     if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     const ParamOffsets po = param_offsets(*cfg);
     const char* P = (const char*)params;
@@ -190,7 +198,7 @@ extern "C" int gpt2_forward(void* logits, void* probs, const int32_t* tokens, co
 
 extern "C" int64_t gpt2_decode_workspace_bytes(const gpt2_config* cfg, int B) {
     if (!config_ok(cfg) || B < 0) return -1;
-    return carve(nullptr, B, cfg->C, elem_size(cfg->dtype), decode_part_bytes(B, cfg->C, cfg->NH, cfg->maxT))
+    return decode_carve(nullptr, B, cfg->C, cfg->NH, cfg->maxT, elem_size(cfg->dtype))
         .bytes;
 }
 
@@ -214,11 +222,20 @@ static int decode_step_impl(void* logits, void* probs, const int32_t* tokens, in
         for (int l = 0; l < L; l++) {
             CHECK(launch_skinny_gemm(w.qkv, nullptr, w.ln, at(po.qkv_w + l * 3 * C64 * C64),
                                      at(po.qkv_b + l * 3 * C64), B, C, 3 * C, 1, EPI_BIAS, dt, s));
+            // an attention split in two (or up to the merge's limit) leaves
+            // its partials to the attproj product, which merges them as it
+            // loads its A operand (no combine launch)
+            int nsp = 1;
+            const bool defer = decode_attention_splits(pos, C / NH, dt) <= skinny_acomb_max_splits();
             CHECK(launch_attention_decode(w.att, w.qkv, (char*)kcache + l * layer_elems * es,
                                           (char*)vcache + l * layer_elems * es, B, pos, cfg->maxT, C, NH,
-                                          dt, w.part, s));
-            CHECK(launch_skinny_gemm(nullptr, w.part, w.att, at(po.ap_w + l * C64 * C64), nullptr, B, C, C,
-                                     s_ap, EPI_BIAS, dt, s));
+                                          dt, w.apart, s, defer ? &nsp : nullptr));
+            if (nsp > 1)
+                CHECK(launch_skinny_gemm_acomb(w.part, w.apart, nsp, C / NH, at(po.ap_w + l * C64 * C64), B, C, C,
+                                               s_ap, dt, s));
+            else
+                CHECK(launch_skinny_gemm(nullptr, w.part, w.att, at(po.ap_w + l * C64 * C64), nullptr, B, C, C,
+                                         s_ap, EPI_BIAS, dt, s));
             CHECK(launch_residual_layernorm(w.ln, w.x, w.part, s_ap, at(po.ap_b + l * C64),
                                             at(po.ln2_g + l * C64), at(po.ln2_b + l * C64), B, C,
                                             cfg->ln_eps, dt, s));
@@ -243,7 +260,7 @@ static int decode_step_impl(void* logits, void* probs, const int32_t* tokens, in
                             B, C, 3 * C, dt, s));
         CHECK(launch_attention_decode(w.att, w.qkv, (char*)kcache + l * layer_elems * es,
                                       (char*)vcache + l * layer_elems * es, B, pos, cfg->maxT, C, NH,
-                                      dt, w.part, s));
+                                      dt, w.apart, s, nullptr));
         CHECK(launch_matmul_epi(w.x, w.att, at(po.ap_w + l * C64 * C64), at(po.ap_b + l * C64), w.x, B, C, C,
                                 EPI_BIAS_RESIDUAL, dt, s));
         CHECK(launch_layernorm(w.ln, nullptr, nullptr, w.x, at(po.ln2_g + l * C64),
@@ -274,7 +291,7 @@ extern "C" int gpt2_decode_step(void* logits, void* probs, const int32_t* tokens
         return GPT2_ERR_UNSUPPORTED;
     if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
     const int C = cfg->C, NH = cfg->NH, es = elem_size(cfg->dtype);
-    Workspace w = carve((char*)workspace, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT));
+    Workspace w = decode_carve((char*)workspace, B, C, NH, cfg->maxT, es);
     if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     return decode_step_impl(logits, probs, tokens, pos, kcache, vcache, params, cfg, B, w, (hipStream_t)stream);
 }
@@ -326,13 +343,13 @@ extern "C" int gpt2_decode_step_noalloc(void* logits, void* probs, const int32_t
         return GPT2_ERR_UNSUPPORTED;
     if (probs == logits) return GPT2_ERR_INVALID_ARGUMENT;
     const int C = cfg->C, NH = cfg->NH, es = elem_size(cfg->dtype);
-    const int64_t need = carve(nullptr, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT)).bytes;
+    const int64_t need = decode_carve(nullptr, B, C, NH, cfg->maxT, es).bytes;
     if (need > (int64_t)GPT2_DECODE_SCRATCH_BYTES) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     void* base = scratch_address();
     if (!base) return GPT2_ERR_HIP;
     // Nothing in the carve has to start at zero: every kernel of the step
     // writes each scratch element before any kernel reads it.
-    const Workspace w = carve((char*)base, B, C, es, decode_part_bytes(B, C, NH, cfg->maxT));
+    const Workspace w = decode_carve((char*)base, B, C, NH, cfg->maxT, es);
     return decode_step_impl(logits, probs, tokens, pos, kcache, vcache, params, cfg, B, w, (hipStream_t)stream);
 }
 
@@ -367,7 +384,7 @@ extern "C" int gpt2_prefill(void* logits, void* probs, const int32_t* tokens, vo
     if (!config_supported(cfg) || !aligned16(logits) || !aligned16(params) || !aligned16(kcache) ||
         !aligned16(vcache) || !aligned16(workspace) || (probs && !aligned16(probs)))
         return GPT2_ERR_UNSUPPORTED;
-    const Workspace w = carve((char*)workspace, (int64_t)B * T, cfg->C, elem_size(cfg->dtype), 0);
+    const Workspace w = carve((char*)workspace, (int64_t)B * T, cfg->C, elem_size(cfg->dtype), 0, 0);
     if (workspace_bytes < w.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     return prefill_impl(logits, probs, tokens, kcache, vcache, (const char*)params, cfg, B, T, w,
                         (hipStream_t)stream);
@@ -380,8 +397,8 @@ struct GenLayout {
 };
 static GenLayout gen_layout(const gpt2_config* cfg, int B, int T) {
     const int C = cfg->C, es = elem_size(cfg->dtype);
-    const int64_t pre = carve(nullptr, (int64_t)B * T, C, es, 0).bytes;
-    const int64_t dec = carve(nullptr, B, C, es, decode_part_bytes(B, C, cfg->NH, cfg->maxT)).bytes;
+    const int64_t pre = carve(nullptr, (int64_t)B * T, C, es, 0, 0).bytes;
+    const int64_t dec = decode_carve(nullptr, B, C, cfg->NH, cfg->maxT, es).bytes;
     GenLayout g;
     g.logits_off = align256(pre > dec ? pre : dec);
     g.tok_off = g.logits_off + align256((int64_t)B * cfg->Vp * es);
@@ -409,8 +426,8 @@ extern "C" int gpt2_generate(int32_t* out_tokens, const int32_t* prompt, int n_n
     if (workspace_bytes < g.bytes) return GPT2_ERR_WORKSPACE_TOO_SMALL;
     char* base = (char*)workspace;
     const int C = cfg->C, es = elem_size(cfg->dtype);
-    const Workspace wp = carve(base, (int64_t)B * T, C, es, 0);
-    const Workspace wd = carve(base, B, C, es, decode_part_bytes(B, C, cfg->NH, cfg->maxT));
+    const Workspace wp = carve(base, (int64_t)B * T, C, es, 0, 0);
+    const Workspace wd = decode_carve(base, B, C, cfg->NH, cfg->maxT, es);
     void* logits = base + g.logits_off;
     int32_t* tok = (int32_t*)(base + g.tok_off);
     hipStream_t s = (hipStream_t)stream;
