@@ -242,35 +242,40 @@ def test_forward_full_size(name):
     assert np.array_equal(b2[:-1, :t + 1], b_logits[:-1, :t + 1])
 
 
-def test_decode_step_matches_oracle():
-    """GPT-2 small bf16 decode: 32 sequences at position 1023 over an N(0,1)
-    prefilled cache; the oracle runs sequences 0..3 (rows are independent)."""
-    announce("decode-step")
+@pytest.mark.parametrize("B,pos", [(32, None), (7, 700)])
+def test_decode_step_matches_oracle(B, pos):
+    """GPT-2 small bf16 decode over an N(0,1) prefilled cache: 32 sequences at
+    position 1023, and 7 at position 700 (fewer rows than the skinny tile);
+    both split the attention in two key chunks, which the attproj product
+    merges. The oracle runs sequences 0..3 (rows are independent)."""
     import torch
     w = I.WORKLOADS["decode"]
+    pos = w.decode_pos if pos is None else pos
+    announce("decode-step", B, pos)
     m = Model(w)
-    tok = I.make_tokens(w)
+    tok = I.make_tokens(w)[:B]
     kc, vc = I.make_kv_cache(w)
+    kc, vc = np.ascontiguousarray(kc[:, :B]), np.ascontiguousarray(vc[:, :B])
     tk, tv = dev(kc, w.dtype), dev(vc, w.dtype)
     # poison the slot being written: the step must never read it first
-    tk[:, :, :, w.decode_pos] = float("nan")
-    tv[:, :, :, w.decode_pos] = float("nan")
-    logits = empty((w.B, w.Vp), w.dtype)
-    probs = empty((w.B, w.Vp), w.dtype)
-    ws = torch.empty(G.decode_workspace_bytes(m.cfg, w.B), dtype=torch.uint8, device="cuda")
-    G.gpt2_decode_step(logits, probs, dev_int(tok), w.decode_pos, tk, tv, m.params, m.cfg, ws)
+    tk[:, :, :, pos] = float("nan")
+    tv[:, :, :, pos] = float("nan")
+    logits = empty((B, w.Vp), w.dtype)
+    probs = empty((B, w.Vp), w.dtype)
+    ws = torch.empty(G.decode_workspace_bytes(m.cfg, B), dtype=torch.uint8, device="cuda")
+    G.gpt2_decode_step(logits, probs, dev_int(tok), pos, tk, tv, m.params, m.cfg, ws)
     gl, gp = host(logits), host(probs)
     S = 4
     kcs = np.ascontiguousarray(kc[:, :S])
     vcs = np.ascontiguousarray(vc[:, :S])
-    rl, rp = oracle.decode_step(tok[:S], w.decode_pos, kcs, vcs, m.params_np, w.L, w.C, w.NH, w.V,
+    rl, rp = oracle.decode_step(tok[:S], pos, kcs, vcs, m.params_np, w.L, w.C, w.NH, w.V,
                                 w.Vp, w.maxT, w.ln_eps)
     check_logits(w, gl[:S], rl)
     assert rel_err(gp[:S], rp) <= 2e-2
     assert np.all(np.isfinite(gl[:, :w.V]))
     # the step wrote this position's keys: compare with the oracle's (fp32) keys
-    kgot = host(tk)[:, :S, :, w.decode_pos]
-    assert rel_err(kgot, kcs[:, :, :, w.decode_pos]) <= 2e-2
+    kgot = host(tk)[:, :S, :, pos]
+    assert rel_err(kgot, kcs[:, :, :, pos]) <= 2e-2
 
 
 def test_decode_matches_forward_tiny_fp32():
