@@ -150,7 +150,7 @@ def _linear_case(d, N, C, OC, seed, integer=False):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N,C,OC", [(64, 64, 256), (37, 104, 40), (130, 256, 64), (1, 8, 8), (1000, 104, 200),
-                                    (1024, 104, 200), (256, 96, 64), (96, 64, 136)])
+                                    (1024, 104, 200), (256, 96, 64), (96, 64, 136), (64, 8, 8), (1024, 8, 16)])
 def test_matmul_backward(dt, N, C, OC):
     announce("matmul_backward", dt, N, C, OC)
     d = DT[dt]
