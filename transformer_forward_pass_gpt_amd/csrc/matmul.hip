@@ -40,8 +40,8 @@ enum GemmCfg {
     P128x256_O4, P128x256_R3, P256x128_G, P128x128_R4, P128x128_K3, P256x256_K2, P128x192_K2,  // bf16
     G_NCFG
 };
-// fp32 128x288_p2: 4 wavefronts of 32x288 (nine accumulator tiles each), so GPT-2 small's qkv
-// (2304 wide) is 256 tiles, one round of the CUs; 128x192_p4_r64: four stages of 64-byte rows.
+// fp32 128x288_p3: 4 wavefronts of 32x288 (nine accumulator tiles each), so GPT-2 small's qkv
+// (2304 wide) is 256 tiles, one round of the CUs; three stages fill 156 KiB of LDS; 128x192_p4_r64: four stages of 64-byte rows.
 // "_p<S>" = S-stage pipeline; "_o<n>" = registers capped so n wavefronts fit per SIMD (2 or 3
 // workgroups per CU); "_k128" = 128-byte k-rows per stage (twice the default bf16 depth); "g" =
 // grouped XCD-aware walk (the fp32 vocabulary tile walks columns instead). 256x256_p2_k128:
@@ -51,7 +51,7 @@ enum GemmCfg {
 static const PipeCfg kCfg[G_NCFG] = {
     {"skinny32", 0},          {"64x64_r", 0},          {"64x128_r", 0},         {"128x96_r", 0},
     {"128x96_p4", 128},       {"128x96_p5", 128},      {"256x128_p3", 128},     {"128x128_p4_o2", 64},
-    {"128x288_p2", 128},      {"128x192_p4_r64", 64},
+    {"128x288_p3", 128},      {"128x192_p4_r64", 64},
     {"128x256_p3_o4", 64},    {"128x256_p3_k128", 128}, {"256x128_p3g", 128},
     {"128x128_p4_k128", 128}, {"128x128_p3_k128", 128}, {"256x256_p2_k128", 128},
     {"128x192_p2_k128", 128},
@@ -111,7 +111,7 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
         case P128x96_S5: PIPE(4, 1, 1, 3, 128, 5, 4, 0, 8, 1); break;
         case P256x128_S3A: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 1, 0); break;
         case P128x128_O2: PIPE(2, 2, 2, 2, 64, 4, 2, 2, 4, 1); break;
-        case P128x288_I: PIPE(4, 1, 1, 9, 128, 2, 1, 0, 8, 1); break;
+        case P128x288_I: PIPE(4, 1, 1, 9, 128, 3, 2, 0, 8, 1); break;
         case P128x192_R4: PIPE(2, 2, 2, 3, 64, 4, 2, 0, 4, 1); break;
         default:
             if constexpr (std::is_same<T, bf16>::value) {  // the bf16-only shapes (choose_pipe)
