@@ -227,7 +227,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(T* out, const T* __re
 // elements long (without SPLITK they are K long and lda, ldb, split_out are
 // unused).
 // TO: the output type; fp32 products of bf16 operands (split-k partial sums
-// that a later fp32 sum reduces) take the plain epilogue only.
+// that a later fp32 sum reduces) take the plain epilogue or EPI_ASUM only.
 // TA / TB: the operand is stored k-major, A as [K][M] (row stride lda), W as
 // [K][N] (row stride ldb): out = A^T-stored . W^T-stored without a transpose
 // pass. Its tile is copied as BK rows of BM (BN) elements.
@@ -305,8 +305,9 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
     // Chunk q of a tile = row q / CH, slot q % CH; the slot holds logical
     // k-chunk slot ^ ((row / RP) % CH).
     // k-major operands: chunk q = k-row q / CM, slot q % CM holding the chunk
-    // of m (n) elements (slot - ROT*((row>>2)&1)) mod CM; columns past M (N)
-    // read a clamped (valid) chunk whose results are never stored.
+    // of m (n) elements (slot - ROT*((row>>2)&1)) mod CM (fp32) or
+    // slot ^ 4(row % 4) (bf16); columns past M (N) read a clamped (valid)
+    // chunk whose results are never stored.
     int64_t offA[LA], offB[LB];
 #pragma unroll
     for (int j = 0; j < LA; j++) {
