@@ -62,12 +62,19 @@ __global__ __launch_bounds__(kBwdThreads) void gelu_backward_kernel(T* dinp, con
 // out[c] = sum_{r < R} part[r * C + c]: 64 columns x 16 row slices per
 // workgroup (1024 threads); slice k sums rows k*q .. k*q+q-1 in ascending
 // order (q = ceil(R/16)), and the 16 slice sums are added in slice order, so
-// the result is a fixed function of the partials.
+// the result is a fixed function of the partials. Grid row y = 1 (when
+// out2 is given) does the same for (out2, part2): two reductions of the same
+// shape in one launch.
 static constexpr int kColSlices = 16;
 
 template <typename T>
-__global__ __launch_bounds__(1024) void colsum_kernel(T* out, const float* __restrict__ part, int R, int C) {
+__global__ __launch_bounds__(1024) void colsum_kernel(T* out, const float* __restrict__ part, int R, int C,
+                                                      T* out2, const float* __restrict__ part2) {
     __shared__ float sh[kColSlices][64];
+    if (blockIdx.y == 1) {  // workgroup-uniform
+        out = out2;
+        part = part2;
+    }
     const int lane = threadIdx.x & 63, k = threadIdx.x >> 6;
     const int c = blockIdx.x * 64 + lane;
     const int q = (R + kColSlices - 1) / kColSlices, r0 = k * q, r1 = min(R, r0 + q);
@@ -94,8 +101,9 @@ __global__ __launch_bounds__(1024) void colsum_kernel(T* out, const float* __res
 }
 
 template <typename T>
-static void launch_colsum(T* out, const float* part, int R, int C, hipStream_t s) {
-    colsum_kernel<T><<<(C + 63) / 64, 1024, 0, s>>>(out, part, R, C);
+static void launch_colsum(T* out, const float* part, int R, int C, hipStream_t s, T* out2 = nullptr,
+                          const float* part2 = nullptr) {
+    colsum_kernel<T><<<dim3((C + 63) / 64, out2 ? 2 : 1), 1024, 0, s>>>(out, part, R, C, out2, part2);
 }
 
 // First stage of the column sums of x [R, C] (fp32): part[y][c] = sum of rows
@@ -279,8 +287,10 @@ static void launch_ln_bwd_t(T* dinp, T* dgamma, T* dbeta, const T* dres, const T
     else if (vpl <= 4) LNB(4);
     else LNB(8);
 #undef LNB
-    if (dgamma) launch_colsum<T>(dgamma, gpart, grid, C, s);
-    if (dbeta) launch_colsum<T>(dbeta, bpart, grid, C, s);
+    // both column sums in one launch when both are wanted
+    if (dgamma && dbeta) launch_colsum<T>(dgamma, gpart, grid, C, s, dbeta, bpart);
+    else if (dgamma) launch_colsum<T>(dgamma, gpart, grid, C, s);
+    else if (dbeta) launch_colsum<T>(dbeta, bpart, grid, C, s);
 }
 
 // ---------------------------------------------------------------- transpose
