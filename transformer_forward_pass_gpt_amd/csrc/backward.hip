@@ -22,7 +22,7 @@ int launch_matmul_splitk_part(float*, const bf16*, const bf16*, int, int, int, i
 int launch_matmul_epi(void*, const void*, const void*, const void*, const void*, int, int, int, int, int,
                       hipStream_t);
 int launch_matmul_kmajor(float*, const float*, const float*, int, int, int, int, int, bool, bool, int, hipStream_t,
-                         const float* = nullptr);
+                         const float* = nullptr, float* = nullptr);
 int launch_matmul_kmajor(float*, const bf16*, const bf16*, int, int, int, int, int, bool, bool, int, float*,
                          hipStream_t);
 int launch_matmul_kmajor(bf16*, const bf16*, const bf16*, int, int, int, int, int, bool, bool, int, hipStream_t);
@@ -434,12 +434,13 @@ static int launch_matmul_bwd_t(T* dinp, T* dweight, T* dbias, const T* dout, con
         }
         if (dweight && km_dw) {
             const int Sk = dw_splits_kmajor(N, C, OC, dtype);
-            // bf16 in slices: the bias partials come from the product's own
-            // reads of dout (per slice, into bpart: Sk <= 8 <= N/64 rows) and
-            // are summed with the weight slices
-            T* db_fused = !f32 && Sk > 1 ? dbias : nullptr;
+            // in slices: the bias partials come from the product's own reads
+            // of dout (per slice, into bpart: Sk <= 8 <= N/64 rows) and are
+            // summed with the weight slices
+            T* db_fused = Sk > 1 ? dbias : nullptr;
             if constexpr (f32)
-                rc = launch_matmul_kmajor(Sk > 1 ? wpart : dweight, dout, inp, OC, C, N / Sk, OC, C, true, true, Sk, s);
+                rc = launch_matmul_kmajor(Sk > 1 ? wpart : dweight, dout, inp, OC, C, N / Sk, OC, C, true, true, Sk, s,
+                                          nullptr, db_fused ? bpart : nullptr);
             else if (Sk > 1)
                 rc = launch_matmul_kmajor(wpart, dout, inp, OC, C, N / Sk, OC, C, true, true, Sk,
                                           db_fused ? bpart : nullptr, s);

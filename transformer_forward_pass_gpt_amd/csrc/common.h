@@ -159,7 +159,7 @@ void set_last_hip_error(int e);
 // row and per group of kStatCols columns, the max m and the sum of
 // e^{y - m} over the group's columns below a limit V (row statistics for a
 // one-pass softmax).
-// EPI_ASUM (weight gradients, bf16 A stored k-major, no bias): the stored
+// EPI_ASUM (weight gradients, A stored k-major, no bias): the stored
 // product plus the sum of A(k, m) over the launch's k-range for every m, i.e.
 // the column sums of the stored A rows (the bias gradient of a linear layer
 // is the column sum of its output gradient, which is this A), taken from the

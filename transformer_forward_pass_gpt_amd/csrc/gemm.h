@@ -273,7 +273,7 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
     constexpr int VO = Vec<TO>::N;          // output elements per 16-byte vector
     static_assert(std::is_same<TO, T>::value || EPI == EPI_BIAS || EPI == EPI_ASUM,
                   "wider output: plain products only");
-    static_assert(EPI != EPI_ASUM || (TA && KBF), "A sums: bf16 k-major A only");
+    static_assert(EPI != EPI_ASUM || TA, "A sums: k-major A only");
     constexpr int LDO = BN + VO;           // row stride of the output tile in the epilogue
     // stage the output tile through LDS when it fits in 160 KiB
     constexpr bool STAGED = !DIRECT && BM * LDO * (int)sizeof(TO) <= 160 * 1024;
@@ -418,8 +418,9 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
         }
     };
     // EPI_ASUM: the waves of tile column 0 with wn == 0 (each A row once) add
-    // up their A fragments: lane (h, r32) sums k = 16kc + 8h .. +7 of row r32
-    // of each of its TM row tiles; the two halves are combined at the end.
+    // up their A fragments: lane (h, r32) sums its k of row r32 (bf16:
+    // 16kc + 8h .. +7; fp32: 8kc + 4h .. +3) of each of its TM row tiles; the
+    // two halves are combined at the end.
     float asum[TM];
 #pragma unroll
     for (int i = 0; i < TM; i++) asum[i] = 0.f;
@@ -451,7 +452,8 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
 #pragma unroll
                         for (int e = 0; e < 4; e++) {
                             const uint32_t x = fa[kc & 1][i][e];
-                            t += __uint_as_float(x << 16) + __uint_as_float(x & 0xffff0000u);
+                            if constexpr (KBF) t += __uint_as_float(x << 16) + __uint_as_float(x & 0xffff0000u);
+                            else t += __uint_as_float(x);
                         }
                         asum[i] += t;
                     }

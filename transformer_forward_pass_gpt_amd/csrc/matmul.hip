@@ -41,7 +41,8 @@ enum GemmCfg {
     G_NCFG
 };
 // fp32 128x288_p3: 4 wavefronts of 32x288 (nine accumulator tiles each), so GPT-2 small's qkv
-// (2304 wide) is 256 tiles, one round of the CUs; three stages fill 156 KiB of LDS; 128x192_p4_r64: four stages of 64-byte rows.
+// (2304 wide) is 256 tiles, one round of the CUs; three stages fill 156 KiB of LDS;
+// 128x192_p4_r64: four stages of 64-byte rows.
 // "_p<S>" = S-stage pipeline; "_o<n>" = registers capped so n wavefronts fit per SIMD (2 or 3
 // workgroups per CU); "_k128" = 128-byte k-rows per stage (twice the default bf16 depth); "g" =
 // grouped XCD-aware walk (the fp32 vocabulary tile walks columns instead). 256x256_p2_k128:
@@ -211,11 +212,19 @@ int launch_matmul_splitk_part(float* part, const bf16* A, const bf16* W, int M, 
 // [K][M] (rows lda apart) when ta else [M][K] (lda = K), W stored [K][N]
 // (rows ldb apart) when tb else [N][K]. K (per slice) % 32 == 0; M % 4 == 0
 // when ta, N % 4 == 0 when tb. gelu_in (nullable; W k-major alone, one
-// slice): the EPI_DGELU epilogue with that [M,N] GELU input.
+// slice): the EPI_DGELU epilogue with that [M,N] GELU input. asum (nullable;
+// both k-major): asum[y*M + m] = the sum of A(k, m) over slice y's k-range
+// (EPI_ASUM).
 int launch_matmul_kmajor(float* out, const float* A, const float* W, int M, int N, int K, int lda, int ldb, bool ta,
-                         bool tb, int splits, hipStream_t s, const float* gelu_in) {
+                         bool tb, int splits, hipStream_t s, const float* gelu_in, float* asum) {
     if (K % 32 || splits < 1 || (ta && M % 4) || (tb && N % 4)) return GPT2_ERR_INVALID_ARGUMENT;
     const int64_t so = (int64_t)M * N;
+    if (asum) {
+        if (!ta || !tb || gelu_in) return GPT2_ERR_INVALID_ARGUMENT;
+        launch_gemm_kmajor<4, 1, 1, 3, 128, 4, 4, 0, true, true, float, float, EPI_ASUM>(
+            out, A, W, nullptr, M, N, K, lda, ldb, splits, so, 8, 1, s, asum);
+        return launch_status();
+    }
     if (gelu_in) {
         if (ta || !tb || splits != 1) return GPT2_ERR_INVALID_ARGUMENT;
         launch_gemm_kmajor<4, 1, 1, 3, 128, 4, 4, 0, false, true, float, float, EPI_DGELU>(
