@@ -169,7 +169,14 @@ void set_last_hip_error(int e);
 // y = acc + bias rounded to the output type, times g'(x) for x = res[row][col]
 // (the GELU's input), rounded again: what a separate GELU backward computes
 // from the stored product.
-enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_STATS = 3, EPI_ASUM = 4, EPI_DGELU = 5 };
+// EPI_BIAS_GELU2 (training forward): y = acc + bias rounded to the output
+// type is stored in out, and GELU of that stored y, rounded, in out2: the
+// pre-activation a GELU backward needs and the activation the next product
+// reads, as a separate GELU kernel would compute it.
+enum Epilogue {
+    EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_STATS = 3, EPI_ASUM = 4, EPI_DGELU = 5,
+    EPI_BIAS_GELU2 = 6
+};
 constexpr int kStatCols = 128;
 // Status after a launch: GPT2_OK, or GPT2_ERR_HIP with the code recorded.
 int launch_status();

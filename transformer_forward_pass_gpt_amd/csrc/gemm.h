@@ -249,7 +249,8 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
                                                                 const T* __restrict__ bias, const TO* res, int M,
                                                                 int N, int K, int group_m, int remap, int lda,
                                                                 int ldb, int64_t split_out,
-                                                                float* __restrict__ stats, int vlim) {
+                                                                float* __restrict__ stats, int vlim,
+                                                                TO* __restrict__ out2) {
     // RB: bytes of k per tile row (64 or 128); S: LDS stages (S-1 tiles in flight;
     // S = 2 is plain double buffering: tile t+1 loads while tile t is multiplied)
     constexpr int NW = WM * WN;
@@ -628,9 +629,17 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
             for (int c = tid; c < BM * CPR; c += NW * 64) {
                 const int rl = c / CPR, cv = c % CPR;
                 const int row = m0 + rl, col = n0 + cv * VO;
-                if (row < M && col < N)
-                    *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) =
-                        *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VO]);
+                if (row < M && col < N) {
+                    const u32x4 y = *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VO]);
+                    *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) = y;
+                    if constexpr (EPI == EPI_BIAS_GELU2) {
+                        float a[VO];
+                        unpack_vec<TO>(y, a);
+#pragma unroll
+                        for (int e = 0; e < VO; e++) a[e] = gelu_tanh(a[e]);
+                        store_vec(out2 + (int64_t)row * N + col, a);
+                    }
+                }
             }
         }
     } else {
@@ -653,6 +662,8 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
                         if constexpr (EPI == EPI_BIAS_RESIDUAL) y = storage_round(out, y) + r;
                         if constexpr (EPI == EPI_DGELU) y = storage_round(out, y) * gelu_tanh_grad(r);
                         store_scalar(out + (int64_t)row * N + col, y);
+                        if constexpr (EPI == EPI_BIAS_GELU2)
+                            store_scalar(out2 + (int64_t)row * N + col, gelu_tanh(storage_round(out, y)));
                     }
                 }
         }
@@ -663,18 +674,18 @@ template <typename T, int WM, int WN, int TM, int TN, int RB, int S, int SCHED, 
 static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int M, int N, int K,
                              int group_m, int remap, hipStream_t s, int epi = EPI_BIAS, const T* res = nullptr,
                              int lda = 0, int splits = 1, int64_t split_out = 0, float* stats = nullptr,
-                             int vlim = 0) {
+                             int vlim = 0, T* out2 = nullptr) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     const int nwg = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(nwg, splits);
     if (lda == 0) lda = K;
 #define GEMM_PIPE_LAUNCH(E)                                                                              \
     gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, E><<<grid, WM * WN * 64, 0, s>>>( \
-        out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out, stats, vlim)
+        out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out, stats, vlim, out2)
     if (splits > 1 || lda != K) {
         gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, DIRECT, EPI_BIAS, true>
             <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap, lda, lda, split_out,
-                                           nullptr, 0);
+                                           nullptr, 0, static_cast<T*>(nullptr));
         return;
     }
     if constexpr (BN % kStatCols == 0) {
@@ -686,6 +697,7 @@ static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int 
     if (epi == EPI_BIAS_GELU) GEMM_PIPE_LAUNCH(EPI_BIAS_GELU);
     else if (epi == EPI_BIAS_RESIDUAL) GEMM_PIPE_LAUNCH(EPI_BIAS_RESIDUAL);
     else if (epi == EPI_DGELU) GEMM_PIPE_LAUNCH(EPI_DGELU);
+    else if (epi == EPI_BIAS_GELU2) GEMM_PIPE_LAUNCH(EPI_BIAS_GELU2);
     else GEMM_PIPE_LAUNCH(EPI_BIAS);
 #undef GEMM_PIPE_LAUNCH
 }
@@ -704,7 +716,7 @@ static void launch_gemm_kmajor(TO* out, const T* A, const T* W, const typename s
     const dim3 grid(nwg, splits);
     gemm_pipe_kernel<T, WM, WN, TM, TN, RB, S, SCHED, WPE, false, EPI, true, TA, TB, TO>
         <<<grid, WM * WN * 64, 0, s>>>(out, A, W, bias, res, M, N, K, group_m, remap, lda, ldb, split_out, stats,
-                                       0);
+                                       0, nullptr);
 }
 
 template <typename T, int WM, int WN, int TM, int TN, int SCHED = 4>

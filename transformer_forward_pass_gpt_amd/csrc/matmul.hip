@@ -95,9 +95,11 @@ static GemmCfg choose_cfg(int M, int N, int K, int dtype) {
     return S32;
 }
 
+// out2: the second output of EPI_BIAS_GELU2 (pipelined tiles only; the
+// caller checks matmul_gelu2_supported).
 template <typename T>
 static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T* res, int M, int N, int K,
-                          int dtype, int epi, hipStream_t s) {
+                          int dtype, int epi, hipStream_t s, T* out2 = nullptr) {
     constexpr int BK = Vec<T>::N * 8;  // 128 bytes of k per row per LDS tile
     switch (choose_cfg(M, N, K, dtype)) {
         case S32: launch_skinny<T>(out, nullptr, A, W, bias, res, M, N, K, 1, epi, s); break;
@@ -107,7 +109,8 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
         case R128x96: launch_gemm_cfg<T, 4, 1, 1, 3, BK>(out, A, W, bias, M, N, K, 8, 1, s, epi, res); break;
         // launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SCHED, WPE>(..., group_m, remap, s, epi, res)
 #define PIPE(WM, WN, TM, TN, RB, S, SC, WPE, G, R) \
-    launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SC, WPE>(out, A, W, bias, M, N, K, G, R, s, epi, res)
+    launch_gemm_pipe<T, WM, WN, TM, TN, RB, S, SC, WPE>(out, A, W, bias, M, N, K, G, R, s, epi, res, 0, 1, 0, \
+                                                        nullptr, 0, out2)
         case P128x96_S4: PIPE(4, 1, 1, 3, 128, 4, 4, 0, 8, 1); break;
         case P128x96_S5: PIPE(4, 1, 1, 3, 128, 5, 4, 0, 8, 1); break;
         case P256x128_S3A: PIPE(4, 2, 2, 2, 128, 3, 2, 0, 1, 0); break;
@@ -157,6 +160,22 @@ int launch_matmul_epi(void* out, const void* inp, const void* weight, const void
     return launch_status();
 }
 
+// out = inp W^T + bias and out2 = GELU(out), both rounded to the storage
+// type, in one product (EPI_BIAS_GELU2) when its tile is a pipelined one;
+// GPT2_ERR_UNSUPPORTED otherwise (the caller then runs the product and
+// launch_gelu).
+int launch_matmul_gelu2(void* out, void* out2, const void* inp, const void* weight, const void* bias, int N, int C,
+                        int OC, int dtype, hipStream_t s) {
+    if (choose_cfg(N, OC, C, dtype) < P128x96_S4) return GPT2_ERR_UNSUPPORTED;  // skinny / register-staged
+    if (dtype == GPT2_BF16)
+        launch_gemm_t<bf16>((bf16*)out, (const bf16*)inp, (const bf16*)weight, (const bf16*)bias, nullptr, N, OC,
+                            C, dtype, EPI_BIAS_GELU2, s, (bf16*)out2);
+    else
+        launch_gemm_t<float>((float*)out, (const float*)inp, (const float*)weight, (const float*)bias, nullptr, N,
+                             OC, C, dtype, EPI_BIAS_GELU2, s, (float*)out2);
+    return launch_status();
+}
+
 int launch_matmul(void* out, const void* inp, const void* weight, const void* bias, int N, int C,
                   int OC, int dtype, hipStream_t s) {
     return launch_matmul_epi(out, inp, weight, bias, nullptr, N, C, OC, EPI_BIAS, dtype, s);
@@ -203,7 +222,7 @@ int launch_matmul_splitk_part(float* part, const bf16* A, const bf16* W, int M, 
     const int nwg = ((M + 127) / 128) * ((N + 127) / 128);
     gemm_pipe_kernel<bf16, 2, 2, 2, 2, 128, 3, 2, 0, false, EPI_BIAS, true, false, false, float>
         <<<dim3(nwg, splits), 256, 0, s>>>(part, A, W, nullptr, nullptr, M, N, Kc, 8, 1, lda, lda, (int64_t)M * N,
-                                           nullptr, 0);
+                                           nullptr, 0, nullptr);
     return launch_status();
 }
 

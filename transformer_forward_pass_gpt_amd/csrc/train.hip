@@ -25,6 +25,7 @@ int launch_layernorm(void*, float*, float*, const void*, const void*, const void
 int launch_matmul(void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
 int launch_matmul_epi(void*, const void*, const void*, const void*, const void*, int, int, int, int, int,
                       hipStream_t);
+int launch_matmul_gelu2(void*, void*, const void*, const void*, const void*, int, int, int, int, hipStream_t);
 int launch_attention(void*, const void*, int, int, int, int, int, hipStream_t, float*);
 int launch_gelu(void*, const void*, int64_t, int, hipStream_t);
 int launch_crossentropy_backward(void*, float*, float*, const void*, const int32_t*, float, int, int, int, int,
@@ -189,10 +190,17 @@ extern "C" int gpt2_train_forward(float* losses, float* mean_loss, const int32_t
                                 EPI_BIAS_RESIDUAL, dt, s));
         CHECK(launch_layernorm(a.ln2, a.ln2_mean, a.ln2_rstd, a.res1, at(po.ln2_g + l * C64), at(po.ln2_b + l * C64),
                                n, C, cfg->ln_eps, dt, s));
-        // the pre-activation is kept for GELU's backward, the activation for fcproj's
-        CHECK(launch_matmul(a.fch, a.ln2, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), n, C, 4 * C,
-                            dt, s));
-        CHECK(launch_gelu(a.fchg, a.fch, N * 4 * C64, dt, s));
+        // the pre-activation is kept for GELU's backward, the activation for
+        // fcproj's: both from the product's epilogue where its tile allows
+        const int rg = launch_matmul_gelu2(a.fch, a.fchg, a.ln2, at(po.fc_w + l * 4 * C64 * C64),
+                                           at(po.fc_b + l * 4 * C64), n, C, 4 * C, dt, s);
+        if (rg == GPT2_ERR_UNSUPPORTED) {
+            CHECK(launch_matmul(a.fch, a.ln2, at(po.fc_w + l * 4 * C64 * C64), at(po.fc_b + l * 4 * C64), n, C,
+                                4 * C, dt, s));
+            CHECK(launch_gelu(a.fchg, a.fch, N * 4 * C64, dt, s));
+        } else {
+            CHECK(rg);
+        }
         CHECK(launch_matmul_epi(xnext, a.fchg, at(po.fp_w + l * 4 * C64 * C64), at(po.fp_b + l * C64), a.res1, n,
                                 4 * C, C, EPI_BIAS_RESIDUAL, dt, s));
     }
