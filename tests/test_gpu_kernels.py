@@ -353,7 +353,9 @@ ATT_SHAPES = [(2, 32, 64, 4), (1, 1, 64, 4), (2, 100, 128, 2), (1, 77, 256, 8), 
               (1, 1024, 768, 12), (1, 300, 512, 4),
               # head size 64 (the GPT-2 head): one key, one partial key block, a
               # ragged second query block, 16 heads, sequences longer than 1024
-              (1, 1, 64, 1), (3, 33, 128, 2), (1, 129, 64, 1), (2, 1024, 1024, 16), (1, 1500, 192, 3)]
+              (1, 1, 64, 1), (3, 33, 128, 2), (1, 129, 64, 1), (2, 1024, 1024, 16), (1, 1500, 192, 3),
+              # more 128-query workgroups than CUs (270), ragged last query block
+              (3, 600, 1152, 18)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -371,6 +373,24 @@ def test_attention(dt, B, T, C, NH):
         assert rel_err(got, ref) <= 1e-2
     else:
         assert max_abs(got, ref) <= 1e-5
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_attention_batch_invariant_across_launch_shapes(dt):
+    """One sequence alone (a grid below the CU count: fp32 takes 64-query
+    workgroups) and inside a batch of three (128-query workgroups) gives the
+    same bits."""
+    announce("attention-batch-invariant", dt)
+    d = DT[dt]
+    B, T, C, NH = 3, 1024, 768, 12
+    qkv = I.random_tensor(23, (B, T, 3 * C), 1.0, d)
+    full = empty((B, T, C), d)
+    G.attention_forward(full, dev(qkv, d), NH)
+    got_full = host_bits(full)
+    for b in range(B):
+        one = empty((1, T, C), d)
+        G.attention_forward(one, dev(np.ascontiguousarray(qkv[b:b + 1]), d), NH)
+        assert np.array_equal(host_bits(one)[0], got_full[b]), b
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])

@@ -59,7 +59,6 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-static constexpr int kBQ = 128;  // queries per workgroup (4 wavefronts x 32)
 static constexpr float kLazyMax = 8.0f;  // running-max slack, log2 units (probabilities < 256)
 static constexpr int kBKV = 64;  // keys per LDS block
 
@@ -80,8 +79,12 @@ __device__ __forceinline__ int vt_slot_bf16(int key) {
 // blocks (the even and the odd one); when two iterations' worth fits in LDS
 // the next pair is loaded while the current one is computed.
 // WPE: minimum wavefronts per SIMD the registers must allow (0: none).
-template <typename T, int HS, int WPE = 0>
-__global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
+// QC: 32-query chunks per workgroup (4: 8 wavefronts, 128 queries, the two
+// staged block pairs double-buffered when they fit; 2: 4 wavefronts, 64
+// queries, one staged pair with the next pair's loads held in registers while
+// the current one is multiplied, so two workgroups share a CU).
+template <typename T, int HS, int WPE = 0, int QC = 4>
+__global__ __launch_bounds__(128 * QC, WPE) void attention_kernel(T* __restrict__ out, const T* __restrict__ qkv,
                                                              int Tn, int C, int NH, float sl2,
                                                              float* __restrict__ lse) {
     constexpr bool F32 = std::is_same<T, float>::value;
@@ -94,24 +97,26 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
     constexpr int LDV = kBKV + VE;  // V^T block [HSP][kBKV], 16-byte row pad
     constexpr int KSZ = kBKV * LDK, VSZ = HSP * LDV;  // elements per block
     constexpr int PAIR = 2 * (KSZ + VSZ);             // one iteration: even + odd block
-    constexpr bool DB = 2 * PAIR * (int)sizeof(T) <= 160 * 1024;  // double-buffered
+    constexpr int NT = 128 * QC, BQ = 32 * QC;        // threads, queries per workgroup
+    constexpr bool DB = QC == 4 && 2 * PAIR * (int)sizeof(T) <= 160 * 1024;  // double-buffered
+    constexpr bool PF = QC == 2;  // single-buffered, next pair prefetched into registers
     constexpr int NBUF = DB ? 2 : 1;
     constexpr int RV = HS / VE;                                  // 16-byte vectors per key row
-    constexpr int NKV = (2 * kBKV * RV + 511) / 512;             // K vectors per thread
-    constexpr int NVS = (2 * kBKV / 4 * RV + 511) / 512;         // V 4-key sub-blocks per thread
-    constexpr int MERGE = 4 * 64 * (DT * 16 + 2);                // floats for the parity merge
+    constexpr int NKV = (2 * kBKV * RV + NT - 1) / NT;           // K vectors per thread
+    constexpr int NVS = (2 * kBKV / 4 * RV + NT - 1) / NT;       // V 4-key sub-blocks per thread
+    constexpr int MERGE = QC * 64 * (DT * 16 + 2);               // floats for the parity merge
     static_assert(MERGE * 4 <= NBUF * PAIR * (int)sizeof(T), "merge area");
     __shared__ __attribute__((aligned(16))) T smem[NBUF * PAIR];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int qc = wid & 3, par = wid >> 2;
+    const int qc = wid % QC, par = wid / QC;
     const int h = lane >> 5, r32 = lane & 31;
     // Workgroups are dispatched in linear order (x fastest): all (batch, head)
     // pairs of the last, longest query block first, then the next, so the
     // causal triangle's long rows never end up in the tail.
     const int qb = gridDim.y - 1 - blockIdx.y;
     const int bh = blockIdx.x, b = bh / NH, hd = bh % NH;
-    const int q0 = qb * kBQ, qw = q0 + qc * 32;
+    const int q0 = qb * BQ, qw = q0 + qc * 32;
     const int64_t rs = 3 * (int64_t)C;
     const T* base = qkv + (int64_t)b * Tn * rs;
     const int qoff = hd * HS, koff = C + hd * HS, voff = 2 * C + hd * HS;
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
 
     // Padded head rows of V^T (HS < 32) are never loaded: zero them once.
     if (HS < HSP) {
-        for (int i = tid; i < NBUF * 2 * (HSP - HS) * LDV; i += 512) {
+        for (int i = tid; i < NBUF * 2 * (HSP - HS) * LDV; i += NT) {
             const int blk = i / ((HSP - HS) * LDV), j = i % ((HSP - HS) * LDV);
             T* vb = Vblk(blk >> 1, blk & 1) + HS * LDV + j;
             if constexpr (F32) *vb = 0.f;
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
     auto gload = [&](int k0) {  // keys k0 .. k0 + 127
 #pragma unroll
         for (int i = 0; i < NKV; i++) {
-            const int li = tid + i * 512, r = li / RV, cv = li % RV, key = k0 + r;
+            const int li = tid + i * NT, r = li / RV, cv = li % RV, key = k0 + r;
             rk[i] = (li < 2 * kBKV * RV && key < Tn)
                         ? *reinterpret_cast<const u32x4*>(base + key * rs + koff + cv * VE) : zero;
         }
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
         // fill one contiguous run of a V^T row (no bank conflicts).
 #pragma unroll
         for (int i = 0; i < NVS; i++) {
-            const int li = tid + i * 512, rest = li >> 4;
+            const int li = tid + i * NT, rest = li >> 4;
             const int kq = (rest / RV) * 16 + (li & 15), cv = rest % RV;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
@@ -167,13 +172,13 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < NKV; i++) {
-            const int li = tid + i * 512, r = li / RV, cv = li % RV;
+            const int li = tid + i * NT, r = li / RV, cv = li % RV;
             if (li < 2 * kBKV * RV)
                 *reinterpret_cast<u32x4*>(&Kblk(buf, r / kBKV)[(r % kBKV) * LDK + cv * VE]) = rk[i];
         }
 #pragma unroll
         for (int i = 0; i < NVS; i++) {
-            const int li = tid + i * 512, rest = li >> 4;
+            const int li = tid + i * NT, rest = li >> 4;
             const int kq = (rest / RV) * 16 + (li & 15), cv = rest % RV;
             if (li < 2 * kBKV / 4 * RV) {
                 T* vb = Vblk(buf, (4 * kq) / kBKV);
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
         }
     };
 
-    const int kend = min(Tn, q0 + kBQ);
+    const int kend = min(Tn, q0 + BQ);
     const int nkb = (kend + kBKV - 1) / kBKV;  // key blocks this workgroup needs
     const int npair = (nkb + 1) / 2;
     auto compute_pair = [&](int buf, int i) {
@@ -326,6 +331,19 @@ __global__ __launch_bounds__(512, WPE) void attention_kernel(T* __restrict__ out
             compute_pair(cur, i);
             if (i + 1 < npair) sstore(cur ^ 1);
             __syncthreads();
+        }
+    } else if constexpr (PF) {
+        gload(0);
+        sstore(0);
+        __syncthreads();
+        for (int i = 0; i < npair; i++) {
+            if (i + 1 < npair) gload((i + 1) * 2 * kBKV);
+            compute_pair(0, i);
+            __syncthreads();
+            if (i + 1 < npair) {
+                sstore(0);
+                __syncthreads();
+            }
         }
     } else {
         for (int i = 0; i < npair; i++) {
@@ -596,11 +614,21 @@ __global__ __launch_bounds__(64 * kAttnD64Waves, 3) void attention_bf16_d64_kern
 template <typename T, int HS>
 static void launch_attn_hs(T* out, const T* qkv, int B, int Tn, int C, int NH, hipStream_t s, float* lse) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)HS);  // log2(e)/sqrt(hs)
-    dim3 grid(B * NH, (Tn + kBQ - 1) / kBQ);
-    if constexpr (std::is_same<T, float>::value)
+    dim3 grid(B * NH, (Tn + 127) / 128);
+    if constexpr (std::is_same<T, float>::value) {
+        if constexpr (HS == 64) {
+            if ((int)(grid.x * grid.y) <= kNumCUs) {
+                // Fewer 128-query workgroups than CUs: 64-query workgroups,
+                // two per CU, reach every CU and halve the longest one's work.
+                grid.y = (Tn + 63) / 64;
+                attention_kernel<T, HS, 2, 2><<<grid, 256, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
+                return;
+            }
+        }
         attention_kernel<T, HS, (HS >= 64 ? 2 : 3)><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
-    else
+    } else {
         attention_kernel<T, HS><<<grid, 512, 0, s>>>(out, qkv, Tn, C, NH, sl2, lse);
+    }
 }
 
 template <typename T>

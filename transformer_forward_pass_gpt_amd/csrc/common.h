@@ -178,6 +178,8 @@ enum Epilogue {
     EPI_BIAS_GELU2 = 6
 };
 constexpr int kStatCols = 128;
+constexpr int kNumCUs = 256;  // compute units of one MI355X (8 XCDs x 32)
+
 // Status after a launch: GPT2_OK, or GPT2_ERR_HIP with the code recorded.
 int launch_status();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
