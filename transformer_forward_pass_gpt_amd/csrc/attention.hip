@@ -748,14 +748,16 @@ __global__ __launch_bounds__(NT) void decode_attn_kernel(T* __restrict__ out, fl
         *reinterpret_cast<u32x4*>(Vc + (int64_t)pos * HS) = *reinterpret_cast<const u32x4*>(vnew);
     }
     // every load first: key row j (the new one from qkv_new, never from the
-    // cache slot being written); rows past the chunk read row j0 and are masked
+    // cache slot being written); rows past the chunk read row j0 and are masked.
+    // The cache is read once per step, so its lines are marked non-temporal:
+    // they do not displace the weights the step's projections read again.
     u32x4 kr[NP], vr[NP];
 #pragma unroll
     for (int p = 0; p < NP; p++) {
         const int j = j0 + kg + p * KPP;
         const int jc = j < j1 ? j : j0;
-        kr[p] = *reinterpret_cast<const u32x4*>(jc == pos ? knew : K + (int64_t)jc * HS);
-        vr[p] = *reinterpret_cast<const u32x4*>(jc == pos ? vnew : Vc + (int64_t)jc * HS);
+        kr[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(jc == pos ? knew : K + (int64_t)jc * HS));
+        vr[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(jc == pos ? vnew : Vc + (int64_t)jc * HS));
     }
     float q[VE];
     load_vec(qrow + hd * HS + sub * VE, q);

@@ -70,6 +70,16 @@ __device__ __forceinline__ void store_vec(bf16* p, const float (&v)[8]) {
     x.z = pack_bf16x2(v[4], v[5]); x.w = pack_bf16x2(v[6], v[7]);
     *reinterpret_cast<uint4*>(p) = x;
 }
+// Non-temporal forms, for streams written once and not read again soon.
+__device__ __forceinline__ void store_vec_nt(float* p, const float (&v)[4]) {
+    const u32x4 x = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_vec_nt(bf16* p, const float (&v)[8]) {
+    const u32x4 x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
 
 // The value a store of v into T's storage keeps (identity for fp32).
 __device__ __forceinline__ float storage_round(const float*, float v) { return v; }
@@ -173,9 +183,11 @@ void set_last_hip_error(int e);
 // type is stored in out, and GELU of that stored y, rounded, in out2: the
 // pre-activation a GELU backward needs and the activation the next product
 // reads, as a separate GELU kernel would compute it.
+// EPI_BIAS_NT: EPI_BIAS with non-temporal stores, for outputs far larger than
+// the caches (the vocabulary logits) that would otherwise displace operands.
 enum Epilogue {
     EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_STATS = 3, EPI_ASUM = 4, EPI_DGELU = 5,
-    EPI_BIAS_GELU2 = 6
+    EPI_BIAS_GELU2 = 6, EPI_BIAS_NT = 7
 };
 constexpr int kStatCols = 128;
 constexpr int kNumCUs = 256;  // compute units of one MI355X (8 XCDs x 32)

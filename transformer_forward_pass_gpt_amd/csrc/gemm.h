@@ -631,7 +631,10 @@ __global__ __launch_bounds__(WM* WN * 64, WPE) void gemm_pipe_kernel(TO* out, co
                 const int row = m0 + rl, col = n0 + cv * VO;
                 if (row < M && col < N) {
                     const u32x4 y = *reinterpret_cast<const u32x4*>(&so[rl * LDO + cv * VO]);
-                    *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) = y;
+                    if constexpr (EPI == EPI_BIAS_NT)
+                        __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(out + (int64_t)row * N + col));
+                    else
+                        *reinterpret_cast<u32x4*>(out + (int64_t)row * N + col) = y;
                     if constexpr (EPI == EPI_BIAS_GELU2) {
                         float a[VO];
                         unpack_vec<TO>(y, a);
@@ -698,6 +701,7 @@ static void launch_gemm_pipe(T* out, const T* A, const T* W, const T* bias, int 
     else if (epi == EPI_BIAS_RESIDUAL) GEMM_PIPE_LAUNCH(EPI_BIAS_RESIDUAL);
     else if (epi == EPI_DGELU) GEMM_PIPE_LAUNCH(EPI_DGELU);
     else if (epi == EPI_BIAS_GELU2) GEMM_PIPE_LAUNCH(EPI_BIAS_GELU2);
+    else if (epi == EPI_BIAS_NT) GEMM_PIPE_LAUNCH(EPI_BIAS_NT);
     else GEMM_PIPE_LAUNCH(EPI_BIAS);
 #undef GEMM_PIPE_LAUNCH
 }

@@ -101,6 +101,8 @@ template <typename T>
 static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T* res, int M, int N, int K,
                           int dtype, int epi, hipStream_t s, T* out2 = nullptr) {
     constexpr int BK = Vec<T>::N * 8;  // 128 bytes of k per row per LDS tile
+    // vocabulary-wide outputs (hundreds of MB) are stored past the caches
+    if (epi == EPI_BIAS && N >= 16384) epi = EPI_BIAS_NT;
     switch (choose_cfg(M, N, K, dtype)) {
         case S32: launch_skinny<T>(out, nullptr, A, W, bias, res, M, N, K, 1, epi, s); break;
         // launch_gemm_cfg<T, WM, WN, TM, TN, BK>(..., group_m, remap, s, epi, res)

@@ -341,6 +341,9 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* probs, const T* logits, 
     const int cv = Vp / VE;
     const int tg = targets ? targets[row] : 0;
     const float lt = targets ? load_scalar(x + tg) : 0.f;
+    // The row is read once and the probabilities written once, so both go
+    // past the caches (non-temporal), leaving them to the operands of the
+    // kernels around this one.
     // Every load of the row is issued before the first use: indices past the
     // row are clamped to its last vector and masked, not branched around
     // (a load inside a divergent branch would be waited for at the branch's end).
@@ -348,7 +351,8 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* probs, const T* logits, 
         u32x4 raw[PT];
 #pragma unroll
         for (int i = 0; i < PT; i++)
-            raw[i] = *reinterpret_cast<const u32x4*>(x + min((int)threadIdx.x + i * NT, cv - 1) * VE);
+            raw[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(x + min((int)threadIdx.x + i * NT, cv - 1) * VE));
         // An empty asm that may rewrite the vectors keeps the compiler from
         // carrying widened copies (or exponentials) from one pass to the next.
         auto opaque = [&]() {
@@ -412,14 +416,18 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* probs, const T* logits, 
                     else
                         v[j] = ex(i, j) * inv;
                 }
-                store_vec(y + idx * VE, v);
+                store_vec_nt(y + idx * VE, v);
             }
         }
     } else {
         float v[PT][VE];
         float m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < PT; i++) load_vec(x + min((int)threadIdx.x + i * NT, cv - 1) * VE, v[i]);
+        for (int i = 0; i < PT; i++) {
+            const u32x4 raw = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(x + min((int)threadIdx.x + i * NT, cv - 1) * VE));
+            unpack_vec<T>(raw, v[i]);
+        }
 #pragma unroll
         for (int i = 0; i < PT; i++) {
             const int idx = threadIdx.x + i * NT;
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(NT) void softmax_kernel(T* probs, const T* logits, 
                     else
                         v[i][j] *= inv;
                 }
-                store_vec(y + idx * VE, v[i]);
+                store_vec_nt(y + idx * VE, v[i]);
             }
         }
     }
