@@ -195,19 +195,38 @@ __global__ __launch_bounds__(64 * kLnbWaves) void layernorm_backward_kernel(T* d
 #pragma unroll
         for (int j = 0; j < V; j++) ag[i][j] = ab[i][j] = 0.f;
     }
-    for (int row = blockIdx.x * kLnbWaves + w; row < N; row += gridDim.x * kLnbWaves) {  // wave-uniform
-        const T* xr = inp + (int64_t)row * C;
-        const T* dr = dout + (int64_t)row * C;
+    // Up to two vectors per lane (PF), the loads of a wave's next row are
+    // issued before its current row is computed (raw 16-byte vectors,
+    // unpacked once the row is current); wider rows would need the registers
+    // of a second resident workgroup or spill.
+    constexpr bool PF = VPL <= 2;
+    const int stride = gridDim.x * kLnbWaves;
+    u32x4 px[VPL], pd[VPL], pr[VPL];
+    float pmu = 0.f, prs = 0.f;
+    auto fetch = [&](int row) {
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+            const int64_t off = (int64_t)row * C + min(lane + i * 64, cv - 1) * V;
+            px[i] = *reinterpret_cast<const u32x4*>(inp + off);
+            pd[i] = *reinterpret_cast<const u32x4*>(dout + off);
+            // unconditional (dout stands in when there is no dres), so no load waits at a branch
+            pr[i] = *reinterpret_cast<const u32x4*>((dres ? dres : dout) + off);
+        }
+        pmu = mean[row];
+        prs = rstd[row];
+    };
+    if (PF && blockIdx.x * kLnbWaves + w < N) fetch(blockIdx.x * kLnbWaves + w);
+    for (int row = blockIdx.x * kLnbWaves + w; row < N; row += stride) {  // wave-uniform
+        if (!PF) fetch(row);
         float x[VPL][V], d[VPL][V], r0[VPL][V];
 #pragma unroll
         for (int i = 0; i < VPL; i++) {
-            const int idx = min(lane + i * 64, cv - 1);
-            load_vec(xr + idx * V, x[i]);
-            load_vec(dr + idx * V, d[i]);
-            // unconditional (dout stands in when there is no dres), so no load waits at a branch
-            load_vec((dres ? dres : dout) + (int64_t)row * C + idx * V, r0[i]);
+            unpack_vec<T>(px[i], x[i]);
+            unpack_vec<T>(pd[i], d[i]);
+            unpack_vec<T>(pr[i], r0[i]);
         }
-        const float mu = mean[row], rs = rstd[row];
+        const float mu = pmu, rs = prs;
+        if (PF && row + stride < N) fetch(row + stride);
         float a = 0.f, b = 0.f;
 #pragma unroll
         for (int i = 0; i < VPL; i++) {
@@ -270,22 +289,39 @@ int64_t layernorm_backward_workspace_bytes(int N, int C) {
     return 2 * align256((int64_t)ln_bwd_grid(N) * C * 4);
 }
 
+// Workgroups of one instantiation resident per CU (registers and LDS decide),
+// asked of the runtime once.
+template <typename T, int P>
+static int ln_bwd_per_cu() {
+    static const int n = [] {
+        int k = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, layernorm_backward_kernel<T, P>, 64 * kLnbWaves, 0) !=
+            hipSuccess)
+            k = 1;
+        return max(k, 1);
+    }();
+    return n;
+}
+
 template <typename T>
 static void launch_ln_bwd_t(T* dinp, T* dgamma, T* dbeta, const T* dres, const T* dout, const T* inp, const T* gamma,
                             const float* mean, const float* rstd, int N, int C, void* ws, hipStream_t s) {
-    const int grid = ln_bwd_grid(N);
+    const int rows = ln_bwd_grid(N);  // workspace bound: at most this many partial rows
     float* gpart = (float*)ws;
-    float* bpart = (float*)((char*)ws + align256((int64_t)grid * C * 4));
+    float* bpart = (float*)((char*)ws + align256((int64_t)rows * C * 4));
     const int vpl = (C / Vec<T>::N + 63) / 64;
-#define LNB(P)                                                                                                \
-    layernorm_backward_kernel<T, P><<<grid, 64 * kLnbWaves, 0, s>>>(dinp, gpart, bpart, dres, dout, inp, gamma, \
-                                                                    mean, rstd, \
-                                                          N, C)
-    if (vpl <= 1) LNB(1);
-    else if (vpl <= 2) LNB(2);
-    else if (vpl <= 3) LNB(3);
-    else if (vpl <= 4) LNB(4);
-    else LNB(8);
+    // One resident round of workgroups (rows strided over it, the next row's
+    // loads in flight while one is computed), not a second partial round.
+    int grid = rows;
+#define LNB(P)                                                                                                    \
+    grid = min(rows, kNumCUs * ln_bwd_per_cu<T, P>());                                                            \
+    layernorm_backward_kernel<T, P><<<grid, 64 * kLnbWaves, 0, s>>>(dinp, gpart, bpart, dres, dout, inp, gamma,   \
+                                                                    mean, rstd, N, C)
+    if (vpl <= 1) { LNB(1); }
+    else if (vpl <= 2) { LNB(2); }
+    else if (vpl <= 3) { LNB(3); }
+    else if (vpl <= 4) { LNB(4); }
+    else { LNB(8); }
 #undef LNB
     // both column sums in one launch when both are wanted
     if (dgamma && dbeta) launch_colsum<T>(dgamma, gpart, grid, C, s, dbeta, bpart);
