@@ -38,6 +38,7 @@ enum GemmCfg {
     S32 = 0, R64x64, R64x128, R128x96,
     P128x96_S4, P128x96_S5, P256x128_S3A, P128x128_O2, P128x288_I, P128x192_R4,  // fp32
     P128x256_O4, P128x256_R3, P256x128_G, P128x128_R4, P128x128_K3, P256x256_K2, P128x192_K2,  // bf16
+    P128x192_K3, P256x192_K2,                                                                     // bf16
     G_NCFG
 };
 // fp32 128x288_p3: 4 wavefronts of 32x288 (nine accumulator tiles each), so GPT-2 small's qkv
@@ -48,14 +49,16 @@ enum GemmCfg {
 // grouped XCD-aware walk (the fp32 vocabulary tile walks columns instead). 256x256_p2_k128:
 // 8 wavefronts of 128x64, two stages of 128-byte rows (the L2 sees one 128-byte request per
 // row per k-tile instead of two 64-byte ones; the same bytes in flight as three 64-byte stages).
-// 128x192_p2_k128: two stages of 128-byte rows in 80 KiB, so two workgroups fill a CU's LDS.
+// 128x192_p2_k128: two stages of 128-byte rows in 80 KiB, so two workgroups fill a CU's LDS;
+// 128x192_p3_k128: three stages (one workgroup per CU) for the 768-wide projections at 8192
+// rows; 256x192_p2_k128: 8 wavefronts of 64x96, chosen where its tile count fills whole rounds.
 static const PipeCfg kCfg[G_NCFG] = {
     {"skinny32", 0},          {"64x64_r", 0},          {"64x128_r", 0},         {"128x96_r", 0},
     {"128x96_p4", 128},       {"128x96_p5", 128},      {"256x128_p3", 128},     {"128x128_p4_o2", 64},
     {"128x288_p3", 128},      {"128x192_p4_r64", 64},
     {"128x256_p3_o4", 64},    {"128x256_p3_k128", 128}, {"256x128_p3g", 128},
     {"128x128_p4_k128", 128}, {"128x128_p3_k128", 128}, {"256x256_p2_k128", 128},
-    {"128x192_p2_k128", 128},
+    {"128x192_p2_k128", 128}, {"128x192_p3_k128", 128}, {"256x192_p2_k128", 128},
 };
 
 static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
@@ -72,14 +75,21 @@ static GemmCfg choose_pipe(int M, int N, int K, int dtype) {
     // use two resident two-stage 128x192 workgroups per CU where the width
     // allows, else 128x256 (two per CU) or two-stage 256x256 tiles; every
     // 128-byte-row tile halves the L2 requests of a 64-byte-row one.
+    auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (N >= 16384) return P256x256_K2;                         // vocabulary projection
     if (K >= 2048) {  // fcproj (and the training step's vocabulary input gradient, K = Vp):
         // enough tiles for the 256 CUs at GPT-2 small's width
-        if (M >= 8192) return P128x256_R3;
+        if (M >= 8192) return N % 192 == 0 ? P128x192_K3 : P128x256_R3;
         return N <= 768 ? P128x96_S4 : P128x128_R4;
     }
-    if (N <= 1024) return M >= 8192 ? P128x256_R3 : P128x128_K3;   // attproj
-    if (N % 192 == 0) return P128x192_K2;                       // qkv, fc at GPT-2 small widths
+    if (N <= 1024) {  // attproj
+        if (M >= 8192) return N % 192 == 0 ? P128x192_K3 : P128x256_R3;
+        return N <= 768 ? P128x96_S4 : P128x128_K3;
+    }
+    if (N % 192 == 0) {  // qkv, fc at GPT-2 small and medium widths
+        if (tiles(256, 192) % 256 == 0) return P256x192_K2;     // whole rounds of the 256 CUs
+        return M >= 8192 ? P128x192_R4 : P128x192_K2;
+    }
     return M >= 8192 ? P128x256_O4 : P256x256_K2;               // qkv, fc
 }
 
@@ -128,6 +138,8 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
                     case P128x128_R4: PIPE(2, 2, 2, 2, 128, 4, 2, 0, 8, 1); break;
                     case P128x128_K3: PIPE(2, 2, 2, 2, 128, 3, 2, 0, 8, 1); break;
                     case P128x192_K2: PIPE(2, 2, 2, 3, 128, 2, 2, 2, 4, 1); break;
+                    case P128x192_K3: PIPE(2, 2, 2, 3, 128, 3, 2, 0, 4, 1); break;
+                    case P256x192_K2: PIPE(4, 2, 2, 3, 128, 2, 2, 0, 4, 1); break;
                     default:
                         if (N >= 16384)  // vocabulary: column sweep within each row band
                             PIPE(2, 4, 4, 2, 128, 2, 2, 0, 1, 0);
