@@ -141,7 +141,9 @@ static void launch_gemm_t(T* out, const T* A, const T* W, const T* bias, const T
                     case P128x192_K3: PIPE(2, 2, 2, 3, 128, 3, 2, 0, 4, 1); break;
                     case P256x192_K2: PIPE(4, 2, 2, 3, 128, 2, 2, 0, 4, 1); break;
                     default:
-                        if (N >= 16384)  // vocabulary: column sweep within each row band
+                        if (N >= 16384 && M >= 8192)  // vocabulary, 8192+ rows: pairs of row
+                            PIPE(2, 4, 4, 2, 128, 2, 2, 0, 2, 1);  // bands, XCD-contiguous ranges
+                        else if (N >= 16384)  // vocabulary: column sweep within each row band
                             PIPE(2, 4, 4, 2, 128, 2, 2, 0, 1, 0);
                         else
                             PIPE(2, 4, 4, 2, 128, 2, 2, 0, 4, 1);
