@@ -501,7 +501,9 @@ __global__ __launch_bounds__(64 * kAttnD64Waves, 3) void attention_bf16_d64_kern
     float l_part = 0.f;                  // this lane's share of the normaliser (its 16 keys per tile)
 
     auto block = [&](const bf16* Ks, const bf16* Vs, int k0) {
-        // every K fragment of the block first, then the score products
+        // every K fragment of the block first, then the score products; the
+        // compiler's MFMA/memory interleaving strategy 1 for the block
+        __builtin_amdgcn_iglp_opt(1);
         u32x4 ka[4][2];
 #pragma unroll
         for (int kc = 0; kc < 4; kc++) {
