@@ -512,9 +512,10 @@ __global__ __launch_bounds__(64 * kAttnD64Waves, 3) void attention_bf16_d64_kern
             ka[kc][1] = *reinterpret_cast<const u32x4*>(&Ks[ko + 32 * HS]);
         }
         f32x16 sc[2];
-        // Issue priority for the score products: of the wavefronts sharing a
-        // SIMD (other workgroups'), one entering its products goes ahead of
-        // those in their softmax, so matrix and vector work overlap more.
+        // Issue priority for the score products and the V^T reads after them:
+        // of the wavefronts sharing a SIMD (other workgroups'), one entering
+        // its products goes ahead of those in their softmax, so matrix and
+        // vector work overlap more.
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kc = 0; kc < 4; kc++)
@@ -523,7 +524,6 @@ __global__ __launch_bounds__(64 * kAttnD64Waves, 3) void attention_bf16_d64_kern
                 sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kc][kt]),
                                                                 __builtin_bit_cast(bf16x8, qf[kc]),
                                                                 kc ? sc[kt] : f32x16{}, 0, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
         // the V^T fragments of the whole block, read while the softmax runs
         const lds_v4s_ptr vt = (lds_v4s_ptr)Vs;
         u32x4 va[2][2][2];
@@ -539,6 +539,7 @@ __global__ __launch_bounds__(64 * kAttnD64Waves, 3) void attention_bf16_d64_kern
                     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
                     va[kt][ks][dt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
                 }
+        __builtin_amdgcn_s_setprio(0);
         const int q = qw + r32;
         if (k0 + KB - 1 > qw) {  // diagonal block: keys after the query are -inf
 #pragma unroll
